@@ -1,0 +1,212 @@
+"""Seeded synthetic inputs shared by the HIP path's tests/bench and the oracle.
+
+This module draws random numbers and nothing else: it holds none of the
+method's arithmetic (no norms, rotations, quantisers or scores).  Both the GPU
+tests and the CPU oracle take their inputs from here, so the two sides see the
+same numbers without sharing any code that computes the method.
+
+Workloads follow the shapes of the decode workloads the TurboQuant article
+(kwkr.cn, "TurboQuant: near-optimal KV cache quantization", header and §七)
+and the A-QJL article (zingnex.cn, "A-QJL", section "实际部署与使用") describe:
+head_dim 128/256, long contexts, GQA, bf16 K/V.  The pages' real
+workloads (LongBench, qasper, model activations) are not available; seeded
+Gaussian tensors with the stated structure stand in for them.
+
+Seeding
+-------
+* Random Gaussians the method itself draws (the matrix that is orthogonalised
+  into the rotation, and the QJL sketch S) come from
+  ``numpy.random.PCG64(42 + 7 * layer)``: first the d*d matrix, then the
+  m*d sketch, from one stream (TurboQuant article §六, per-layer seed rule).
+* Every K/V slice is drawn per (workload, layer, batch, kv-head, tensor,
+  token block of ``BLOCK`` tokens) from its own ``SeedSequence``, so any part
+  of a large cache can be regenerated on the host without reading it back.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+BLOCK = 4096  # tokens per independently seeded block of a K/V slot
+
+_TENSOR_IDS = {"k": 1, "v": 2, "q": 3, "outlier": 4, "kscale": 5, "vscale": 6}
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic decode workload: cache shape, codec and value recipe."""
+
+    name: str
+    wid: int                 # numeric id mixed into every seed
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    context: int
+    head_dim: int
+    mse_bits: int            # Lloyd-Max bits per rotated coordinate (0 = pure QJL)
+    sketch_dims: Tuple[int, ...]   # per layer; length == layers
+    value_bits: int = 2
+    value_group: int = 32
+    layers: int = 1
+    dtype: str = "bf16"      # K/V element type handed to the kernels
+    recipe: str = "normal"   # normal | outliers | chscale | layer_sigma
+    scores: bool = False     # also return the per-token score estimates
+    notes: str = ""
+
+    def sketch_dim(self, layer: int) -> int:
+        return self.sketch_dims[layer]
+
+    @property
+    def n_slots(self) -> int:
+        return self.batch * self.n_kv_heads
+
+
+def _aqjl_dims(layers: int = 32) -> Tuple[int, ...]:
+    # A-QJL article, "实际部署与使用": boundaries 8,16,24 and k = 512,384,256,192
+    ks = (512, 384, 256, 192)
+    bounds = (8, 16, 24)
+    out = []
+    for layer in range(layers):
+        g = sum(layer >= b for b in bounds)
+        out.append(ks[g])
+    return tuple(out)
+
+
+WORKLOADS = {
+    "single_head_d128_t1k": Workload(
+        "single_head_d128_t1k", 1, batch=1, n_q_heads=1, n_kv_heads=1, context=1024,
+        head_dim=128, mse_bits=2, sketch_dims=(128,), dtype="fp32", recipe="normal",
+        scores=True, notes="fp32 K/V/q ~N(0,1); 2-bit Lloyd-Max + 1-bit QJL keys"),
+    "llama2_7b_layer_mha32_t32k": Workload(
+        "llama2_7b_layer_mha32_t32k", 2, batch=1, n_q_heads=32, n_kv_heads=32,
+        context=32768, head_dim=128, mse_bits=2, sketch_dims=(128,), recipe="outliers",
+        notes="bf16 K/V ~N(0,1), 4 outlier channels per head scaled x10"),
+    "llama3_8b_layer_gqa32x8_b8_t128k": Workload(
+        "llama3_8b_layer_gqa32x8_b8_t128k", 3, batch=8, n_q_heads=32, n_kv_heads=8,
+        context=131072, head_dim=128, mse_bits=2, sketch_dims=(128,), recipe="chscale",
+        notes="bf16 K/V ~N(0,1) x per-(kv head, channel) LogNormal(0,0.5) scale"),
+    "d256_gqa32x16_b4_t64k": Workload(
+        "d256_gqa32x16_b4_t64k", 4, batch=4, n_q_heads=32, n_kv_heads=16, context=65536,
+        head_dim=256, mse_bits=3, sketch_dims=(256,), recipe="normal",
+        notes="bf16 K/V ~N(0,1); 3-bit Lloyd-Max + 1-bit QJL keys"),
+    "aqjl_32layer_gqa32x8_b16_t32k": Workload(
+        "aqjl_32layer_gqa32x8_b16_t32k", 5, batch=16, n_q_heads=32, n_kv_heads=8,
+        context=32768, head_dim=128, mse_bits=0, sketch_dims=_aqjl_dims(32), layers=32,
+        recipe="layer_sigma",
+        notes="pure 1-bit QJL keys, k per layer group; keys ~N(0, sigma_l^2)"),
+}
+
+
+# --------------------------------------------------------------------------
+# bf16 storage helpers (round-to-nearest-even from fp32, plain bit handling)
+# --------------------------------------------------------------------------
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# random matrices drawn by the method (per layer)
+# --------------------------------------------------------------------------
+
+def layer_seed(layer: int) -> int:
+    """TurboQuant article §六: each layer's matrices come from seed 42 + 7*layer."""
+    return 42 + 7 * layer
+
+
+def layer_gaussians(layer: int, head_dim: int, sketch_dim: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(G, S): G is d x d N(0,1) (to be orthogonalised into the rotation),
+    S is m x d N(0,1) (the QJL sketch), float64, one PCG64 stream per layer."""
+    rng = np.random.Generator(np.random.PCG64(layer_seed(layer)))
+    g = rng.standard_normal((head_dim, head_dim))
+    s = rng.standard_normal((sketch_dim, head_dim))
+    return g, s
+
+
+# --------------------------------------------------------------------------
+# K / V / q tensors
+# --------------------------------------------------------------------------
+
+def _rng(w: Workload, layer: int, b: int, h: int, tensor: str, block: int = 0) -> np.random.Generator:
+    ss = np.random.SeedSequence([w.wid, layer, b, h, _TENSOR_IDS[tensor], block])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def _channel_scale(w: Workload, layer: int, h: int, tensor: str) -> Optional[np.ndarray]:
+    d = w.head_dim
+    if w.recipe == "outliers":
+        rng = _rng(w, layer, 0, h, "outlier")
+        ch = rng.choice(d, size=4, replace=False)
+        sc = np.ones(d, dtype=np.float32)
+        sc[ch] = 10.0
+        return sc
+    if w.recipe == "chscale":
+        rng = _rng(w, layer, 0, h, "kscale" if tensor == "k" else "vscale")
+        return rng.lognormal(0.0, 0.5, size=d).astype(np.float32)
+    if w.recipe == "layer_sigma" and tensor == "k":
+        sigma = 2.0 - 1.5 * layer / max(w.layers - 1, 1)
+        return np.full(d, sigma, dtype=np.float32)
+    return None
+
+
+def kv_slot(w: Workload, layer: int, b: int, h: int, tensor: str,
+            t0: int = 0, t1: Optional[int] = None) -> np.ndarray:
+    """Tokens [t0, t1) of one (batch, kv-head) slot of K or V as float32 [T, d].
+
+    For bf16 workloads the values are already rounded to bf16 (so they are
+    exactly what the device sees); use ``to_bf16_bits`` to get the bits."""
+    assert tensor in ("k", "v")
+    t1 = w.context if t1 is None else t1
+    d = w.head_dim
+    out = np.empty((t1 - t0, d), dtype=np.float32)
+    sc = _channel_scale(w, layer, h, tensor)
+    blk0, blk1 = t0 // BLOCK, (t1 + BLOCK - 1) // BLOCK
+    for blk in range(blk0, blk1):
+        bs, be = blk * BLOCK, min((blk + 1) * BLOCK, w.context)
+        rng = _rng(w, layer, b, h, tensor, blk)
+        x = rng.standard_normal((be - bs, d), dtype=np.float32)
+        if sc is not None:
+            x *= sc
+        lo, hi = max(bs, t0), min(be, t1)
+        out[lo - t0:hi - t0] = x[lo - bs:hi - bs]
+    if w.dtype == "bf16":
+        out = bf16_bits_to_f32(to_bf16_bits(out))
+    return out
+
+
+def queries(w: Workload, layer: int) -> np.ndarray:
+    """Decode queries [B, Hq, d] float32 ~N(0,1)."""
+    rng = _rng(w, layer, 0, 0, "q")
+    return rng.standard_normal((w.batch, w.n_q_heads, w.head_dim), dtype=np.float32)
+
+
+def kv_tensor(w: Workload, layer: int, tensor: str, batches=None, heads=None,
+              t0: int = 0, t1: Optional[int] = None) -> np.ndarray:
+    """[len(batches), len(heads), T, d] float32 built slot by slot."""
+    batches = range(w.batch) if batches is None else batches
+    heads = range(w.n_kv_heads) if heads is None else heads
+    t1 = w.context if t1 is None else t1
+    out = np.empty((len(batches), len(heads), t1 - t0, w.head_dim), dtype=np.float32)
+    for i, b in enumerate(batches):
+        for j, h in enumerate(heads):
+            out[i, j] = kv_slot(w, layer, b, h, tensor, t0, t1)
+    return out
+
+
+def small_workload(base: Workload, **over) -> Workload:
+    """A reduced copy of a workload (same recipe and codec) for parity tests
+    the oracle finishes in seconds."""
+    fields = dict(base.__dict__)
+    fields.update(over)
+    if "layers" in over and "sketch_dims" not in over:
+        fields["sketch_dims"] = base.sketch_dims[: over["layers"]]
+    return Workload(**fields)

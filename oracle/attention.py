@@ -1,0 +1,61 @@
+"""Query preparation, score estimator and decode attention (oracle, float64).
+
+TurboQuant article §六: the query is rotated (q Pi^T) and sketched (q S^T)
+once per query; the score of a cached key is the MSE part plus the QJL part,
+the scores become logits and go through softmax over the dequantised values.
+
+The oracle deliberately evaluates the score in the *dequantised-key* form
+(§五: <y, x~_mse> + ||r|| sqrt(pi/2)/m <S^T signs, y>) -- it rebuilds k^ in
+the original space and takes <q, k^> -- so it shares no algebra with a
+query-side implementation.  Softmax is the textbook two-pass form with the
+maximum subtracted; logits are score / sqrt(d) unless another scale is given.
+GQA: query head hq reads kv head hq // (Hq / Hkv).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .keys import dequantize_keys
+from .values import dequantize_values
+
+
+def prepare_query(q, rotation, sketch, w: int):
+    """q [n, d] -> (q_rot = Pi q [n, d] or None for w == 0, q_sk = S q [n, m])."""
+    q = np.asarray(q, dtype=np.float64)
+    S = np.asarray(sketch, dtype=np.float64)
+    q_sk = q @ S.T
+    if w == 0:
+        return None, q_sk
+    Pi = np.asarray(rotation, dtype=np.float64)
+    return q @ Pi.T, q_sk
+
+
+def scores(q, key_rows, rotation, sketch, centroids, w: int):
+    """<q_h, k^_t> for queries q [G, d] against dequantised keys; [G, T]."""
+    idx, bits, norm, rnorm = key_rows
+    k_hat = dequantize_keys(idx, bits, norm, rnorm, rotation, sketch, centroids, w)
+    return np.asarray(q, dtype=np.float64) @ k_hat.T
+
+
+def softmax_attention(s, v_hat, softmax_scale: float):
+    """Two-pass softmax over tokens; s [G, T], v_hat [T, d] -> out [G, d]."""
+    logits = np.asarray(s, dtype=np.float64) * softmax_scale
+    mx = np.max(logits, axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    p = e / np.sum(e, axis=1, keepdims=True)
+    return p @ np.asarray(v_hat, dtype=np.float64)
+
+
+def decode_slot(q, key_rows, value_rows, rotation, sketch, centroids, w: int,
+                softmax_scale=None, group: int = 32):
+    """Decode attention of the G query heads that share one KV slot.
+
+    q [G, d]; key_rows = (idx, bits, norm, rnorm); value_rows = (codes, scale, vmin).
+    Returns (scores [G, T], out [G, d])."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / np.sqrt(d)
+    s = scores(q, key_rows, rotation, sketch, centroids, w)
+    v_hat = dequantize_values(*value_rows, group=group)
+    return s, softmax_attention(s, v_hat, softmax_scale)
