@@ -1,0 +1,213 @@
+/*
+ * aqkv.h -- compressed KV-cache key quantisation and decode attention on
+ * packed bits, for AMD Instinct MI355X (gfx950).  C ABI of libaqkv.so.
+ *
+ * The method is the one the TurboQuant article (kwkr.cn, "TurboQuant:
+ * near-optimal KV cache quantization for LLM inference (3-bit keys, 2-bit
+ * values)") describes, plus the pure-QJL keys with per-layer sketch size of
+ * the A-QJL article (zingnex.cn, "A-QJL: adaptive layer-wise KV cache
+ * compression"):
+ *
+ *   keys    (TurboQuant §二, §五): n = ||x||; y = Pi (x / n); idx_j = number of
+ *           decision boundaries below y_j (w = b - 1 Lloyd-Max bits per
+ *           coordinate); r = x - n Pi^T c[idx]; signs of S r (one bit per
+ *           sketch row); gamma = ||r||.  w = 0 is pure QJL (A-QJL, section
+ *           "QJL"): signs of S x, only n stored.
+ *   values  (TurboQuant component table, §七): per token, per group of
+ *           `value_group` contiguous channels, min-max quantisation to
+ *           `value_bits` bits.
+ *   decode  (TurboQuant §五, §六): the query is rotated (Pi q) and sketched
+ *           (S q) once; the score of cached token t is
+ *             n_t <Pi q, c[idx_t]> + sqrt(pi/2)/m * gamma_t * <S q, 2 bits_t - 1>
+ *           (an unbiased estimate of <q, k_t>), computed on the packed bits;
+ *           softmax(score * softmax_scale) weights the dequantised values
+ *           code * scale + min.  No fp key is ever materialised.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Pointers marked (dev) are device memory on the current HIP device, owned
+ *   by the caller; they must stay valid until the enqueued work finishes.
+ *   Pointers marked (host) are host memory.  The library allocates nothing
+ *   and keeps no state between calls.
+ * - Compute calls only enqueue work on `stream` (a hipStream_t; NULL = the
+ *   default stream) and never synchronise.  Calls on the same stream are
+ *   ordered; concurrent calls that write the same cache rows race.
+ * - Arguments are validated on the host before anything is enqueued.  On an
+ *   error the call returns a negative aqkv_status and writes nothing.  A
+ *   launch failure reported by the HIP runtime returns AQKV_ERR_HIP.  Nothing
+ *   prints, aborts or throws across this interface.
+ *
+ * Cache layout (one plane per array, rows contiguous; slot s = b * H + h of
+ * the K/V view; token t of slot s is row s * capacity + t):
+ *   key_codes  w * d / 8 bytes per row: w bit-planes of d/8 bytes each; plane p
+ *              holds bit p of every coordinate's index, coordinate j at bit
+ *              j % 8 of byte j / 8.  (NULL allowed when w == 0.)
+ *   key_signs  m / 8 bytes per row, sketch row i at bit i % 8 of byte i / 8;
+ *              bit 1 = non-negative projection.
+ *   key_norm   fp32 ||x|| per row.
+ *   key_rnorm  fp32 ||r|| per row (NULL allowed when w == 0).
+ *   val_codes  d * value_bits / 8 bytes per row, LSB-first bitstream: channel
+ *              j occupies bits [value_bits*j, value_bits*(j+1)).
+ *   val_scale  fp32 [d / value_group] per row.
+ *   val_min    fp32 [d / value_group] per row.
+ * Every plane pointer must be 16-byte aligned.
+ */
+#ifndef AQKV_H
+#define AQKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AQKV_OK = 0,
+  AQKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  AQKV_ERR_SHAPE = -2,       /* unsupported or inconsistent sizes / bit widths */
+  AQKV_ERR_ALIGN = -3,       /* a pointer or stride breaks the alignment rules */
+  AQKV_ERR_CAPACITY = -4,    /* token_offset + tokens exceeds the cache capacity */
+  AQKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+  AQKV_ERR_DTYPE = -6,       /* unknown element type */
+  AQKV_ERR_HIP = -7,         /* the HIP runtime reported an error */
+  AQKV_ERR_UNSUPPORTED = -8  /* valid request this build does not implement */
+} aqkv_status;
+
+typedef enum { AQKV_FP32 = 0, AQKV_BF16 = 1 } aqkv_dtype;
+
+/* Codec configuration, fixed per cache. */
+typedef struct {
+  int32_t head_dim;    /* d: 64, 128 or 256 */
+  int32_t mse_bits;    /* w = b - 1 Lloyd-Max bits per coordinate, 0..3 (0 = pure QJL) */
+  int32_t sketch_dim;  /* m: QJL sketch rows, multiple of 64, 64..1024 (m = d for TurboQuant keys) */
+  int32_t value_bits;  /* 2 or 4 */
+  int32_t value_group; /* channels per value group: 32 */
+} aqkv_config;
+
+/* Per-layer parameters (TurboQuant §二: Pi from a QR decomposition and S
+ * Gaussian, one seed per layer; Lloyd-Max codebook computed offline). */
+typedef struct {
+  const float *rotation;   /* (dev) Pi [d][d] row-major fp32, y = Pi x; required iff mse_bits > 0 */
+  const float *sketch;     /* (dev) S [m][d] row-major fp32, z = S r */
+  const float *centroids;  /* (dev) [2^w] ascending fp32; required iff mse_bits > 0 */
+  const float *boundaries; /* (dev) [2^w - 1] ascending fp32; required iff mse_bits > 0 */
+} aqkv_layer;
+
+/* The compressed cache planes (layout above). */
+typedef struct {
+  uint8_t *key_codes;
+  uint8_t *key_signs;
+  float *key_norm;
+  float *key_rnorm;
+  uint8_t *val_codes;
+  float *val_scale;
+  float *val_min;
+  int64_t n_slots;   /* batch * kv heads */
+  int64_t capacity;  /* token rows per slot */
+} aqkv_cache;
+
+/* A strided 4-D K or V tensor [batch][heads][tokens][d] in device memory.
+ * Element (b, h, t, j) is at data + (b*batch_stride + h*head_stride +
+ * t*token_stride + j) elements: channels are contiguous.  Strides must be
+ * multiples of 8 elements. */
+typedef struct {
+  const void *data;   /* (dev) */
+  aqkv_dtype dtype;
+  int64_t batch, heads, tokens;
+  int64_t batch_stride, head_stride, token_stride;
+} aqkv_kv_view;
+
+/* Bytes per token row of each cache plane for a configuration. */
+typedef struct {
+  int64_t key_codes, key_signs, key_norm, key_rnorm, val_codes, val_scale, val_min;
+} aqkv_row_bytes;
+
+/* ---------------------------------------------------------------- host only */
+
+/* Human-readable name of a status code (static string). */
+const char *aqkv_status_string(aqkv_status status);
+
+/* Checks a configuration and reports the per-row byte sizes of every plane
+ * (out may be NULL to only validate).  AQKV_ERR_SHAPE for unsupported
+ * head_dim / mse_bits / sketch_dim / value_bits / value_group. */
+aqkv_status aqkv_cache_layout(const aqkv_config *cfg, aqkv_row_bytes *out);
+
+/* Lloyd-Max codebook for one coordinate of a uniformly random unit vector in
+ * R^head_dim (TurboQuant §二: the rotated coordinates share one scaled-Beta
+ * law; the quantiser is its continuous 1-D k-means).  Computed on the host
+ * in double precision; writes 2^bits ascending centroids and the 2^bits - 1
+ * midpoint boundaries, both rounded to fp32.  (host) outputs.
+ * bits in 1..4, head_dim in 3..4096. */
+aqkv_status aqkv_build_codebook(int32_t head_dim, int32_t bits, float *centroids, float *boundaries);
+
+/* Random orthogonal rotation from a Gaussian matrix (TurboQuant §二, "QR
+ * decomposition"): Householder QR of gaussian [d][d] (host, row-major
+ * double), Pi = Q diag(sign(diag R)), written row-major fp32 to rotation
+ * (host).  d in 1..4096. */
+aqkv_status aqkv_build_rotation(int32_t d, const double *gaussian, float *rotation);
+
+/* Workspace bytes aqkv_quantize_keys needs for this configuration. */
+size_t aqkv_quantize_keys_workspace_bytes(const aqkv_config *cfg);
+
+/* Workspace bytes aqkv_decode_attention needs for these sizes. */
+size_t aqkv_decode_workspace_bytes(const aqkv_config *cfg, int32_t batch, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int64_t context_len);
+
+/* -------------------------------------------------------------- GPU compute */
+
+/* Key quantisation (TurboQuant §二 three-stage pipeline; §五 quantize() ->
+ * MSE indices, QJL sign bytes, residual norm, original norm; A-QJL pure QJL
+ * when mse_bits == 0).  Quantises tokens [0, k->tokens) of every slot of k
+ * into cache rows [token_offset, token_offset + k->tokens) (chunked append,
+ * TurboQuant §六 CompressedKVStore).  k->batch * k->heads must equal
+ * cache->n_slots; the key element type is fp32 or bf16.  Writes key_codes,
+ * key_signs, key_norm and key_rnorm; workspace is scratch of at least
+ * aqkv_quantize_keys_workspace_bytes(cfg) bytes (dev, 256-byte aligned).
+ * A zero key stores n = 0, gamma = 0, the index of y = 0 and all sign bits 1. */
+aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer,
+                               const aqkv_kv_view *k, int64_t token_offset,
+                               const aqkv_cache *cache, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Value quantisation (TurboQuant component table and §七: conventional
+ * min-max grouped quantisation with bit packing).  Per token, per group of
+ * value_group contiguous channels: min, scale = (max - min) / (2^vb - 1),
+ * code = clamp(rint((v - min) / scale), 0, 2^vb - 1), all in IEEE fp32; code 0
+ * when scale == 0.  Same view / offset rules as aqkv_quantize_keys; writes
+ * val_codes, val_scale, val_min. */
+aqkv_status aqkv_quantize_values(const aqkv_config *cfg, const aqkv_kv_view *v, int64_t token_offset,
+                                 const aqkv_cache *cache, void *stream);
+
+/* Query preparation (TurboQuant §六: the query is rotated, q Pi^T, and
+ * pre-sketched, q S^T, once per query).  q is [n_q][d] (dev, contiguous, fp32
+ * or bf16); writes q_rot = Pi q [n_q][d] (dev fp32; may be NULL when
+ * mse_bits == 0) and q_sketch = S q [n_q][m] (dev fp32). */
+aqkv_status aqkv_prepare_query(const aqkv_config *cfg, const aqkv_layer *layer, const void *q,
+                               aqkv_dtype dtype, int64_t n_q, float *q_rot, float *q_sketch,
+                               void *stream);
+
+/* Decode attention on the packed cache (TurboQuant §五 estimator, §六 fused
+ * decode with online softmax).  For every batch b and query head hq (kv head
+ * hq / (n_q_heads / n_kv_heads), slot b * n_kv_heads + that head) over
+ * cache rows [0, context_len):
+ *   score_t = n_t <q_rot, c[idx_t]> + sqrt(pi/2)/m gamma_t <q_sketch, 2 bits_t - 1>
+ *   out     = sum_t softmax_t(score * softmax_scale) (code_t * scale_t + min_t)
+ * q_rot [batch][n_q_heads][d] and q_sketch [batch][n_q_heads][m] come from
+ * aqkv_prepare_query (dev fp32).  out is [batch][n_q_heads][d] (dev fp32).
+ * scores, if not NULL, receives the unscaled estimates [batch][n_q_heads]
+ * [context_len] (dev fp32).  context_len == 0 writes out = 0.  workspace
+ * (dev, 256-byte aligned) must hold aqkv_decode_workspace_bytes(...) bytes.
+ * cache->n_slots must equal batch * n_kv_heads and n_q_heads must be a
+ * multiple of n_kv_heads. */
+aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *layer,
+                                  const aqkv_cache *cache, int32_t batch, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int64_t context_len, const float *q_rot,
+                                  const float *q_sketch, float softmax_scale, float *scores,
+                                  float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AQKV_H */

@@ -1,0 +1,275 @@
+"""Thin ctypes binding of libaqkv.so (include/aqkv.h).
+
+Argument marshalling only: every step of the method runs in the library's HIP
+kernels.  torch tensors are used for device memory and the current stream;
+host-side numpy arrays for the host-only builders.  A missing library is an
+error (``AqkvError``), never a fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("AQKV_LIB", os.path.join(_HERE, "libaqkv.so"))
+
+STATUS = {
+    0: "AQKV_OK", -1: "AQKV_ERR_NULL", -2: "AQKV_ERR_SHAPE", -3: "AQKV_ERR_ALIGN",
+    -4: "AQKV_ERR_CAPACITY", -5: "AQKV_ERR_WORKSPACE", -6: "AQKV_ERR_DTYPE",
+    -7: "AQKV_ERR_HIP", -8: "AQKV_ERR_UNSUPPORTED",
+}
+FP32, BF16 = 0, 1
+
+
+class AqkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class Config(C.Structure):
+    _fields_ = [("head_dim", C.c_int32), ("mse_bits", C.c_int32), ("sketch_dim", C.c_int32),
+                ("value_bits", C.c_int32), ("value_group", C.c_int32)]
+
+
+class LayerParams(C.Structure):
+    _fields_ = [("rotation", C.c_void_p), ("sketch", C.c_void_p), ("centroids", C.c_void_p),
+                ("boundaries", C.c_void_p)]
+
+
+class CacheDesc(C.Structure):
+    _fields_ = [("key_codes", C.c_void_p), ("key_signs", C.c_void_p), ("key_norm", C.c_void_p),
+                ("key_rnorm", C.c_void_p), ("val_codes", C.c_void_p), ("val_scale", C.c_void_p),
+                ("val_min", C.c_void_p), ("n_slots", C.c_int64), ("capacity", C.c_int64)]
+
+
+class KvView(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("dtype", C.c_int), ("batch", C.c_int64), ("heads", C.c_int64),
+                ("tokens", C.c_int64), ("batch_stride", C.c_int64), ("head_stride", C.c_int64),
+                ("token_stride", C.c_int64)]
+
+
+class RowBytes(C.Structure):
+    _fields_ = [("key_codes", C.c_int64), ("key_signs", C.c_int64), ("key_norm", C.c_int64),
+                ("key_rnorm", C.c_int64), ("val_codes", C.c_int64), ("val_scale", C.c_int64),
+                ("val_min", C.c_int64)]
+
+
+_P = C.POINTER
+_SIGS = {
+    "aqkv_status_string": (C.c_char_p, [C.c_int]),
+    "aqkv_cache_layout": (C.c_int, [_P(Config), _P(RowBytes)]),
+    "aqkv_build_codebook": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
+    "aqkv_build_rotation": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p]),
+    "aqkv_quantize_keys_workspace_bytes": (C.c_size_t, [_P(Config)]),
+    "aqkv_decode_workspace_bytes": (C.c_size_t, [_P(Config), C.c_int32, C.c_int32, C.c_int32, C.c_int64]),
+    "aqkv_quantize_keys": (C.c_int, [_P(Config), _P(LayerParams), _P(KvView), C.c_int64, _P(CacheDesc),
+                                     C.c_void_p, C.c_size_t, C.c_void_p]),
+    "aqkv_quantize_values": (C.c_int, [_P(Config), _P(KvView), C.c_int64, _P(CacheDesc), C.c_void_p]),
+    "aqkv_prepare_query": (C.c_int, [_P(Config), _P(LayerParams), C.c_void_p, C.c_int, C.c_int64,
+                                     C.c_void_p, C.c_void_p, C.c_void_p]),
+    "aqkv_decode_attention": (C.c_int, [_P(Config), _P(LayerParams), _P(CacheDesc), C.c_int32, C.c_int32,
+                                        C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_float,
+                                        C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+}
+
+_lib_handle = None
+
+
+def lib():
+    """The loaded libaqkv.so (raises AqkvError-compatible RuntimeError if it is not built)."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libaqkv.so not built at {LIB_PATH}; run "
+                               "`python -m kv_cache_compression_quantize_amd.build`")
+        h = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib_handle = h
+    return _lib_handle
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise AqkvError(st, where)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return C.c_void_p(stream)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return FP32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ----------------------------------------------------------------- host only
+
+def config(head_dim: int, mse_bits: int, sketch_dim: int, value_bits: int = 2, value_group: int = 32) -> Config:
+    return Config(head_dim, mse_bits, sketch_dim, value_bits, value_group)
+
+
+def cache_layout(cfg: Config) -> dict:
+    rb = RowBytes()
+    _check(lib().aqkv_cache_layout(C.byref(cfg), C.byref(rb)), "aqkv_cache_layout")
+    return {name: getattr(rb, name) for name, _ in RowBytes._fields_}
+
+
+def build_codebook(head_dim: int, bits: int):
+    """(centroids, boundaries) float32 numpy arrays, computed by the library on the host."""
+    c = np.zeros(1 << bits, dtype=np.float32)
+    t = np.zeros(max((1 << bits) - 1, 1), dtype=np.float32)
+    _check(lib().aqkv_build_codebook(head_dim, bits, c.ctypes.data, t.ctypes.data), "aqkv_build_codebook")
+    return c, t[: (1 << bits) - 1]
+
+
+def build_rotation(gaussian: np.ndarray) -> np.ndarray:
+    g = np.ascontiguousarray(gaussian, dtype=np.float64)
+    d = g.shape[0]
+    assert g.shape == (d, d)
+    out = np.zeros((d, d), dtype=np.float32)
+    _check(lib().aqkv_build_rotation(d, g.ctypes.data, out.ctypes.data), "aqkv_build_rotation")
+    return out
+
+
+def quantize_keys_workspace_bytes(cfg: Config) -> int:
+    return int(lib().aqkv_quantize_keys_workspace_bytes(C.byref(cfg)))
+
+
+def decode_workspace_bytes(cfg: Config, batch: int, n_q_heads: int, n_kv_heads: int, context_len: int) -> int:
+    return int(lib().aqkv_decode_workspace_bytes(C.byref(cfg), batch, n_q_heads, n_kv_heads, context_len))
+
+
+# ------------------------------------------------------------ device objects
+
+@dataclass
+class Layer:
+    """Device copies of one layer's parameters (fp32 torch tensors)."""
+    rotation: object = None
+    sketch: object = None
+    centroids: object = None
+    boundaries: object = None
+
+    def desc(self) -> LayerParams:
+        return LayerParams(_ptr(self.rotation), _ptr(self.sketch), _ptr(self.centroids), _ptr(self.boundaries))
+
+
+@dataclass
+class Cache:
+    """The seven cache planes as uint8 / float32 torch tensors."""
+    cfg: Config
+    n_slots: int
+    capacity: int
+    key_codes: object
+    key_signs: object
+    key_norm: object
+    key_rnorm: object
+    val_codes: object
+    val_scale: object
+    val_min: object
+
+    @staticmethod
+    def allocate(cfg: Config, n_slots: int, capacity: int, device="cuda") -> "Cache":
+        import torch
+        rb = cache_layout(cfg)
+        rows = n_slots * capacity
+
+        def u8(nb):
+            return torch.empty((rows, max(nb, 0)), dtype=torch.uint8, device=device) if nb > 0 else None
+
+        def f32(nb):
+            return torch.empty((rows, nb // 4), dtype=torch.float32, device=device) if nb > 0 else None
+
+        return Cache(cfg, n_slots, capacity, u8(rb["key_codes"]), u8(rb["key_signs"]),
+                     f32(rb["key_norm"]).view(-1), (f32(rb["key_rnorm"]).view(-1) if rb["key_rnorm"] else None),
+                     u8(rb["val_codes"]), f32(rb["val_scale"]), f32(rb["val_min"]))
+
+    def desc(self) -> CacheDesc:
+        return CacheDesc(_ptr(self.key_codes), _ptr(self.key_signs), _ptr(self.key_norm), _ptr(self.key_rnorm),
+                         _ptr(self.val_codes), _ptr(self.val_scale), _ptr(self.val_min), self.n_slots, self.capacity)
+
+
+def kv_view(t) -> KvView:
+    """View of a [B, H, T, d] tensor (any strides with contiguous channels)."""
+    assert t.dim() == 4 and t.stride(3) == 1
+    B, H, T, _ = t.shape
+    return KvView(_ptr(t), _dtype_code(t), B, H, T, t.stride(0), t.stride(1), t.stride(2))
+
+
+# ---------------------------------------------------------------- compute
+
+def quantize_keys(cfg: Config, layer: Layer, k, cache: Cache, token_offset: int = 0, workspace=None, stream=None):
+    v = kv_view(k)
+    ws_bytes = quantize_keys_workspace_bytes(cfg)
+    if workspace is None and ws_bytes > 0:
+        import torch
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=k.device)
+    st = lib().aqkv_quantize_keys(C.byref(cfg), C.byref(layer.desc()), C.byref(v), token_offset,
+                                  C.byref(cache.desc()), _ptr(workspace),
+                                  workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(st, "aqkv_quantize_keys")
+
+
+def quantize_values(cfg: Config, v, cache: Cache, token_offset: int = 0, stream=None):
+    view = kv_view(v)
+    _check(lib().aqkv_quantize_values(C.byref(cfg), C.byref(view), token_offset, C.byref(cache.desc()),
+                                      _stream(stream)), "aqkv_quantize_values")
+
+
+def prepare_query(cfg: Config, layer: Layer, q, q_rot=None, q_sketch=None, stream=None):
+    """q [..., d] -> (q_rot [..., d] or None when mse_bits == 0, q_sketch [..., m]) fp32."""
+    import torch
+    assert q.is_contiguous() and q.shape[-1] == cfg.head_dim
+    n_q = q.numel() // cfg.head_dim
+    lead = tuple(q.shape[:-1])
+    if q_sketch is None:
+        q_sketch = torch.empty(lead + (cfg.sketch_dim,), dtype=torch.float32, device=q.device)
+    if q_rot is None and cfg.mse_bits > 0:
+        q_rot = torch.empty(lead + (cfg.head_dim,), dtype=torch.float32, device=q.device)
+    _check(lib().aqkv_prepare_query(C.byref(cfg), C.byref(layer.desc()), _ptr(q), _dtype_code(q), n_q,
+                                    _ptr(q_rot), _ptr(q_sketch), _stream(stream)), "aqkv_prepare_query")
+    return q_rot, q_sketch
+
+
+def decode_attention(cfg: Config, layer: Layer, cache: Cache, batch: int, n_q_heads: int, n_kv_heads: int,
+                     context_len: int, q_rot, q_sketch, softmax_scale: Optional[float] = None,
+                     scores=None, out=None, workspace=None, stream=None):
+    import torch
+    dev = q_sketch.device
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(np.sqrt(cfg.head_dim))
+    if out is None:
+        out = torch.empty((batch, n_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    ws_bytes = decode_workspace_bytes(cfg, batch, n_q_heads, n_kv_heads, context_len)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    st = lib().aqkv_decode_attention(C.byref(cfg), C.byref(layer.desc()), C.byref(cache.desc()), batch,
+                                     n_q_heads, n_kv_heads, context_len, _ptr(q_rot), _ptr(q_sketch),
+                                     C.c_float(softmax_scale), _ptr(scores), _ptr(out), _ptr(workspace),
+                                     workspace.numel(), _stream(stream))
+    _check(st, "aqkv_decode_attention")
+    return out

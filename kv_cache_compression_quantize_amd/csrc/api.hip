@@ -1,0 +1,319 @@
+// C entry points of libaqkv.so: argument validation on the host, then the
+// kernel launchers.  Validation never touches the HIP runtime, so a call that
+// fails validation works (and returns its status) on a machine without a GPU.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+using namespace aqkv;
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+aqkv_status check_config(const aqkv_config *cfg) {
+  if (!cfg) return AQKV_ERR_NULL;
+  const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
+  if (d != 64 && d != 128 && d != 256) return AQKV_ERR_SHAPE;
+  if (w < 0 || w > 3) return AQKV_ERR_SHAPE;
+  if (m < 64 || m > kMaxSketch || m % 64 != 0) return AQKV_ERR_SHAPE;
+  if (cfg->value_bits != 2 && cfg->value_bits != 4) return AQKV_ERR_SHAPE;
+  if (cfg->value_group != 32) return AQKV_ERR_SHAPE;
+  return AQKV_OK;
+}
+
+aqkv_status check_view(const aqkv_kv_view *v, int d) {
+  if (!v) return AQKV_ERR_NULL;
+  if (v->dtype != AQKV_FP32 && v->dtype != AQKV_BF16) return AQKV_ERR_DTYPE;
+  if (v->batch < 0 || v->heads < 0 || v->tokens < 0) return AQKV_ERR_SHAPE;
+  if (v->tokens > 0 && v->batch * v->heads > 0 && !v->data) return AQKV_ERR_NULL;
+  if (v->batch_stride < 0 || v->head_stride < 0 || v->token_stride < d) return AQKV_ERR_SHAPE;
+  if (v->batch_stride % 8 || v->head_stride % 8 || v->token_stride % 8) return AQKV_ERR_ALIGN;
+  if (v->data && !aligned(v->data, 16)) return AQKV_ERR_ALIGN;
+  return AQKV_OK;
+}
+
+aqkv_status check_cache_shape(const aqkv_cache *c) {
+  if (!c) return AQKV_ERR_NULL;
+  if (c->n_slots < 0 || c->capacity < 0) return AQKV_ERR_SHAPE;
+  return AQKV_OK;
+}
+
+aqkv_status check_plane(const void *p) {
+  if (!p) return AQKV_ERR_NULL;
+  if (!aligned(p, 16)) return AQKV_ERR_ALIGN;
+  return AQKV_OK;
+}
+
+aqkv_status hip_status(hipError_t e) { return e == hipSuccess ? AQKV_OK : AQKV_ERR_HIP; }
+
+size_t key_workspace_bytes(int d, int w, int m) {
+  // the [m][d] fp32 projection S Pi^T used for the residual sketch
+  return w > 0 ? round_up(static_cast<size_t>(m) * d * sizeof(float), 256) : 0;
+}
+
+}  // namespace
+
+namespace aqkv {
+
+DecodePlan decode_plan(int d, int64_t n_slots, int g, int64_t context) {
+  constexpr int64_t kChunk = 256;      // tokens per block iteration
+  constexpr int64_t kTargetBlocks = 2048;
+  DecodePlan p{};
+  const int64_t chunks = (context + kChunk - 1) / kChunk;
+  int64_t split = n_slots > 0 ? (kTargetBlocks + n_slots - 1) / n_slots : 1;
+  if (split > chunks) split = chunks;
+  if (split < 1) split = 1;
+  const int64_t per_split_chunks = chunks > 0 ? (chunks + split - 1) / split : 1;
+  p.split_tokens = per_split_chunks * kChunk;
+  p.n_split = static_cast<int>(chunks > 0 ? (chunks + per_split_chunks - 1) / per_split_chunks : 1);
+  const size_t heads = static_cast<size_t>(n_slots) * g;
+  p.acc_bytes = round_up(heads * p.n_split * d * sizeof(float), 256);
+  p.ml_bytes = round_up(heads * p.n_split * 2 * sizeof(float), 256);
+  p.total_bytes = p.acc_bytes + p.ml_bytes;
+  return p;
+}
+
+}  // namespace aqkv
+
+extern "C" {
+
+const char *aqkv_status_string(aqkv_status s) {
+  switch (s) {
+    case AQKV_OK: return "ok";
+    case AQKV_ERR_NULL: return "required pointer is NULL";
+    case AQKV_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case AQKV_ERR_ALIGN: return "misaligned pointer or stride";
+    case AQKV_ERR_CAPACITY: return "token range exceeds cache capacity";
+    case AQKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case AQKV_ERR_DTYPE: return "unknown element type";
+    case AQKV_ERR_HIP: return "HIP runtime error";
+    case AQKV_ERR_UNSUPPORTED: return "not supported by this build";
+  }
+  return "unknown status";
+}
+
+aqkv_status aqkv_cache_layout(const aqkv_config *cfg, aqkv_row_bytes *out) {
+  aqkv_status st = check_config(cfg);
+  if (st != AQKV_OK) return st;
+  if (out) {
+    const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
+    out->key_codes = static_cast<int64_t>(w) * d / 8;
+    out->key_signs = m / 8;
+    out->key_norm = 4;
+    out->key_rnorm = w > 0 ? 4 : 0;
+    out->val_codes = static_cast<int64_t>(d) * cfg->value_bits / 8;
+    out->val_scale = 4 * (d / cfg->value_group);
+    out->val_min = 4 * (d / cfg->value_group);
+  }
+  return AQKV_OK;
+}
+
+size_t aqkv_quantize_keys_workspace_bytes(const aqkv_config *cfg) {
+  if (check_config(cfg) != AQKV_OK) return 0;
+  return key_workspace_bytes(cfg->head_dim, cfg->mse_bits, cfg->sketch_dim);
+}
+
+size_t aqkv_decode_workspace_bytes(const aqkv_config *cfg, int32_t batch, int32_t n_q_heads,
+                                   int32_t n_kv_heads, int64_t context_len) {
+  if (check_config(cfg) != AQKV_OK) return 0;
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads || context_len < 0) return 0;
+  const int64_t n_slots = static_cast<int64_t>(batch) * n_kv_heads;
+  return decode_plan(cfg->head_dim, n_slots, n_q_heads / n_kv_heads, context_len).total_bytes;
+}
+
+aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_kv_view *k,
+                               int64_t token_offset, const aqkv_cache *cache, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  aqkv_status st = check_config(cfg);
+  if (st != AQKV_OK) return st;
+  if (!layer) return AQKV_ERR_NULL;
+  const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
+  if ((st = check_view(k, d)) != AQKV_OK) return st;
+  if ((st = check_cache_shape(cache)) != AQKV_OK) return st;
+  if (k->batch * k->heads != cache->n_slots) return AQKV_ERR_SHAPE;
+  if (token_offset < 0) return AQKV_ERR_SHAPE;
+  if (token_offset + k->tokens > cache->capacity) return AQKV_ERR_CAPACITY;
+  if ((st = check_plane(layer->sketch)) != AQKV_OK) return st;
+  if (w > 0) {
+    if ((st = check_plane(layer->rotation)) != AQKV_OK) return st;
+    if (!layer->centroids || !layer->boundaries) return AQKV_ERR_NULL;
+  }
+  if ((st = check_plane(cache->key_signs)) != AQKV_OK) return st;
+  if ((st = check_plane(cache->key_norm)) != AQKV_OK) return st;
+  if (w > 0) {
+    if ((st = check_plane(cache->key_codes)) != AQKV_OK) return st;
+    if ((st = check_plane(cache->key_rnorm)) != AQKV_OK) return st;
+  }
+  const size_t need = key_workspace_bytes(d, w, m);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return AQKV_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 256)) return AQKV_ERR_ALIGN;
+  if (k->tokens == 0 || cache->n_slots == 0) return AQKV_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float *proj = layer->sketch;
+  if (w > 0) {
+    float *p = static_cast<float *>(workspace);
+    hipError_t e = launch_make_projection(layer->sketch, layer->rotation, p, m, d, s);
+    if (e != hipSuccess) return AQKV_ERR_HIP;
+    proj = p;
+  }
+  KeyJob job{};
+  job.k = k->data;
+  job.dtype = k->dtype;
+  job.heads = k->heads;
+  job.batch_stride = k->batch_stride;
+  job.head_stride = k->head_stride;
+  job.token_stride = k->token_stride;
+  job.n_slots = cache->n_slots;
+  job.n_tokens = k->tokens;
+  job.token_offset = token_offset;
+  job.capacity = cache->capacity;
+  job.d = d;
+  job.w = w;
+  job.m = m;
+  job.rotation = layer->rotation;
+  job.proj = proj;
+  job.centroids = layer->centroids;
+  job.boundaries = layer->boundaries;
+  job.codes = cache->key_codes;
+  job.signs = cache->key_signs;
+  job.norm = cache->key_norm;
+  job.rnorm = cache->key_rnorm;
+  return hip_status(launch_quantize_keys(job, s));
+}
+
+aqkv_status aqkv_quantize_values(const aqkv_config *cfg, const aqkv_kv_view *v, int64_t token_offset,
+                                 const aqkv_cache *cache, void *stream) {
+  aqkv_status st = check_config(cfg);
+  if (st != AQKV_OK) return st;
+  const int d = cfg->head_dim;
+  if ((st = check_view(v, d)) != AQKV_OK) return st;
+  if ((st = check_cache_shape(cache)) != AQKV_OK) return st;
+  if (v->batch * v->heads != cache->n_slots) return AQKV_ERR_SHAPE;
+  if (token_offset < 0) return AQKV_ERR_SHAPE;
+  if (token_offset + v->tokens > cache->capacity) return AQKV_ERR_CAPACITY;
+  if ((st = check_plane(cache->val_codes)) != AQKV_OK) return st;
+  if ((st = check_plane(cache->val_scale)) != AQKV_OK) return st;
+  if ((st = check_plane(cache->val_min)) != AQKV_OK) return st;
+  if (v->tokens == 0 || cache->n_slots == 0) return AQKV_OK;
+  ValueJob job{};
+  job.v = v->data;
+  job.dtype = v->dtype;
+  job.heads = v->heads;
+  job.batch_stride = v->batch_stride;
+  job.head_stride = v->head_stride;
+  job.token_stride = v->token_stride;
+  job.n_slots = cache->n_slots;
+  job.n_tokens = v->tokens;
+  job.token_offset = token_offset;
+  job.capacity = cache->capacity;
+  job.d = d;
+  job.vb = cfg->value_bits;
+  job.group = cfg->value_group;
+  job.codes = cache->val_codes;
+  job.scale = cache->val_scale;
+  job.vmin = cache->val_min;
+  return hip_status(launch_quantize_values(job, static_cast<hipStream_t>(stream)));
+}
+
+aqkv_status aqkv_prepare_query(const aqkv_config *cfg, const aqkv_layer *layer, const void *q,
+                               aqkv_dtype dtype, int64_t n_q, float *q_rot, float *q_sketch,
+                               void *stream) {
+  aqkv_status st = check_config(cfg);
+  if (st != AQKV_OK) return st;
+  if (!layer) return AQKV_ERR_NULL;
+  if (dtype != AQKV_FP32 && dtype != AQKV_BF16) return AQKV_ERR_DTYPE;
+  if (n_q < 0) return AQKV_ERR_SHAPE;
+  const int w = cfg->mse_bits;
+  if (n_q == 0) return AQKV_OK;
+  if (!q || !q_sketch || !layer->sketch) return AQKV_ERR_NULL;
+  if (w > 0 && (!q_rot || !layer->rotation)) return AQKV_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(q_sketch, 16) || (q_rot && !aligned(q_rot, 16))) return AQKV_ERR_ALIGN;
+  QueryJob job{};
+  job.q = q;
+  job.dtype = dtype;
+  job.n_q = n_q;
+  job.d = cfg->head_dim;
+  job.w = w;
+  job.m = cfg->sketch_dim;
+  job.rotation = layer->rotation;
+  job.sketch = layer->sketch;
+  job.q_rot = w > 0 ? q_rot : nullptr;
+  job.q_sketch = q_sketch;
+  return hip_status(launch_prepare_query(job, static_cast<hipStream_t>(stream)));
+}
+
+aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache,
+                                  int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t context_len,
+                                  const float *q_rot, const float *q_sketch, float softmax_scale,
+                                  float *scores, float *out, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  aqkv_status st = check_config(cfg);
+  if (st != AQKV_OK) return st;
+  if (!layer) return AQKV_ERR_NULL;
+  if ((st = check_cache_shape(cache)) != AQKV_OK) return st;
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || context_len < 0) return AQKV_ERR_SHAPE;
+  if (n_q_heads % n_kv_heads) return AQKV_ERR_SHAPE;
+  const int g = n_q_heads / n_kv_heads;
+  if (g > kMaxQPerKv) return AQKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(batch) * n_kv_heads != cache->n_slots) return AQKV_ERR_SHAPE;
+  if (context_len > cache->capacity) return AQKV_ERR_CAPACITY;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return AQKV_ERR_SHAPE;
+  const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
+  if (!decode_supported(d, w, g, m, cfg->value_bits)) return AQKV_ERR_UNSUPPORTED;
+  if (batch == 0) return AQKV_OK;
+  if (!out || !q_sketch) return AQKV_ERR_NULL;
+  if (w > 0 && (!q_rot || !layer->centroids)) return AQKV_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q_sketch, 16) || (q_rot && !aligned(q_rot, 16)) ||
+      (scores && !aligned(scores, 16)))
+    return AQKV_ERR_ALIGN;
+  if (context_len > 0) {
+    if ((st = check_plane(cache->key_signs)) != AQKV_OK) return st;
+    if ((st = check_plane(cache->key_norm)) != AQKV_OK) return st;
+    if (w > 0) {
+      if ((st = check_plane(cache->key_codes)) != AQKV_OK) return st;
+      if ((st = check_plane(cache->key_rnorm)) != AQKV_OK) return st;
+    }
+    if ((st = check_plane(cache->val_codes)) != AQKV_OK) return st;
+    if ((st = check_plane(cache->val_scale)) != AQKV_OK) return st;
+    if ((st = check_plane(cache->val_min)) != AQKV_OK) return st;
+  }
+  const DecodePlan plan = decode_plan(d, cache->n_slots, g, context_len);
+  if (!workspace || workspace_bytes < plan.total_bytes) return AQKV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return AQKV_ERR_ALIGN;
+
+  DecodeJob job{};
+  job.d = d;
+  job.w = w;
+  job.m = m;
+  job.vb = cfg->value_bits;
+  job.group = cfg->value_group;
+  job.n_slots = cache->n_slots;
+  job.capacity = cache->capacity;
+  job.context = context_len;
+  job.g = g;
+  job.n_split = plan.n_split;
+  job.split_tokens = plan.split_tokens;
+  job.centroids = layer->centroids;
+  job.codes = cache->key_codes;
+  job.signs = cache->key_signs;
+  job.norm = cache->key_norm;
+  job.rnorm = cache->key_rnorm;
+  job.vcodes = cache->val_codes;
+  job.vscale = cache->val_scale;
+  job.vmin = cache->val_min;
+  job.q_rot = q_rot;
+  job.q_sketch = q_sketch;
+  job.softmax_scale = softmax_scale;
+  job.scores = scores;
+  job.out = out;
+  job.part_acc = static_cast<float *>(workspace);
+  job.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.acc_bytes);
+  return hip_status(launch_decode(job, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,274 @@
+"""GPU parity: every HIP entry point, called through the C ABI, against the
+oracle on the same seeded inputs, at sizes the oracle finishes in seconds that
+still span several tiles and a ragged tail.
+
+Bars: packed codes and sign bits bit-exact outside the 1e-5 decision-boundary
+window (mismatch rate inside the window reported); value codes, scales and
+minima bit-exact (both sides decide them in IEEE fp32); norms to fp32
+rounding; scores within 1e-3 relative; attention outputs within 2e-3 absolute.
+"""
+import numpy as np
+import pytest
+
+from kv_cache_compression_quantize_amd import aqkv, inputs
+from oracle import attention as oatt
+from oracle import layout as olay
+from oracle import values as ovals
+
+from gpu_helpers import (OUT_ATOL, SCORE_RTOL, cfg_of, compare_keys, device_layer, host_layer,
+                         oracle_rows, read_planes, say, score_err, to_device_kv, torch_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _kv(B, H, T, d, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, H, T, d)) * scale).astype(np.float32)
+
+
+def _as_dtype(x, dtype):
+    return inputs.bf16_bits_to_f32(inputs.to_bf16_bits(x)) if dtype == "bf16" else x
+
+
+KEY_CASES = [
+    (128, 2, 128, "bf16"), (128, 2, 128, "fp32"), (256, 3, 256, "bf16"), (128, 0, 192, "bf16"),
+    (128, 0, 512, "bf16"), (64, 1, 64, "fp32"), (128, 1, 128, "bf16"), (128, 3, 128, "bf16"),
+    (128, 2, 256, "bf16"), (256, 0, 384, "fp32"),
+]
+
+
+@pytest.mark.parametrize("d,w,m,dtype", KEY_CASES)
+def test_quantize_keys_parity(d, w, m, dtype):
+    torch, dev = torch_dev()
+    say("quantize_keys", d, w, m, dtype)
+    B, H, T = 2, 2, 1000
+    k = _as_dtype(_kv(B, H, T, d, seed=d + w + m), dtype)
+    k[0, 0, 5] = 0.0                     # a zero key
+    k[1, 1, 7] *= 1024.0                 # a large one (power of two: stays exactly representable)
+    hl = host_layer(d, w, m, layer=1)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    cache = aqkv.Cache.allocate(cfg, B * H, T + 24)
+    aqkv.quantize_keys(cfg, layer, to_device_kv(k, dtype), cache, token_offset=24)
+    torch.cuda.synchronize()
+    tot_win = tot_mis_win = 0
+    for s in range(B * H):
+        b, h = divmod(s, H)
+        gpu = read_planes(cache, s, 24, 24 + T)
+        qk, kr, _, _ = oracle_rows(hl, k[b, h], np.zeros((T, d), np.float32))
+        par = compare_keys(hl, k[b, h], qk, gpu)
+        assert par.idx_mismatch_outside == 0, par
+        assert par.sign_mismatch_outside == 0, par
+        tot_win += par.idx_in_window
+        tot_mis_win += par.idx_mismatch_in_window
+        np.testing.assert_allclose(gpu["norm"], qk.norm, rtol=2e-6, atol=0)
+        if w > 0:
+            clean = (olay.unpack_code_planes(gpu["codes"], d, w) == qk.idx).all(axis=1)
+            np.testing.assert_allclose(gpu["rnorm"][clean], qk.rnorm[clean], rtol=5e-5, atol=1e-30)
+        if s == 0:
+            assert gpu["norm"][5] == 0.0 and np.all(gpu["signs"][5] == 0xFF)
+            if w > 0:
+                assert gpu["rnorm"][5] == 0.0
+    say(f"index window: {tot_win} coords, {tot_mis_win} differ inside it")
+
+
+@pytest.mark.parametrize("d,vb,dtype", [(128, 2, "bf16"), (128, 2, "fp32"), (256, 2, "bf16"), (64, 4, "fp32"),
+                                        (128, 4, "bf16")])
+def test_quantize_values_bit_exact(d, vb, dtype):
+    torch, dev = torch_dev()
+    say("quantize_values", d, vb, dtype)
+    B, H, T = 2, 3, 777
+    v = _as_dtype(_kv(B, H, T, d, seed=7 + d + vb, scale=3.0), dtype)
+    v[0, 0, 3, :32] = 1.25                # constant group
+    v[1, 2, 9, 32:64] = -0.0
+    hl = host_layer(d, 2, d)
+    cfg = cfg_of(hl, vb)
+    cache = aqkv.Cache.allocate(cfg, B * H, T)
+    aqkv.quantize_values(cfg, to_device_kv(v, dtype), cache)
+    torch.cuda.synchronize()
+    for s in range(B * H):
+        b, h = divmod(s, H)
+        gpu = read_planes(cache, s, 0, T)
+        vc, vs, vm = ovals.quantize_values(v[b, h], vb)
+        np.testing.assert_array_equal(gpu["vcodes"], olay.pack_value_codes(vc, vb))
+        np.testing.assert_array_equal(gpu["vscale"].view(np.uint32), vs.view(np.uint32))
+        np.testing.assert_array_equal(gpu["vmin"].view(np.uint32), vm.view(np.uint32))
+
+
+def test_chunked_append_matches_one_call():
+    torch, dev = torch_dev()
+    say("chunked append")
+    d, w, m = 128, 2, 128
+    B, H, T = 1, 2, 700
+    k = _as_dtype(_kv(B, H, T, d, seed=3), "bf16")
+    v = _as_dtype(_kv(B, H, T, d, seed=4), "bf16")
+    hl = host_layer(d, w, m)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    kd, vd = to_device_kv(k, "bf16"), to_device_kv(v, "bf16")
+    one = aqkv.Cache.allocate(cfg, B * H, T)
+    aqkv.quantize_keys(cfg, layer, kd, one)
+    aqkv.quantize_values(cfg, vd, one)
+    parts = aqkv.Cache.allocate(cfg, B * H, T)
+    for a, e in ((0, 300), (300, 301), (301, 333), (333, T)):
+        aqkv.quantize_keys(cfg, layer, kd[:, :, a:e], parts, token_offset=a)
+        aqkv.quantize_values(cfg, vd[:, :, a:e], parts, token_offset=a)
+    torch.cuda.synchronize()
+    for name in ("key_codes", "key_signs", "key_norm", "key_rnorm", "val_codes", "val_scale", "val_min"):
+        assert torch.equal(getattr(one, name), getattr(parts, name)), name
+
+
+@pytest.mark.parametrize("d,w,m,qdtype", [(128, 2, 128, "fp32"), (128, 0, 512, "bf16"), (256, 3, 256, "fp32")])
+def test_prepare_query_parity(d, w, m, qdtype):
+    torch, dev = torch_dev()
+    say("prepare_query", d, w, m, qdtype)
+    hl = host_layer(d, w, m, layer=2)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    q = _as_dtype(np.random.default_rng(5).standard_normal((3, 5, d)).astype(np.float32), qdtype)
+    qd = to_device_kv(q.reshape(1, 3, 5, d), qdtype).reshape(3, 5, d).contiguous()
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, qd)
+    torch.cuda.synchronize()
+    r_rot, r_sk = oatt.prepare_query(q.reshape(-1, d), hl.rotation, hl.sketch, w)
+    qn = np.linalg.norm(q.reshape(-1, d), axis=1, keepdims=True)
+    assert np.max(np.abs(q_sk.cpu().numpy().reshape(-1, m) - r_sk) / qn) < 2e-5
+    if w > 0:
+        assert np.max(np.abs(q_rot.cpu().numpy().reshape(-1, d) - r_rot) / qn) < 2e-6
+    else:
+        assert q_rot is None
+
+
+def _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity):
+    """Oracle-quantised planes for slots ks[s] / vs[s] copied into a device cache."""
+    torch, dev = torch_dev()
+    n_slots = len(ks)
+    cache = aqkv.Cache.allocate(cfg, n_slots, capacity)
+    for name in ("key_codes", "key_signs", "key_norm", "key_rnorm", "val_codes", "val_scale", "val_min"):
+        t = getattr(cache, name)
+        if t is not None:
+            t.zero_()
+    refs = []
+    for s in range(n_slots):
+        qk, kr, vt, vpacked = oracle_rows(hl, ks[s], vs[s], vb)
+        T = ks[s].shape[0]
+        r0 = s * capacity
+        codes, signs, norm, rnorm = kr
+        if hl.w > 0:
+            cache.key_codes[r0:r0 + T] = torch.from_numpy(codes).to(dev)
+            cache.key_rnorm[r0:r0 + T] = torch.from_numpy(rnorm).to(dev)
+        cache.key_signs[r0:r0 + T] = torch.from_numpy(signs).to(dev)
+        cache.key_norm[r0:r0 + T] = torch.from_numpy(norm).to(dev)
+        cache.val_codes[r0:r0 + T] = torch.from_numpy(vpacked).to(dev)
+        cache.val_scale[r0:r0 + T] = torch.from_numpy(vt[1]).to(dev)
+        cache.val_min[r0:r0 + T] = torch.from_numpy(vt[2]).to(dev)
+        # the oracle consumes exactly what was stored (fp32 norms)
+        refs.append(((qk.idx, qk.bits, norm.astype(np.float64), rnorm.astype(np.float64)), vt))
+    return cache, refs
+
+
+DECODE_CASES = [
+    # d, w, m, G, vb, T
+    (128, 2, 128, 4, 2, 1000), (128, 2, 128, 1, 2, 256), (128, 2, 128, 2, 2, 1), (128, 2, 128, 8, 2, 4097),
+    (256, 3, 256, 2, 2, 700), (128, 0, 192, 4, 2, 513), (128, 0, 512, 4, 2, 300), (64, 1, 64, 4, 4, 255),
+    (128, 2, 128, 4, 4, 999),
+]
+
+
+@pytest.mark.parametrize("d,w,m,G,vb,T", DECODE_CASES)
+def test_decode_parity_on_oracle_planes(d, w, m, G, vb, T):
+    torch, dev = torch_dev()
+    say("decode", d, w, m, G, vb, T)
+    B, Hkv = 2, 2
+    Hq = Hkv * G
+    hl = host_layer(d, w, m, layer=3)
+    cfg = cfg_of(hl, vb)
+    layer = device_layer(hl)
+    rng = np.random.default_rng(d * 7 + T)
+    ks = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(B * Hkv)]
+    vs = [(rng.standard_normal((T, d)) * 2).astype(np.float32) for _ in range(B * Hkv)]
+    cache, refs = _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity=T + 5)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    q_rot, q_sk = oatt.prepare_query(q.reshape(-1, d), hl.rotation, hl.sketch, w)
+    qr_d = torch.from_numpy(q_rot.astype(np.float32)).to(dev) if w > 0 else None
+    qs_d = torch.from_numpy(q_sk.astype(np.float32)).to(dev)
+    scores = torch.full((B, Hq, T), float("nan"), device=dev)
+    out = aqkv.decode_attention(cfg, layer, cache, B, Hq, Hkv, T, qr_d, qs_d, scores=scores)
+    torch.cuda.synchronize()
+    out, scores = out.cpu().numpy(), scores.cpu().numpy()
+    worst_s = worst_o = 0.0
+    for s in range(B * Hkv):
+        b, hkv = divmod(s, Hkv)
+        qh = q[b, hkv * G:(hkv + 1) * G]
+        s_ref, o_ref = oatt.decode_slot(qh, refs[s][0], refs[s][1], hl.rotation, hl.sketch, hl.centroids, w)
+        worst_s = max(worst_s, score_err(scores[b, hkv * G:(hkv + 1) * G], s_ref))
+        worst_o = max(worst_o, float(np.max(np.abs(out[b, hkv * G:(hkv + 1) * G] - o_ref))))
+    say(f"score err {worst_s:.2e}, out err {worst_o:.2e}")
+    assert worst_s <= SCORE_RTOL
+    assert worst_o <= OUT_ATOL
+
+
+def test_decode_empty_context_and_degenerate_softmax():
+    torch, dev = torch_dev()
+    say("decode edge cases")
+    d, w, m, G = 128, 2, 128, 2
+    hl = host_layer(d, w, m)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    rng = np.random.default_rng(0)
+    T = 300
+    ks = [rng.standard_normal((T, d)).astype(np.float32)]
+    vs = [rng.standard_normal((T, d)).astype(np.float32)]
+    cache, refs = _upload_oracle_cache(hl, cfg, ks, vs, 2, capacity=T)
+    q = np.zeros((1, G, d), np.float32)          # all scores equal -> mean of the values
+    qr = torch.zeros((1, G, d), device=dev)
+    qs = torch.zeros((1, G, m), device=dev)
+    out = aqkv.decode_attention(cfg, layer, cache, 1, G, 1, T, qr, qs).cpu().numpy()
+    v_hat = ovals.dequantize_values(*refs[0][1])
+    np.testing.assert_allclose(out[0], np.broadcast_to(v_hat.mean(0), (G, d)), atol=OUT_ATOL)
+    out0 = aqkv.decode_attention(cfg, layer, cache, 1, G, 1, 0, qr, qs).cpu().numpy()
+    assert np.all(out0 == 0.0)
+    out1 = aqkv.decode_attention(cfg, layer, cache, 1, G, 1, 1, qr, qs).cpu().numpy()
+    np.testing.assert_allclose(out1[0], np.broadcast_to(v_hat[0], (G, d)), atol=1e-5)
+
+
+@pytest.mark.parametrize("d,w,m,G,dtype", [(128, 2, 128, 4, "bf16"), (128, 2, 128, 1, "fp32"),
+                                           (256, 3, 256, 2, "bf16"), (128, 0, 256, 4, "bf16")])
+def test_end_to_end(d, w, m, G, dtype):
+    torch, dev = torch_dev()
+    say("end to end", d, w, m, G, dtype)
+    B, Hkv, T = 2, 2, 1500
+    Hq = Hkv * G
+    hl = host_layer(d, w, m, layer=4)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    k = _as_dtype(_kv(B, Hkv, T, d, seed=11), dtype)
+    v = _as_dtype(_kv(B, Hkv, T, d, seed=12), dtype)
+    q = _as_dtype(np.random.default_rng(13).standard_normal((B, Hq, d)).astype(np.float32), dtype)
+    cache = aqkv.Cache.allocate(cfg, B * Hkv, T)
+    aqkv.quantize_keys(cfg, layer, to_device_kv(k, dtype), cache)
+    aqkv.quantize_values(cfg, to_device_kv(v, dtype), cache)
+    qd = to_device_kv(q.reshape(1, B, Hq, d), dtype).reshape(B, Hq, d).contiguous()
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, qd)
+    scores = torch.empty((B, Hq, T), device=dev)
+    out = aqkv.decode_attention(cfg, layer, cache, B, Hq, Hkv, T, q_rot, q_sk, scores=scores)
+    out2 = aqkv.decode_attention(cfg, layer, cache, B, Hq, Hkv, T, q_rot, q_sk)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)       # deterministic
+    out, scores = out.cpu().numpy(), scores.cpu().numpy()
+    for s in range(B * Hkv):
+        b, h = divmod(s, Hkv)
+        gpu = read_planes(cache, s, 0, T)
+        qk, kr, vt, _ = oracle_rows(hl, k[b, h], v[b, h])
+        qh = q[b, h * G:(h + 1) * G]
+        rows = (qk.idx, qk.bits, kr[2].astype(np.float64), kr[3].astype(np.float64))
+        s_ref, o_ref = oatt.decode_slot(qh, rows, vt, hl.rotation, hl.sketch, hl.centroids, w)
+        assert np.max(np.abs(out[b, h * G:(h + 1) * G] - o_ref)) <= OUT_ATOL
+        clean = np.ones(T, bool)
+        if w > 0:
+            clean &= (olay.unpack_code_planes(gpu["codes"], d, w) == qk.idx).all(axis=1)
+        clean &= (olay.unpack_bits(gpu["signs"], m) == qk.bits).all(axis=1)
+        sg = scores[b, h * G:(h + 1) * G]
+        rms = np.sqrt(np.mean(s_ref ** 2, axis=-1, keepdims=True))
+        rel = np.abs(sg - s_ref) / np.maximum(np.abs(s_ref), rms)
+        assert np.max(rel[:, clean]) <= SCORE_RTOL
+        say(f"slot {s}: {int((~clean).sum())} keys differ from the oracle inside the boundary window")
