@@ -1,0 +1,347 @@
+"""Benchmark of the compressed-KV hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input, inputs already
+resident in HBM: quantise every key (norm, rotation, Lloyd-Max index, residual
+QJL signs, norms) and every value (min-max 2-bit groups) of the workload's
+cache, prepare the queries (rotation + sketch), and decode attention for every
+query head on the packed bits (split-K + combine).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints ONE JSON line.  `value` is keys scored per second over the whole step
+(B * Hq * T per step / step time).  The `roofline` object covers the kernel
+that takes the most time in the step, measured with HIP events on the stream
+the kernels are launched on; `decode` and `quantize` carry the per-stage
+figures; `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed-KV decode attn: keys scored/s + HBM GB/s (%peak); quantize tokens/s"
+DEFAULT_WORKLOAD = "llama2_7b_layer_mha32_t32k"
+HBM_PEAK_GBPS = 8000.0
+# fp32 FMA on the vector ALUs without packed math: 256 CU x 64 lanes x 2 flop x 2.4 GHz
+VALU_FP32_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "i8": 5000.0, "fp32": 157.3}
+KERNEL_SOURCES = {
+    "decode": ["decode.hip"],
+    "quantize_keys": ["quant_keys.hip", "query.hip"],
+    "quantize_values": ["quant_values.hip"],
+    "prepare_query": ["query.hip"],
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "kv_cache_compression_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def build_layer(w, layer: int):
+    """Layer parameters built by the library itself (host builders), then copied to HBM."""
+    import torch
+
+    from kv_cache_compression_quantize_amd import aqkv, inputs
+    d, m = w.head_dim, w.sketch_dim(layer)
+    g, s = inputs.layer_gaussians(layer, d, m)
+    dev = torch.device("cuda:0")
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    if w.mse_bits > 0:
+        pi = aqkv.build_rotation(g)
+        c, t = aqkv.build_codebook(d, w.mse_bits)
+        return aqkv.Layer(rotation=f(pi), sketch=f(s), centroids=f(c), boundaries=f(t))
+    return aqkv.Layer(sketch=f(s))
+
+
+def make_inputs(w, layer: int):
+    import torch
+
+    from kv_cache_compression_quantize_amd import inputs
+    dev = torch.device("cuda:0")
+    shape = (w.batch, w.n_kv_heads, w.context, w.head_dim)
+    tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = {}
+    for name in ("k", "v"):
+        t = torch.empty(shape, dtype=tdtype, device=dev)
+        for b in range(w.batch):
+            for h in range(w.n_kv_heads):
+                x = inputs.kv_slot(w, layer, b, h, name)
+                if w.dtype == "bf16":
+                    t[b, h] = torch.from_numpy(inputs.to_bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+                else:
+                    t[b, h] = torch.from_numpy(x).to(dev)
+        out[name] = t
+    out["q"] = torch.from_numpy(inputs.queries(w, layer)).to(dev)
+    return out
+
+
+class Path:
+    """All buffers for one layer of the workload and the four calls of one step."""
+
+    def __init__(self, w, layer: int):
+        import torch
+
+        from kv_cache_compression_quantize_amd import aqkv
+        self.aqkv = aqkv
+        self.w = w
+        self.cfg = aqkv.config(w.head_dim, w.mse_bits, w.sketch_dim(layer), w.value_bits, w.value_group)
+        self.layer = build_layer(w, layer)
+        self.x = make_inputs(w, layer)
+        dev = torch.device("cuda:0")
+        self.cache = aqkv.Cache.allocate(self.cfg, w.n_slots, w.context)
+        self.kws = torch.empty(max(aqkv.quantize_keys_workspace_bytes(self.cfg), 256), dtype=torch.uint8, device=dev)
+        self.dws = torch.empty(aqkv.decode_workspace_bytes(self.cfg, w.batch, w.n_q_heads, w.n_kv_heads, w.context),
+                               dtype=torch.uint8, device=dev)
+        self.q_rot = (torch.empty((w.batch, w.n_q_heads, w.head_dim), device=dev) if w.mse_bits > 0 else None)
+        self.q_sk = torch.empty((w.batch, w.n_q_heads, self.cfg.sketch_dim), device=dev)
+        self.out = torch.empty((w.batch, w.n_q_heads, w.head_dim), device=dev)
+        self.scores = (torch.empty((w.batch, w.n_q_heads, w.context), device=dev) if w.scores else None)
+
+    def quantize_keys(self):
+        self.aqkv.quantize_keys(self.cfg, self.layer, self.x["k"], self.cache, 0, self.kws)
+
+    def quantize_values(self):
+        self.aqkv.quantize_values(self.cfg, self.x["v"], self.cache, 0)
+
+    def prepare_query(self):
+        self.aqkv.prepare_query(self.cfg, self.layer, self.x["q"], self.q_rot, self.q_sk)
+
+    def decode(self):
+        w = self.w
+        self.aqkv.decode_attention(self.cfg, self.layer, self.cache, w.batch, w.n_q_heads, w.n_kv_heads,
+                                   w.context, self.q_rot, self.q_sk, None, self.scores, self.out, self.dws)
+
+    def step(self):
+        self.quantize_keys()
+        self.quantize_values()
+        self.prepare_query()
+        self.decode()
+
+
+def unit_costs(w, layer: int) -> dict:
+    """Algorithmic bytes / flops per unit of each kernel (stated in the design notes)."""
+    d, wb, m, vb = w.head_dim, w.mse_bits, w.sketch_dim(layer), w.value_bits
+    in_bytes = 2 if w.dtype == "bf16" else 4
+    key_row = wb * d // 8 + m // 8 + 4 + (4 if wb > 0 else 0)
+    val_row = d * vb // 8 + 2 * 4 * (d // w.value_group)
+    return {
+        # decode: the compressed planes of one token of one kv head
+        "decode_bytes_per_token_head": key_row + val_row,
+        # key quantise: read the key, write its row; flops of Pi x, Pi^T c and S r
+        "qkeys_bytes_per_key": d * in_bytes + key_row,
+        "qkeys_flops_per_key": (4 * d * d + 2 * m * d) if wb > 0 else 2 * m * d,
+        "qvals_bytes_per_value": d * in_bytes + val_row,
+    }
+
+
+def time_calls(path, reps: int) -> dict:
+    """Average duration of each call, HIP events on the launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    names = ["quantize_keys", "quantize_values", "prepare_query", "decode"]
+    ev = {n: [] for n in names}
+    for _ in range(reps):
+        for n in names:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            getattr(path, n)()
+            b.record(stream)
+            ev[n].append((a, b))
+    torch.cuda.synchronize()
+    return {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in names}
+
+
+def time_decode_cold(path, reps: int) -> float:
+    """Decode duration with the last-level cache flushed before every launch
+    (a 512 MiB write between launches), HIP events around the decode only."""
+    import torch
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+    ts = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        path.decode()
+        b.record(stream)
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ts]))
+
+
+def traffic_from_profiles(kernel: str, units: float):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or k.get("source_hash") != source_hash(kernel):
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, layer: int, budget_s: float = 20.0) -> dict:
+    """The oracle, as it stands, on whole slots of the same workload (one slot
+    = one (batch, kv head) at full context with its query heads): quantise keys
+    and values, then decode.  Reports keys scored per second."""
+    from threadpoolctl import threadpool_info
+
+    from kv_cache_compression_quantize_amd import inputs
+    from oracle import attention as oatt
+    from oracle import codebook as ocb
+    from oracle import keys as okeys
+    from oracle import rotation as orot
+    from oracle import values as ovals
+    d, m = w.head_dim, w.sketch_dim(layer)
+    g, s = inputs.layer_gaussians(layer, d, m)
+    pi = orot.rotation_fp32(g) if w.mse_bits > 0 else None
+    s32 = s.astype(np.float32)
+    c, t = ocb.codebook_fp32(d, w.mse_bits) if w.mse_bits > 0 else (np.zeros(1, np.float32), np.zeros(0, np.float32))
+    q = inputs.queries(w, layer)
+    G = w.n_q_heads // w.n_kv_heads
+    slots, keys_scored, busy = 0, 0, 0.0
+    while busy < budget_s and slots < w.n_slots:
+        b, h = divmod(slots, w.n_kv_heads)
+        k = inputs.kv_slot(w, layer, b, h, "k")
+        v = inputs.kv_slot(w, layer, b, h, "v")
+        t0 = time.perf_counter()
+        qk = okeys.quantize_keys(k, pi, s32, c, t, w.mse_bits)
+        vr = ovals.quantize_values(v, w.value_bits, w.value_group)
+        rows = (qk.idx, qk.bits, qk.norm, qk.rnorm)
+        oatt.decode_slot(q[b, h * G:(h + 1) * G], rows, vr, pi, s32, c, w.mse_bits, group=w.value_group)
+        busy += time.perf_counter() - t0
+        slots += 1
+        keys_scored += G * w.context
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {"value": keys_scored / busy, "unit": "keys/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{slots} of {w.n_slots} (batch, kv-head) slots at full context {w.context} with their "
+                      f"{G} query heads: oracle key+value quantisation and decode, {busy:.1f} s of CPU work; "
+                      f"numpy BLAS threads = {threads}, elementwise numpy single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--layer", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true", help="skip per-call timing (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_compression_quantize_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    layer = args.layer
+    log(f"workload {w.name}: setting up inputs")
+    path = Path(w, layer)
+    torch.cuda.synchronize()
+    log("warmup")
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        path.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / max(args.steps, 1) * 1e3
+    G = w.n_q_heads // w.n_kv_heads
+    keys_per_step = w.batch * w.n_q_heads * w.context
+    value = keys_per_step / (ms_per_step / 1e3)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    rec = {"metric": METRIC, "value": value, "unit": "keys/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
+                      "context": w.context, "head_dim": w.head_dim, "mse_bits": w.mse_bits,
+                      "sketch_dim": w.sketch_dim(layer), "value_bits": w.value_bits,
+                      "value_group": w.value_group, "kv_dtype": w.dtype, "recipe": w.recipe}}
+    if not args.no_detail:
+        log("per-call timing")
+        per = time_calls(path, reps=max(5, args.steps))
+        cold = time_decode_cold(path, reps=5)
+        uc = unit_costs(w, layer)
+        th = w.n_slots * w.context
+        dec_bytes = uc["decode_bytes_per_token_head"] * th
+        qk_bytes = uc["qkeys_bytes_per_key"] * th
+        qk_flops = uc["qkeys_flops_per_key"] * th
+        qv_bytes = uc["qvals_bytes_per_value"] * th
+        rec["decode"] = {
+            "ms": per["decode"], "ms_cold_llc": cold,
+            "keys_scored_per_s": keys_per_step / (per["decode"] / 1e3),
+            "kv_token_heads_per_s": th / (per["decode"] / 1e3),
+            "GBps": dec_bytes / (per["decode"] / 1e3) / 1e9,
+            "GBps_cold_llc": dec_bytes / (cold / 1e3) / 1e9,
+            "pct_peak_hbm": 100 * dec_bytes / (per["decode"] / 1e3) / 1e9 / HBM_PEAK_GBPS,
+            "bytes_per_launch": dec_bytes}
+        rec["quantize"] = {
+            "keys_ms": per["quantize_keys"], "values_ms": per["quantize_values"],
+            "tokens_per_s": w.batch * w.context / ((per["quantize_keys"] + per["quantize_values"]) / 1e3),
+            "token_heads_per_s": th / ((per["quantize_keys"] + per["quantize_values"]) / 1e3),
+            "keys_TFLOPs": qk_flops / (per["quantize_keys"] / 1e3) / 1e12,
+            "keys_GBps": qk_bytes / (per["quantize_keys"] / 1e3) / 1e9,
+            "values_GBps": qv_bytes / (per["quantize_values"] / 1e3) / 1e9}
+        rec["prepare_query_ms"] = per["prepare_query"]
+        dominant = max(["decode", "quantize_keys", "quantize_values"], key=lambda n: per[n])
+        if dominant == "decode":
+            ach = dec_bytes / (per["decode"] / 1e3) / 1e9
+            rec["roofline"] = {"kernel": "decode_attention (decode + combine)", "bound": "hbm", "achieved": ach,
+                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                               "traffic": traffic_from_profiles("decode", th)}
+        elif dominant == "quantize_keys":
+            ach = qk_flops / (per["quantize_keys"] / 1e3) / 1e12
+            rec["roofline"] = {"kernel": "quantize_keys", "bound": "alu", "achieved": ach,
+                               "peak": VALU_FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / VALU_FP32_PEAK_TFLOPS,
+                               "traffic": traffic_from_profiles("quantize_keys", th)}
+        else:
+            ach = qv_bytes / (per["quantize_values"] / 1e3) / 1e9
+            rec["roofline"] = {"kernel": "quantize_values", "bound": "hbm", "achieved": ach,
+                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                               "traffic": traffic_from_profiles("quantize_values", th)}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        rec["cpu_baseline"] = cpu_baseline(w, layer)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()
