@@ -59,17 +59,20 @@ size_t key_workspace_bytes(int d, int w, int m) {
 
 namespace aqkv {
 
-DecodePlan decode_plan(int d, int64_t n_slots, int g, int64_t context) {
-  constexpr int64_t kChunk = 256;      // tokens per block iteration
-  constexpr int64_t kTargetBlocks = 2048;
+DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int64_t context) {
+  constexpr int64_t kGrain = 256;      // split granularity (tokens)
+  constexpr int64_t kCUs = 256;        // MI355X compute units
   DecodePlan p{};
-  const int64_t chunks = (context + kChunk - 1) / kChunk;
-  int64_t split = n_slots > 0 ? (kTargetBlocks + n_slots - 1) / n_slots : 1;
-  if (split > chunks) split = chunks;
+  p.mfma = decode_mfma_supported(d, w, g, m, vb);
+  // two rounds of resident blocks for the matrix-core kernel, ~4 per CU otherwise
+  const int64_t target = p.mfma ? 2 * kCUs * decode_mfma_blocks_per_cu(d, w, g, m, vb) : 4 * kCUs;
+  const int64_t grains = (context + kGrain - 1) / kGrain;
+  int64_t split = n_slots > 0 ? (target + n_slots - 1) / n_slots : 1;
+  if (split > grains) split = grains;
   if (split < 1) split = 1;
-  const int64_t per_split_chunks = chunks > 0 ? (chunks + split - 1) / split : 1;
-  p.split_tokens = per_split_chunks * kChunk;
-  p.n_split = static_cast<int>(chunks > 0 ? (chunks + per_split_chunks - 1) / per_split_chunks : 1);
+  const int64_t per_split = grains > 0 ? (grains + split - 1) / split : 1;
+  p.split_tokens = per_split * kGrain;
+  p.n_split = static_cast<int>(grains > 0 ? (grains + per_split - 1) / per_split : 1);
   const size_t heads = static_cast<size_t>(n_slots) * g;
   p.acc_bytes = round_up(heads * p.n_split * d * sizeof(float), 256);
   p.ml_bytes = round_up(heads * p.n_split * 2 * sizeof(float), 256);
@@ -122,7 +125,9 @@ size_t aqkv_decode_workspace_bytes(const aqkv_config *cfg, int32_t batch, int32_
   if (check_config(cfg) != AQKV_OK) return 0;
   if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads || context_len < 0) return 0;
   const int64_t n_slots = static_cast<int64_t>(batch) * n_kv_heads;
-  return decode_plan(cfg->head_dim, n_slots, n_q_heads / n_kv_heads, context_len).total_bytes;
+  return decode_plan(cfg->head_dim, cfg->mse_bits, cfg->sketch_dim, cfg->value_bits, n_slots,
+                     n_q_heads / n_kv_heads, context_len)
+      .total_bytes;
 }
 
 aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_kv_view *k,
@@ -264,7 +269,8 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   if (context_len > cache->capacity) return AQKV_ERR_CAPACITY;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return AQKV_ERR_SHAPE;
   const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
-  if (!decode_supported(d, w, g, m, cfg->value_bits)) return AQKV_ERR_UNSUPPORTED;
+  if (!decode_supported(d, w, g, m, cfg->value_bits) && !decode_mfma_supported(d, w, g, m, cfg->value_bits))
+    return AQKV_ERR_UNSUPPORTED;
   if (batch == 0) return AQKV_OK;
   if (!out || !q_sketch) return AQKV_ERR_NULL;
   if (w > 0 && (!q_rot || !layer->centroids)) return AQKV_ERR_NULL;
@@ -282,7 +288,7 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
     if ((st = check_plane(cache->val_scale)) != AQKV_OK) return st;
     if ((st = check_plane(cache->val_min)) != AQKV_OK) return st;
   }
-  const DecodePlan plan = decode_plan(d, cache->n_slots, g, context_len);
+  const DecodePlan plan = decode_plan(d, w, m, cfg->value_bits, cache->n_slots, g, context_len);
   if (!workspace || workspace_bytes < plan.total_bytes) return AQKV_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return AQKV_ERR_ALIGN;
 
@@ -313,7 +319,9 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   job.out = out;
   job.part_acc = static_cast<float *>(workspace);
   job.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.acc_bytes);
-  return hip_status(launch_decode(job, static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.mfma) return hip_status(launch_decode_mfma(job, s));
+  return hip_status(launch_decode(job, s));
 }
 
 }  // extern "C"

@@ -213,21 +213,47 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
   }
 }
 
+// Merge the split partials of one query head: M = max_i m_i, weights
+// w_i = 2^(m_i - M) (0 for empty splits), out = sum_i w_i acc_i / sum_i w_i l_i.
+// The weights are computed once per split into LDS (splits <= 1024 in one pass,
+// more in a loop), then each thread sums its channels over the splits.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeJob job) {
+  __shared__ float wts[1024];
+  __shared__ float red[256];
   const int64_t head = blockIdx.x;
-  const int d = job.d, ns = job.n_split;
+  const int d = job.d, ns = job.n_split, tid = threadIdx.x;
   const float *ml = job.part_ml + head * ns * 2;
   float mx = -INFINITY;
-  for (int i = 0; i < ns; ++i)
+  for (int i = tid; i < ns; i += 256)
     if (ml[2 * i + 1] > 0.0f) mx = fmaxf(mx, ml[2 * i]);
-  float l = 0.0f;
-  for (int i = 0; i < ns; ++i)
-    if (ml[2 * i + 1] > 0.0f) l += ml[2 * i + 1] * exp2f(ml[2 * i] - mx);
-  for (int j = threadIdx.x; j < d; j += blockDim.x) {
-    float o = 0.0f;
-    for (int i = 0; i < ns; ++i)
-      if (ml[2 * i + 1] > 0.0f) o = fmaf(job.part_acc[(head * ns + i) * d + j], exp2f(ml[2 * i] - mx), o);
-    job.out[head * d + j] = l > 0.0f ? o / l : 0.0f;
+  red[tid] = mx;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  float o[2] = {0.0f, 0.0f};
+  float lsum = 0.0f;
+  for (int c0 = 0; c0 < ns; c0 += 1024) {
+    const int cn = min(1024, ns - c0);
+    for (int i = tid; i < cn; i += 256) {
+      const float l = ml[2 * (c0 + i) + 1];
+      wts[i] = l > 0.0f ? exp2f(ml[2 * (c0 + i)] - mx) : 0.0f;
+    }
+    __syncthreads();
+    for (int i = 0; i < cn; ++i) lsum = fmaf(ml[2 * (c0 + i) + 1], wts[i], lsum);
+    for (int r = 0; r < 2; ++r) {
+      const int j = tid + 256 * r;
+      if (j < d)
+        for (int i = 0; i < cn; ++i) o[r] = fmaf(job.part_acc[(head * ns + c0 + i) * d + j], wts[i], o[r]);
+    }
+    __syncthreads();
+  }
+  for (int r = 0; r < 2; ++r) {
+    const int j = tid + 256 * r;
+    if (j < d) job.out[head * d + j] = lsum > 0.0f ? o[r] / lsum : 0.0f;
   }
 }
 
@@ -244,8 +270,7 @@ hipError_t launch_dwg(const DecodeJob &job, hipStream_t stream) {
   decode_kernel<D, W, G><<<grid, kThreads, smem, stream>>>(job);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<<<static_cast<unsigned>(job.n_slots * G), 256, 0, stream>>>(job);
-  return hipGetLastError();
+  return launch_combine(job, stream);
 }
 
 template <int D, int W>
@@ -270,6 +295,11 @@ hipError_t launch_d(const DecodeJob &job, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_combine(const DecodeJob &job, hipStream_t stream) {
+  combine_kernel<<<static_cast<unsigned>(job.n_slots * job.g), 256, 0, stream>>>(job);
+  return hipGetLastError();
+}
 
 bool decode_supported(int d, int w, int g, int m, int vb) {
   if (g != 1 && g != 2 && g != 4 && g != 8) return false;

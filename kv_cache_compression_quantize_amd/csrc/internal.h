@@ -68,11 +68,12 @@ struct DecodeJob {
 
 // Decode split-K plan shared by the workspace query and the launch.
 struct DecodePlan {
+  bool mfma;             // matrix-core kernel (else the scalar fallback)
   int n_split;
   int64_t split_tokens;
   size_t acc_bytes, ml_bytes, total_bytes;
 };
-DecodePlan decode_plan(int d, int64_t n_slots, int g, int64_t context);
+DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int64_t context);
 
 // Launchers (return a hipError_t from hipGetLastError after the launch).
 hipError_t launch_make_projection(const float *sketch, const float *rotation, float *proj, int m,
@@ -81,7 +82,12 @@ hipError_t launch_quantize_keys(const KeyJob &job, hipStream_t stream);
 hipError_t launch_quantize_values(const ValueJob &job, hipStream_t stream);
 hipError_t launch_prepare_query(const QueryJob &job, hipStream_t stream);
 hipError_t launch_decode(const DecodeJob &job, hipStream_t stream);
+hipError_t launch_combine(const DecodeJob &job, hipStream_t stream);
 bool decode_supported(int d, int w, int g, int m, int vb);
+// matrix-core decode (decode + combine)
+bool decode_mfma_supported(int d, int w, int g, int m, int vb);
+int decode_mfma_blocks_per_cu(int d, int w, int g, int m, int vb);
+hipError_t launch_decode_mfma(const DecodeJob &job, hipStream_t stream);
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
