@@ -38,16 +38,22 @@
  *   prints, aborts or throws across this interface.
  *
  * Cache layout (one plane per array, rows contiguous; slot s = b * H + h of
- * the K/V view; token t of slot s is row s * capacity + t):
- *   key_codes  w * d / 8 bytes per row: w bit-planes of d/8 bytes each; plane p
- *              holds bit p of every coordinate's index, coordinate j at bit
- *              j % 8 of byte j / 8.  (NULL allowed when w == 0.)
- *   key_signs  m / 8 bytes per row, sketch row i at bit i % 8 of byte i / 8;
- *              bit 1 = non-negative projection.
+ * the K/V view; token t of slot s is row s * capacity + t; capacity is a
+ * multiple of 32):
+ *   bit rows   32-bit little-endian words of 32 consecutive elements; element
+ *              j = 4 i + k of a word (i in 0..7, k in 0..3) is bit 8 k + i.
+ *   key_codes  w * d / 8 bytes per row: w bit rows of d bits; row p holds bit
+ *              p of every coordinate's index.  (NULL allowed when w == 0.)
+ *   key_signs  m / 8 bytes per row: one bit row, bit 1 = non-negative
+ *              projection.
  *   key_norm   fp32 ||x|| per row.
  *   key_rnorm  fp32 ||r|| per row (NULL allowed when w == 0).
- *   val_codes  d * value_bits / 8 bytes per row, LSB-first bitstream: channel
- *              j occupies bits [value_bits*j, value_bits*(j+1)).
+ *   val_codes  d * value_bits / 8 bytes per row, stored in blocks of 32 rows
+ *              (tokens 32 c .. 32 c + 31 of a slot).  In a block, channel
+ *              32 g + 16 h + n (group g, half h, column n) of token 4 i + r
+ *              (r in 0..3, i in 0..7) is at
+ *                value_bits 2: word (16 g + n) * 4 + r, bits 8 h + 16 (i & 1) + 2 (i >> 1);
+ *                value_bits 4: word ((16 g + n) * 4 + r) * 2 + h, bits 16 (i & 1) + 4 (i >> 1).
  *   val_scale  fp32 [d / value_group] per row.
  *   val_min    fp32 [d / value_group] per row.
  * Every plane pointer must be 16-byte aligned.
@@ -104,7 +110,7 @@ typedef struct {
   float *val_scale;
   float *val_min;
   int64_t n_slots;   /* batch * kv heads */
-  int64_t capacity;  /* token rows per slot */
+  int64_t capacity;  /* token rows per slot, a multiple of 32 */
 } aqkv_cache;
 
 /* A strided 4-D K or V tensor [batch][heads][tokens][d] in device memory.

@@ -194,8 +194,10 @@ class Cache:
 
     @staticmethod
     def allocate(cfg: Config, n_slots: int, capacity: int, device="cuda") -> "Cache":
+        """Planes for n_slots x capacity tokens (capacity rounded up to a multiple of 32)."""
         import torch
         rb = cache_layout(cfg)
+        capacity = (capacity + 31) // 32 * 32
         rows = n_slots * capacity
 
         def u8(nb):

@@ -39,6 +39,7 @@ aqkv_status check_view(const aqkv_kv_view *v, int d) {
 aqkv_status check_cache_shape(const aqkv_cache *c) {
   if (!c) return AQKV_ERR_NULL;
   if (c->n_slots < 0 || c->capacity < 0) return AQKV_ERR_SHAPE;
+  if (c->capacity % 32) return AQKV_ERR_SHAPE;   // value codes live in 32-token blocks
   return AQKV_OK;
 }
 

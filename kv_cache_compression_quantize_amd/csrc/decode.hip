@@ -23,6 +23,9 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
+// bit of element j (0..31) in a 32-bit bit-row word: 8 (j % 4) + j / 4
+__device__ __forceinline__ int word_bit(int j) { return 8 * (j & 3) + (j >> 2); }
+
 template <int D, int W, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -69,9 +72,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
     const bool valid = t < t_end;
     const int64_t row = slot * job.capacity + t;
 
-    // stage this thread's token's value row (zeros past the end)
+    // stage this thread's share of the chunk's value-code blocks (whole 32-token
+    // blocks: a block's words hold codes of all its tokens); past the end -> 0
+    const bool block_valid = c0 + (tid & ~31) < t_end;
     for (int i = 0; i < vwords; ++i)
-      vcw[tid * vwords + i] = valid ? reinterpret_cast<const uint32_t *>(job.vcodes + row * (D * vb / 8))[i] : 0u;
+      vcw[tid * vwords + i] = block_valid ? reinterpret_cast<const uint32_t *>(job.vcodes + row * (D * vb / 8))[i] : 0u;
     for (int i = 0; i < kGroups; ++i) {
       vsc[tid * kGroups + i] = valid ? job.vscale[row * kGroups + i] : 0.0f;
       vmn[tid * kGroups + i] = valid ? job.vmin[row * kGroups + i] : 0.0f;
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
           for (int l = 0; l < 32; ++l) {
             int idx = 0;
 #pragma unroll
-            for (int p = 0; p < W; ++p) idx |= static_cast<int>((pl[p] >> l) & 1u) << p;
+            for (int p = 0; p < W; ++p) idx |= static_cast<int>((pl[p] >> word_bit(l)) & 1u) << p;
             float v = cen[0];
 #pragma unroll
             for (int k = 1; k < (1 << W); ++k) v = (idx == k) ? cen[k] : v;
@@ -128,10 +133,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
           for (int l4 = 0; l4 < 8; ++l4) {
             const float4 q = q4[l4];
             const int l = 4 * l4;
-            qjl[g] += ((bits >> (l + 0)) & 1u) ? q.x : -q.x;
-            qjl[g] += ((bits >> (l + 1)) & 1u) ? q.y : -q.y;
-            qjl[g] += ((bits >> (l + 2)) & 1u) ? q.z : -q.z;
-            qjl[g] += ((bits >> (l + 3)) & 1u) ? q.w : -q.w;
+            qjl[g] += ((bits >> word_bit(l + 0)) & 1u) ? q.x : -q.x;
+            qjl[g] += ((bits >> word_bit(l + 1)) & 1u) ? q.y : -q.y;
+            qjl[g] += ((bits >> word_bit(l + 2)) & 1u) ? q.z : -q.z;
+            qjl[g] += ((bits >> word_bit(l + 3)) & 1u) ? q.w : -q.w;
           }
         }
       }
@@ -182,12 +187,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
       const int pi = tid + i * kThreads;
       if (pi < G * D) {
         const int g = pi / D, j = pi % D;
-        const int word = (j * vb) >> 5, shift = (j * vb) & 31, grp = j >> 5;
+        // 32-token block layout: channel j = 32 grp + 16 hh + n, token 4 ii + r of a block
+        const int grp = j >> 5, hh = (j >> 4) & 1, n = j & 15;
         const uint32_t mask = (1u << vb) - 1u;
         float a = acc[i] * stat[4 * g + 2];
         const float *pg = sc + g * kChunk;
         for (int tt = 0; tt < kChunk; ++tt) {
-          const float code = static_cast<float>((vcw[tt * vwords + word] >> shift) & mask);
+          const int r = tt & 3, ii = (tt >> 2) & 7;
+          const int word = (tt >> 5) * (32 * vwords) +
+                           (vb == 2 ? (16 * grp + n) * 4 + r : ((16 * grp + n) * 4 + r) * 2 + hh);
+          const int shift = vb == 2 ? 8 * hh + 16 * (ii & 1) + 2 * (ii >> 1) : 16 * (ii & 1) + 4 * (ii >> 1);
+          const float code = static_cast<float>((vcw[word] >> shift) & mask);
           const float vh = fmaf(code, vsc[tt * kGroups + grp], vmn[tt * kGroups + grp]);
           a = fmaf(pg[tt], vh, a);
         }

@@ -18,8 +18,9 @@
 // (4 bits per shift, multiply, mask); no fp key is formed.
 //
 // Values: out[g] = sum_t p_t (code_t scale_t + min_t).  The f16 operand
-// 1 + code/4 (exact: the code sits in mantissa bits 8..9) is built from the
-// packed code byte; the token weights a_t = p_t scale_t are split into f16
+// 1 + code/4 (exact: the code sits in mantissa bits 8..9) is built with one
+// shift and one mask from the 32-token block word that holds 8 tokens' codes
+// of one channel; the token weights a_t = p_t scale_t are split into f16
 // hi + lo and v_mfma_f32_16x16x32_f16 accumulates sum_t a_t (1 + code_t/4)
 // over 32 tokens; sum_t p_t (min_t - 4 scale_t) is added at the end.
 //
@@ -59,11 +60,13 @@ static_assert(sizeof(QConst) == 256, "constants block");
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// 16 bits -> 16 int8 {0,1} operand bytes (bit i -> byte i)
-__device__ __forceinline__ v4i spread16(uint32_t piece) {
+// Bit-row words hold element j = 4 i + k at bit 8 k + i, so (x >> i) & 0x01010101
+// is elements 4i .. 4i+3 as int8 {0,1} bytes.  Half hf of a word (elements
+// 16 hf .. 16 hf + 15) -> the 16 operand bytes of one K-chunk.
+__device__ __forceinline__ v4i spread_half(uint32_t x, int hf) {
   v4i r;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) r[k] = static_cast<int>((((piece >> (4 * k)) & 0xfu) * 0x00204081u) & 0x01010101u);
+  for (int k = 0; k < 4; ++k) r[k] = static_cast<int>((x >> (4 * hf + k)) & 0x01010101u);
   return r;
 }
 
@@ -266,7 +269,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeJob job, in
     async_copy(reinterpret_cast<const uint8_t *>(job.norm + row0), b + o_norm, kTT * 4, nt * 4, lane);
     if constexpr (W > 0)
       async_copy(reinterpret_cast<const uint8_t *>(job.rnorm + row0), b + o_rnorm, kTT * 4, nt * 4, lane);
-    async_copy(job.vcodes + row0 * VBY, b + o_vcodes, kTT * VBY, nt * VBY, lane);
+    // the value codes of a 32-token block interleave all its tokens: copy it whole
+    async_copy(job.vcodes + row0 * VBY, b + o_vcodes, kTT * VBY, kTT * VBY, lane);
     async_copy(reinterpret_cast<const uint8_t *>(job.vscale + row0 * kGroups), b + o_vscale, kTT * kGroups * 4,
                nt * kGroups * 4, lane);
     async_copy(reinterpret_cast<const uint8_t *>(job.vmin + row0 * kGroups), b + o_vmin, kTT * kGroups * 4,
@@ -294,24 +298,33 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeJob job, in
       for (int r = 0; r < RB; ++r) acc[r] = v4i{0, 0, 0, 0};
       int chunk = 0;
       if constexpr (W > 0) {
-        uint64_t pl[W > 0 ? W : 1];      // this lane's D/4 bits of each index plane
+        // this lane's coordinates (D/4) q .. (D/4) q + D/4 - 1 of each index plane,
+        // as the 32-bit words that hold them (D = 64: half of one word)
+        constexpr int kWordsPerLane = D >= 128 ? D / 128 : 1;
+        uint32_t pl[W > 0 ? W : 1][kWordsPerLane];
 #pragma unroll
-        for (int k = 0; k < W; ++k) {
-          const uint8_t *p = tb + tok * CB + k * (D / 8) + (D / 32) * q;
-          if constexpr (D == 64) pl[k] = *reinterpret_cast<const uint16_t *>(p);
-          else if constexpr (D == 128) pl[k] = *reinterpret_cast<const uint32_t *>(p);
-          else pl[k] = *reinterpret_cast<const uint64_t *>(p);
-        }
+        for (int k = 0; k < W; ++k)
+#pragma unroll
+          for (int u = 0; u < kWordsPerLane; ++u) {
+            const int word = D >= 128 ? (D / 128) * q + u : q / 2;
+            pl[k][u] = *reinterpret_cast<const uint32_t *>(tb + tok * CB + k * (D / 8) + 4 * word);
+          }
 #pragma unroll
         for (int A = 1; A <= kPlanes; ++A) {
           if ((pmask >> A) & 1u) {
-            uint64_t x = 0;
+            uint32_t x[kWordsPerLane];
 #pragma unroll
-            for (int k = 0; k < W; ++k)
-              if ((A >> k) & 1) x ^= pl[k];
+            for (int u = 0; u < kWordsPerLane; ++u) {
+              x[u] = 0;
+#pragma unroll
+              for (int k = 0; k < W; ++k)
+                if ((A >> k) & 1) x[u] ^= pl[k][u];
+            }
 #pragma unroll
             for (int h = 0; h < D / 64; ++h) {
-              const v4i bop = spread16(static_cast<uint32_t>(x >> (16 * h)) & 0xffffu);
+              // chunk h = coordinates (D/4) q + 16 h .. + 15
+              const int hf = D >= 128 ? (h & 1) : (q & 1);
+              const v4i bop = spread_half(x[D >= 128 ? h >> 1 : 0], hf);
 #pragma unroll
               for (int r = 0; r < RB; ++r) {
                 const v4i aop = *reinterpret_cast<const v4i *>(qa + ((chunk * RB + r) * 4 + q) * 256 + n16 * 16);
@@ -323,10 +336,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeJob job, in
         }
       }
       {
-        const uint8_t *sp = tb + o_signs + tok * SB + (m / 32) * q;
+        const uint8_t *sp = tb + o_signs + tok * SB;
         for (int h = 0; h < m / 64; ++h) {
-          const uint32_t piece = *reinterpret_cast<const uint16_t *>(sp + 2 * h);
-          const v4i bop = spread16(piece);
+          const int c = (m / 4) * q + 16 * h;          // first sketch row of this chunk
+          const uint32_t word = *reinterpret_cast<const uint32_t *>(sp + 4 * (c >> 5));
+          const v4i bop = spread_half(word, (c >> 4) & 1);
 #pragma unroll
           for (int r = 0; r < RB; ++r) {
             const v4i aop = *reinterpret_cast<const v4i *>(qa + ((chunk * RB + r) * 4 + q) * 256 + n16 * 16);
@@ -451,28 +465,33 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeJob job, in
 #pragma unroll
       for (int grp = 0; grp < kGroups; ++grp) {
         const v8h aop = *reinterpret_cast<const v8h *>(aval + ((grp * 4 + q) * 16 + n16) * 16);
-        uint32_t wv[4];
+        // block word(s) of column n16: tokens 4 i + q of channels 32 grp + 16 h + n16;
+        // operand dword k = K-slots (8q + 2k, 8q + 2k + 1) = i (2k, 2k + 1)
+        uint32_t wv[2];
+        if constexpr (VB == 2) {
+          wv[0] = reinterpret_cast<const uint32_t *>(vc)[(16 * grp + n16) * 4 + q];
+        } else {
+          const uint2 t2 = reinterpret_cast<const uint2 *>(vc)[(16 * grp + n16) * 4 + q];
+          wv[0] = t2.x;
+          wv[1] = t2.y;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          if (VB == 4 || h == 0) {
-            // column byte of tokens (8k + q, 8k + 4 + q) = K-slots (8q + 2k, 8q + 2k + 1)
-            const int bc = VB == 2 ? 8 * grp + (n16 >> 1) : 16 * grp + 8 * h + (n16 >> 1);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t b0 = vc[(8 * k + q) * VBY + bc];
-              const uint32_t b1 = vc[(8 * k + 4 + q) * VBY + bc];
-              wv[k] = b0 | (b1 << 16);
-            }
-          }
           v4i bw;
           if constexpr (VB == 2) {
-            const int s = 4 * h + 2 * (n16 & 1);
+            // h = 0: code of i = 2k at bits 2k, of 2k+1 at 16 + 2k; h = 1: 8 bits higher
 #pragma unroll
-            for (int k = 0; k < 4; ++k) bw[k] = static_cast<int>(((wv[k] << (8 - s)) & 0x03000300u) | 0x3c003c00u);
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t sh = h == 0 ? (wv[0] << (8 - 2 * k)) : (wv[0] >> (2 * k));
+              bw[k] = static_cast<int>((sh & 0x03000300u) | 0x3c003c00u);
+            }
           } else {
-            const int s = 4 * (n16 & 1);
+            // code of i = 2k at bits 4k, of 2k+1 at 16 + 4k -> mantissa bits 6..9
 #pragma unroll
-            for (int k = 0; k < 4; ++k) bw[k] = static_cast<int>(((wv[k] << (6 - s)) & 0x03c003c0u) | 0x3c003c00u);
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t sh = k < 2 ? (wv[h] << (6 - 4 * k)) : (wv[h] >> (4 * k - 6));
+              bw[k] = static_cast<int>((sh & 0x03c003c0u) | 0x3c003c00u);
+            }
           }
           const v8h bop = __builtin_bit_cast(v8h, bw);
           cval[2 * grp + h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cval[2 * grp + h], 0, 0, 0);
@@ -518,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeJob job, in
         const float cg = mrg_corr[wave * G * kGroups + g * kGroups + grp];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int ch = VB == 2 ? 32 * grp + 4 * (n16 >> 1) + 2 * h + (n16 & 1) : 32 * grp + 16 * h + n16;
+          const int ch = 32 * grp + 16 * h + n16;
           const v4f c = cval[2 * grp + h];
           mrg[(wave * G + g) * D + ch] = kMag * (c[2 * e] + c[2 * e + 1]) + cg;
         }

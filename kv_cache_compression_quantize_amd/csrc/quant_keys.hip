@@ -24,6 +24,11 @@ constexpr int kKC = 16;      // reduction chunk staged in LDS
 constexpr int kRB = 128;     // output rows per pass
 constexpr int kRPT = kRB / 16;
 
+// Bit rows are 32-bit words; element j = 4 i + k of a word sits at bit 8 k + i
+// (byte k holds the elements j % 4 == k), so a decoder gets 4 consecutive
+// elements as 4 operand bytes with one shift and one mask.
+__device__ __forceinline__ int word_bit(int j) { return 8 * (j & 3) + (j >> 2); }
+
 // Stage W[r0 .. r0+128)[k0 .. k0+16) transposed into wt[16][128] (rows >= nrows -> 0).
 __device__ __forceinline__ void stage_chunk(float (*wt)[kRB], const float *__restrict__ W, int ld, int nrows,
                                             int r0, int k0) {
@@ -186,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(KeyJob job) {
 #pragma unroll
       for (int c = 0; c < kRPT; ++c) {
         const int i = r0 + jq + 16 * c;
-        if (i < m && (z[a][c] >= 0.0f || zero_key)) atomicOr(&sbits[key][i >> 5], 1u << (i & 31));
+        if (i < m && (z[a][c] >= 0.0f || zero_key)) atomicOr(&sbits[key][i >> 5], 1u << word_bit(i & 31));
       }
     }
   }
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void quantize_keys_kernel(KeyJob job) {
       const int p = r / kWordsPerPlane, wi = r % kWordsPerPlane;
       uint32_t word = 0;
 #pragma unroll 8
-      for (int l = 0; l < 32; ++l) word |= static_cast<uint32_t>((idxs[key][32 * wi + l] >> p) & 1) << l;
+      for (int l = 0; l < 32; ++l) word |= static_cast<uint32_t>((idxs[key][32 * wi + l] >> p) & 1) << word_bit(l);
       reinterpret_cast<uint32_t *>(job.codes + (row0 + key) * (W * D / 8) + p * (D / 8))[wi] = word;
     }
   }

@@ -3,17 +3,23 @@
 TurboQuant article §二 says the d sign bits of the QJL sketch are packed into
 d/8 bytes, and §五 that quantize() returns four bit-packed things per key
 (MSE indices, QJL sign bytes, residual norm, original norm); the value codes
-are bit-packed too (§七, kv_cache.py).  The exact bit order is not given;
-the reading used on both sides is:
+are bit-packed too (§七, kv_cache.py).  The bit order is not given.  The
+reading used on both sides (chosen so a decoder turns 4 bits into 4 operand
+bytes with one shift and one mask, and gets one value code per token of a
+32-token block from one 32-bit word):
 
-* key codes, one row of w*d/8 bytes per token: w bit-planes one after the
-  other, plane p holding bit p of every coordinate's index; inside a plane,
-  coordinate j is bit (j % 8) of byte j // 8 (LSB first);
-* key signs, one row of m/8 bytes per token, sketch row i at bit (i % 8)
-  of byte i // 8, bit = 1 for a non-negative projection;
-* value codes, one row of d*vb/8 bytes per token, LSB-first bitstream:
-  channel j occupies bits [vb*j, vb*j + vb) of the little-endian row;
-* norms, value scales and value minima are fp32.
+* bit rows (key signs, and each key index plane): 32-bit little-endian words
+  of 32 consecutive elements; element j = 4 i + k of a word (i in 0..7,
+  k in 0..3) is bit 8 k + i, i.e. byte k holds the elements with j % 4 == k;
+* key codes, one row of w*d/8 bytes per token: w such bit rows one after the
+  other, plane p holding bit p of every coordinate's index;
+* key signs, one row of m/8 bytes per token, bit 1 = non-negative projection;
+* value codes, in blocks of 32 tokens (32 * d * vb / 8 bytes per block): for
+  channel group g (32 channels), column n (0..15), half h (0..1) -- channel
+  32 g + 16 h + n -- and token T = 4 i + r of the block (r in 0..3, i in 0..7):
+    vb = 2: 32-bit word (16 g + n) * 4 + r, bit 8 h + 16 (i & 1) + 2 (i >> 1);
+    vb = 4: 32-bit word ((16 g + n) * 4 + r) * 2 + h, bit 16 (i & 1) + 4 (i >> 1);
+* norms, value scales and value minima are fp32, one row per token.
 """
 from __future__ import annotations
 
@@ -21,15 +27,22 @@ import numpy as np
 
 
 def pack_bits(bits: np.ndarray) -> np.ndarray:
-    """[N, k] booleans -> [N, k/8] uint8, element i at bit i%8 of byte i//8."""
+    """[N, k] booleans (k % 32 == 0) -> [N, k/8] uint8 in the word layout above."""
     bits = np.asarray(bits, dtype=bool)
-    assert bits.shape[-1] % 8 == 0
-    return np.packbits(bits, axis=-1, bitorder="little")
+    n, k = bits.shape[:-1], bits.shape[-1]
+    assert k % 32 == 0
+    w = bits.reshape(n + (k // 32, 8, 4))          # [.., word, i, k]
+    w = np.swapaxes(w, -1, -2)                     # [.., word, k, i]
+    by = np.packbits(w, axis=-1, bitorder="little")[..., 0]   # byte k: bit i = element 4 i + k
+    return by.reshape(n + (k // 8,))
 
 
 def unpack_bits(packed: np.ndarray, k: int) -> np.ndarray:
-    return np.unpackbits(np.asarray(packed, dtype=np.uint8), axis=-1, count=k,
-                         bitorder="little").astype(bool)
+    packed = np.asarray(packed, dtype=np.uint8)
+    n = packed.shape[:-1]
+    by = packed.reshape(n + (k // 32, 4, 1))
+    w = np.unpackbits(by, axis=-1, count=8, bitorder="little").astype(bool)   # [.., word, k, i]
+    return np.swapaxes(w, -1, -2).reshape(n + (k,))
 
 
 def pack_code_planes(idx: np.ndarray, w: int) -> np.ndarray:
@@ -50,22 +63,50 @@ def unpack_code_planes(rows: np.ndarray, d: int, w: int) -> np.ndarray:
     return idx
 
 
+def _value_bit_positions(d: int, vb: int):
+    """(word index, bit offset) of every (token-in-block, channel) pair: two [32, d] arrays."""
+    t = np.arange(32)[:, None]
+    ch = np.arange(d)[None, :]
+    g, rem = ch // 32, ch % 32
+    h, n = rem // 16, rem % 16
+    i, r = t // 4, t % 4
+    if vb == 2:
+        word = (16 * g + n) * 4 + r
+        bit = 8 * h + 16 * (i & 1) + 2 * (i >> 1)
+    elif vb == 4:
+        word = ((16 * g + n) * 4 + r) * 2 + h
+        bit = 16 * (i & 1) + 4 * (i >> 1)
+    else:
+        raise ValueError("value bits must be 2 or 4")
+    return np.broadcast_to(word, (32, d)), np.broadcast_to(bit, (32, d))
+
+
 def pack_value_codes(codes: np.ndarray, vb: int) -> np.ndarray:
-    """[N, d] codes in [0, 2**vb) -> [N, d*vb/8] uint8, LSB-first bitstream."""
+    """[T, d] codes in [0, 2**vb) -> [ceil(T/32) * 32, d*vb/8] uint8 rows of 32-token blocks
+    (tokens past T are zero)."""
     codes = np.asarray(codes, dtype=np.int64)
-    n, d = codes.shape[:-1], codes.shape[-1]
-    bits = np.zeros(n + (d * vb,), dtype=bool)
-    for b in range(vb):
-        bits[..., b::vb] = (codes >> b) & 1
-    return pack_bits(bits)
+    T, d = codes.shape
+    nblk = (T + 31) // 32
+    padded = np.zeros((nblk * 32, d), dtype=np.int64)
+    padded[:T] = codes
+    word, bit = _value_bit_positions(d, vb)
+    words = np.zeros((nblk, 32 * d * vb // 32), dtype=np.uint64)
+    blk = padded.reshape(nblk, 32, d)
+    vals = blk.astype(np.uint64) << bit.astype(np.uint64)[None]
+    for b in range(nblk):
+        np.bitwise_or.at(words[b], word.reshape(-1), vals[b].reshape(-1))
+    out = words.astype("<u4").view(np.uint8).reshape(nblk * 32, d * vb // 8)
+    return out
 
 
-def unpack_value_codes(rows: np.ndarray, d: int, vb: int) -> np.ndarray:
-    bits = unpack_bits(rows, d * vb).astype(np.int64)
-    codes = np.zeros(bits.shape[:-1] + (d,), dtype=np.int64)
-    for b in range(vb):
-        codes |= bits[..., b::vb] << b
-    return codes
+def unpack_value_codes(rows: np.ndarray, T: int, d: int, vb: int) -> np.ndarray:
+    """Inverse of pack_value_codes for the first T tokens."""
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.uint8))
+    nblk = (T + 31) // 32
+    words = rows[: nblk * 32].reshape(nblk, -1).view("<u4").astype(np.int64)
+    word, bit = _value_bit_positions(d, vb)
+    codes = (words[:, word] >> bit[None]) & ((1 << vb) - 1)
+    return codes.reshape(nblk * 32, d)[:T]
 
 
 def row_bytes(d: int, w: int, m: int, vb: int = 2, group: int = 32) -> dict:

@@ -90,7 +90,7 @@ def test_quantize_values_bit_exact(d, vb, dtype):
         b, h = divmod(s, H)
         gpu = read_planes(cache, s, 0, T)
         vc, vs, vm = ovals.quantize_values(v[b, h], vb)
-        np.testing.assert_array_equal(gpu["vcodes"], olay.pack_value_codes(vc, vb))
+        np.testing.assert_array_equal(olay.unpack_value_codes(gpu["vcodes"], T, d, vb), vc)
         np.testing.assert_array_equal(gpu["vscale"].view(np.uint32), vs.view(np.uint32))
         np.testing.assert_array_equal(gpu["vmin"].view(np.uint32), vm.view(np.uint32))
 
@@ -106,10 +106,16 @@ def test_chunked_append_matches_one_call():
     cfg = cfg_of(hl)
     layer = device_layer(hl)
     kd, vd = to_device_kv(k, "bf16"), to_device_kv(v, "bf16")
-    one = aqkv.Cache.allocate(cfg, B * H, T)
+    def zeroed(cache):
+        # rows past T (capacity is rounded up to 32) must compare equal too
+        for name in ("key_codes", "key_signs", "key_norm", "key_rnorm", "val_codes", "val_scale", "val_min"):
+            getattr(cache, name).zero_()
+        return cache
+
+    one = zeroed(aqkv.Cache.allocate(cfg, B * H, T))
     aqkv.quantize_keys(cfg, layer, kd, one)
     aqkv.quantize_values(cfg, vd, one)
-    parts = aqkv.Cache.allocate(cfg, B * H, T)
+    parts = zeroed(aqkv.Cache.allocate(cfg, B * H, T))
     for a, e in ((0, 300), (300, 301), (301, 333), (333, T)):
         aqkv.quantize_keys(cfg, layer, kd[:, :, a:e], parts, token_offset=a)
         aqkv.quantize_values(cfg, vd[:, :, a:e], parts, token_offset=a)
@@ -151,14 +157,14 @@ def _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity):
     for s in range(n_slots):
         qk, kr, vt, vpacked = oracle_rows(hl, ks[s], vs[s], vb)
         T = ks[s].shape[0]
-        r0 = s * capacity
+        r0 = s * cache.capacity          # allocate() rounds the capacity up to 32
         codes, signs, norm, rnorm = kr
         if hl.w > 0:
             cache.key_codes[r0:r0 + T] = torch.from_numpy(codes).to(dev)
             cache.key_rnorm[r0:r0 + T] = torch.from_numpy(rnorm).to(dev)
         cache.key_signs[r0:r0 + T] = torch.from_numpy(signs).to(dev)
         cache.key_norm[r0:r0 + T] = torch.from_numpy(norm).to(dev)
-        cache.val_codes[r0:r0 + T] = torch.from_numpy(vpacked).to(dev)
+        cache.val_codes[r0:r0 + vpacked.shape[0]] = torch.from_numpy(vpacked).to(dev)
         cache.val_scale[r0:r0 + T] = torch.from_numpy(vt[1]).to(dev)
         cache.val_min[r0:r0 + T] = torch.from_numpy(vt[2]).to(dev)
         # the oracle consumes exactly what was stored (fp32 norms)

@@ -100,14 +100,23 @@ def test_distortion_matches_codebook_mse(d, w):
 def test_golden_layouts():
     with open(os.path.join(GOLDEN, "layout_example.json")) as f:
         g = json.load(f)
-    e = g["key_codes_d8_w2"]
-    assert layout.pack_code_planes(np.array([e["idx"]]), 2)[0].tobytes().hex() == e["row_hex"]
-    e = g["key_codes_d8_w3"]
-    assert layout.pack_code_planes(np.array([e["idx"]]), 3)[0].tobytes().hex() == e["row_hex"]
-    e = g["signs_m16"]
-    assert layout.pack_bits(np.array([e["bits"]], dtype=bool))[0].tobytes().hex() == e["row_hex"]
-    e = g["value_codes_d8_vb2"]
-    assert layout.pack_value_codes(np.array([e["codes"]]), 2)[0].tobytes().hex() == e["row_hex"]
+    e = g["key_codes_d32_w2"]
+    idx = np.zeros((1, e["d"]), dtype=np.int64)
+    for k, v in e["idx_nonzero"].items():
+        idx[0, int(k)] = v
+    assert layout.pack_code_planes(idx, 2)[0].tobytes().hex() == e["row_hex"]
+    e = g["signs_m64"]
+    bits = np.zeros((1, 64), dtype=bool)
+    bits[0, e["set"]] = True
+    assert layout.pack_bits(bits)[0].tobytes().hex() == e["row_hex"]
+    for key, vb in (("value_codes_d32_vb2", 2), ("value_codes_d32_vb4", 4)):
+        e = g[key]
+        codes = np.zeros((32, 32), dtype=np.int64)
+        for t, ch, v in e["codes_nonzero"]:
+            codes[t, ch] = v
+        out = layout.pack_value_codes(codes, vb).reshape(-1)
+        assert out.size == e["block_bytes"]
+        assert {str(i): int(x) for i, x in enumerate(out) if x} == e["bytes_nonzero"]
 
 
 def test_pack_roundtrip():
@@ -115,9 +124,15 @@ def test_pack_roundtrip():
     for d, w in ((128, 2), (256, 3), (64, 1)):
         idx = rng.integers(0, 1 << w, size=(7, d))
         np.testing.assert_array_equal(layout.unpack_code_planes(layout.pack_code_planes(idx, w), d, w), idx)
+    for k in (64, 192, 512):
+        bits = rng.random((9, k)) < 0.5
+        np.testing.assert_array_equal(layout.unpack_bits(layout.pack_bits(bits), k), bits)
     for vb in (2, 4):
-        codes = rng.integers(0, 1 << vb, size=(5, 128))
-        np.testing.assert_array_equal(layout.unpack_value_codes(layout.pack_value_codes(codes, vb), 128, vb), codes)
+        for T in (32, 77, 130):
+            codes = rng.integers(0, 1 << vb, size=(T, 128))
+            packed = layout.pack_value_codes(codes, vb)
+            assert packed.shape == ((T + 31) // 32 * 32, 128 * vb // 8)
+            np.testing.assert_array_equal(layout.unpack_value_codes(packed, T, 128, vb), codes)
 
 
 def test_bit_budget_and_compression_ratio():
