@@ -52,8 +52,8 @@ aqkv_status check_plane(const void *p) {
 aqkv_status hip_status(hipError_t e) { return e == hipSuccess ? AQKV_OK : AQKV_ERR_HIP; }
 
 size_t key_workspace_bytes(int d, int w, int m) {
-  // the [m][d] fp32 projection S Pi^T used for the residual sketch
-  return w > 0 ? round_up(static_cast<size_t>(m) * d * sizeof(float), 256) : 0;
+  // matrix-core operands of Pi and S Pi^T (w > 0) or S (w == 0), f16 hi + lo
+  return round_up(aqkv::key_operand_bytes(d, w, m), 256);
 }
 
 }  // namespace
@@ -155,18 +155,14 @@ aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, 
     if ((st = check_plane(cache->key_rnorm)) != AQKV_OK) return st;
   }
   const size_t need = key_workspace_bytes(d, w, m);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return AQKV_ERR_WORKSPACE;
-  if (need > 0 && !aligned(workspace, 256)) return AQKV_ERR_ALIGN;
+  if (!workspace || workspace_bytes < need) return AQKV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return AQKV_ERR_ALIGN;
   if (k->tokens == 0 || cache->n_slots == 0) return AQKV_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const float *proj = layer->sketch;
-  if (w > 0) {
-    float *p = static_cast<float *>(workspace);
-    hipError_t e = launch_make_projection(layer->sketch, layer->rotation, p, m, d, s);
-    if (e != hipSuccess) return AQKV_ERR_HIP;
-    proj = p;
-  }
+  uint8_t *ops = static_cast<uint8_t *>(workspace);
+  hipError_t e = launch_key_operands(layer->rotation, layer->sketch, ops, d, w, m, s);
+  if (e != hipSuccess) return AQKV_ERR_HIP;
   KeyJob job{};
   job.k = k->data;
   job.dtype = k->dtype;
@@ -181,15 +177,14 @@ aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, 
   job.d = d;
   job.w = w;
   job.m = m;
-  job.rotation = layer->rotation;
-  job.proj = proj;
+  job.ops = ops;
   job.centroids = layer->centroids;
   job.boundaries = layer->boundaries;
   job.codes = cache->key_codes;
   job.signs = cache->key_signs;
   job.norm = cache->key_norm;
   job.rnorm = cache->key_rnorm;
-  return hip_status(launch_quantize_keys(job, s));
+  return hip_status(launch_quantize_keys_mfma(job, s));
 }
 
 aqkv_status aqkv_quantize_values(const aqkv_config *cfg, const aqkv_kv_view *v, int64_t token_offset,

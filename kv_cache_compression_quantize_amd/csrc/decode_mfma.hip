@@ -440,8 +440,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeJob job, in
           const float pa = P[g * kTT + ta], pb = P[g * kTT + tb4];
           const float sa = vs[ta * kGroups + grp], sb = vs[tb4 * kGroups + grp];
           const float ma = vm[ta * kGroups + grp], mb = vm[tb4 * kGroups + grp];
-          const float aa = pa > 0.0f ? pa * sa : 0.0f;
-          const float ab = pb > 0.0f ? pb * sb : 0.0f;
+          float aa = pa > 0.0f ? pa * sa : 0.0f;
+          float ab = pb > 0.0f ? pb * sb : 0.0f;
+          // pin the fp32 weights so both uses of the f16 high part round the same value
+          asm volatile("" : "+v"(aa), "+v"(ab));
           float cacc = corr[k];
           if (pa > 0.0f) cacc = fmaf(pa, ma - kMag * sa, cacc);
           if (pb > 0.0f) cacc = fmaf(pb, mb - kMag * sb, cacc);

@@ -20,8 +20,7 @@ struct KeyJob {
   int64_t batch_stride, head_stride, token_stride;  // elements
   int64_t n_slots, n_tokens, token_offset, capacity;
   int d, w, m;
-  const float *rotation;  // Pi [d][d]
-  const float *proj;      // [m][d]: S Pi^T (w > 0) or S (w == 0)
+  const uint8_t *ops;     // matrix-core operands of Pi and S Pi^T (or S), see quant_keys_mfma.hip
   const float *centroids, *boundaries;
   uint8_t *codes, *signs;
   float *norm, *rnorm;
@@ -76,9 +75,11 @@ struct DecodePlan {
 DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int64_t context);
 
 // Launchers (return a hipError_t from hipGetLastError after the launch).
-hipError_t launch_make_projection(const float *sketch, const float *rotation, float *proj, int m,
-                                  int d, hipStream_t stream);
-hipError_t launch_quantize_keys(const KeyJob &job, hipStream_t stream);
+// matrix-core key quantisation: operand preparation (workspace) + kernel
+size_t key_operand_bytes(int d, int w, int m);
+hipError_t launch_key_operands(const float *rotation, const float *sketch, uint8_t *ops, int d, int w, int m,
+                               hipStream_t stream);
+hipError_t launch_quantize_keys_mfma(const KeyJob &job, hipStream_t stream);
 hipError_t launch_quantize_values(const ValueJob &job, hipStream_t stream);
 hipError_t launch_prepare_query(const QueryJob &job, hipStream_t stream);
 hipError_t launch_decode(const DecodeJob &job, hipStream_t stream);

@@ -1,0 +1,728 @@
+// Key quantisation on CDNA4 matrix cores (TurboQuant article §二 three-stage
+// pipeline and §五 quantize(); A-QJL article, section "QJL", for the
+// pure-QJL mode w == 0).
+//
+// Per key x: n = ||x||, y = Pi x / n, idx_j = number of boundaries below y_j,
+// e = y - c[idx], gamma = n ||e|| (= ||x - n Pi^T c[idx]|| for orthogonal
+// Pi), and the residual sketch S r = n (S Pi^T) e, one sign bit per row
+// (w == 0: S x).  The two dense products run on v_mfma_f32_16x16x32_f16 with
+// every fp32 operand that is not already an f16 number split into f16 high
+// and low parts,
+//   a b ~= a_hi b_hi + a_hi b_lo + a_lo b_hi,
+// a relative error of about 3 * 2^-22 per product, far inside the 1e-5
+// decision window.  The weights are scaled by 2^8 first so the low parts of
+// typical entries stay normal f16 numbers.  A bf16 key scaled by a power of
+// two is an exact f16 vector, so for bf16 keys the products with the key take
+// two passes (W_hi x', W_lo x'), for fp32 keys three (u = x / n split).
+//
+// Keys are the N side of every product: one MFMA column block is 16 keys, and
+// lane (n, g) = (lane % 16, lane / 16) receives rows 4g .. 4g+3 of each 16-row
+// output tile for key n.  The rows of the weight operands are permuted so that
+// what a lane receives are whole nibbles of the words it writes: in the
+// bit-row word layout (element 4 i' + k at bit 8 k + i'),
+//   tile t of a full group of 8 tiles: C row (g, i) is element
+//       16 (t % 2) + 4 i + (t % 8) / 2 of word 4 (t / 8) + g, i.e. bit 4 (t % 8) + i;
+//   tile t of a trailing group of 4 (tt = its place in the group): element
+//       16 (tt % 2) + 4 i + 2 (g % 2) + tt / 2 of word 4 G + g / 2, i.e. bit
+//       16 (g % 2) + 4 tt + i
+// (G full groups).  A lane builds its code words most significant bit first,
+// one carry-add per bit, with no cross-lane traffic (a trailing group merges
+// two half words).  The residual e a lane holds for tiles 2k and 2k+1 is, as
+// is, its B operand for k-step k of the sketch product, whose weight columns
+// follow the same permutation.  No fp key and no reconstruction is formed.
+//
+// The weights (Pi, and S Pi^T or S) are prepared once per call into the
+// workspace as ready-made MFMA A operands, [slab][k-step][hi, lo][lane][8 f16],
+// one slab per 16-row tile.  When the whole set fits in LDS (d = 128, m = 128:
+// 128 KiB) a block of 8 waves loads it once and every wave then walks its own
+// 32-key tiles without block synchronisation, prefetching the next tile's
+// keys into registers.  Larger sets go through LDS for one key tile per block:
+// the rotation in groups of 8 slabs, the sketch in double-buffered chunks
+// (global_load_lds_dwordx4).
+#include <algorithm>
+
+#include "internal.h"
+
+namespace aqkv {
+namespace {
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr float kUp = 256.0f;   // weights, fp32 split inputs, boundaries and centroids are scaled by 2^8
+constexpr float kDown8 = 1.0f / 256.0f;
+
+__host__ __device__ constexpr int chunk_slabs(int d) { return d >= 256 ? 2 : 4; }
+__host__ __device__ constexpr int keys_per_wave(int d) { return d >= 256 ? 16 : 32; }
+
+// Output row held by C row r (lane group r / 4, register r % 4) of 16-row tile
+// t, when the dimension has `tiles` tiles (a multiple of 4).
+__host__ __device__ inline int permuted_row(int t, int r, int tiles) {
+  const int full = tiles >> 3;
+  const int go = r >> 2, io = r & 3;
+  if (t < 8 * full) {
+    const int tt = t & 7;
+    return 32 * (4 * (t >> 3) + go) + 16 * (tt & 1) + 4 * io + (tt >> 1);
+  }
+  const int tt = t - 8 * full;
+  return 32 * (4 * full + (go >> 1)) + 16 * (tt & 1) + 4 * io + 2 * (go & 1) + (tt >> 1);
+}
+
+// (a, b) -> high parts hi2 = (f16(a), f16(b)) and low parts
+// lo2 = (f16(a - hi_a), f16(b - hi_b)); a - hi is exact in fp32 and rounded
+// once.  The asm takes a and b as register operands, so both parts derive
+// from the same rounded fp32 values (the compiler may not fold a product
+// into a mixed-precision instruction for one part only).
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi2, uint32_t &lo2) {
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(hi2) : "v"(a), "v"(b));
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %3, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(lo2)
+      : "v"(a), "v"(hi2), "v"(b));
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  uint32_t r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// w = 2 w + (this lane's bit of mask): one carry-add
+__device__ __forceinline__ uint32_t push_bit(uint32_t w, uint64_t mask) {
+  uint32_t r;
+  asm("v_addc_co_u32_e64 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(w), "s"(mask) : "vcc");
+  return r;
+}
+
+__device__ __forceinline__ uint64_t lane_mask(bool c) { return __builtin_amdgcn_ballot_w64(c); }
+
+// ---------------------------------------------------------------- operands
+
+// One thread per (slab, k-step, lane, slot): writes the high and low f16
+// parts of one A-operand element (scaled by 2^8).
+__global__ __launch_bounds__(256) void key_operands_kernel(const float *__restrict__ rot,
+                                                           const float *__restrict__ sketch,
+                                                           uint8_t *__restrict__ ops, int d, int w, int m) {
+  const int ks = d / 32, td = d / 16, tm = m / 16;
+  const int slabs = (w > 0 ? td : 0) + tm;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(slabs) * ks * 512) return;
+  const int s = static_cast<int>(idx & 7);
+  const int lane = static_cast<int>((idx >> 3) & 63);
+  const int k = static_cast<int>((idx >> 9) % ks);
+  const int slab = static_cast<int>((idx >> 9) / ks);
+  const int r = lane & 15, g = lane >> 4;
+  float v;
+  if (w > 0 && slab < td) {
+    // rotation: row = permuted coordinate, column = input coordinate 32k + 8g + s
+    const int row = permuted_row(slab, r, td);
+    v = rot[static_cast<int64_t>(row) * d + 32 * k + 8 * g + s];
+  } else {
+    const int tz = slab - (w > 0 ? td : 0);
+    const int row = permuted_row(tz, r, tm);
+    const float *srow = sketch + static_cast<int64_t>(row) * d;
+    if (w > 0) {
+      // (S Pi^T)[row][col], col = the coordinate lane group g holds in slot s of k-step k
+      const int col = permuted_row(2 * k + (s >> 2), 4 * g + (s & 3), td);
+      const float *prow = rot + static_cast<int64_t>(col) * d;
+      float acc = 0.0f;
+      for (int j = 0; j < d; ++j) acc = fmaf(srow[j], prow[j], acc);
+      v = acc;
+    } else {
+      v = srow[32 * k + 8 * g + s];
+    }
+  }
+  v *= kUp;
+  const _Float16 hi = static_cast<_Float16>(v);
+  const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
+  uint8_t *base = ops + ((static_cast<int64_t>(slab) * ks + k) * 2) * 1024 + lane * 16 + 2 * s;
+  *reinterpret_cast<_Float16 *>(base) = hi;
+  *reinterpret_cast<_Float16 *>(base + 1024) = lo;
+}
+
+// ---------------------------------------------------------------- keys
+
+__device__ __forceinline__ v8h lds_op(const uint8_t *p) { return *reinterpret_cast<const v8h *>(p); }
+
+template <int D>
+struct Geo {
+  static constexpr int KS = D / 32;                  // k-steps of a d-long contraction
+  static constexpr int TD = D / 16;                  // 16-row tiles of the coordinates
+  static constexpr int FD = TD / 8;                  // full 8-tile groups of the coordinates
+  static constexpr int WPL = FD + (TD % 8 ? 1 : 0);  // code words per plane a lane builds
+  static constexpr int NT = keys_per_wave(D) / 16;   // 16-key column blocks per wave
+  static constexpr int KT = NT * 16;                 // keys per wave tile
+  static constexpr int SLAB = KS * 2048;             // bytes of one 16-row operand slab
+};
+
+// B operand of one k-step: 8 f16 as 4 packed words
+struct Op {
+  uint32_t w[4];
+};
+__device__ __forceinline__ v8h as_v8h(const Op &o) { return __builtin_bit_cast(v8h, o); }
+
+template <int D>
+using Ops = Op[Geo<D>::NT][Geo<D>::KS];
+
+// Raw key elements of one lane: 8 consecutive elements per k-step
+// (bf16: one 16-byte load, fp32: two).
+template <int D, bool BF16>
+struct RawKeys {
+  uint4 v[Geo<D>::NT][Geo<D>::KS][BF16 ? 1 : 2];
+};
+
+// Where this lane's keys of a wave tile live: key0 (wave-uniform) + nt*16 + n.
+template <int D>
+struct TileLoc {
+  int64_t src[Geo<D>::NT];   // element offset of the key row in the K view
+  int64_t row[Geo<D>::NT];   // cache row
+  bool valid[Geo<D>::NT];
+};
+
+template <int D>
+__device__ __forceinline__ TileLoc<D> locate(const KeyJob &job, int64_t key0, int n) {
+  TileLoc<D> L;
+  const int64_t total = job.n_slots * job.n_tokens;
+  // the wave-uniform part: slot and token of the tile's first key (32-bit
+  // division when the sizes allow it)
+  int64_t slot0, b0;
+  if (total < (int64_t(1) << 31)) {
+    slot0 = static_cast<uint32_t>(key0) / static_cast<uint32_t>(job.n_tokens);
+    b0 = static_cast<uint32_t>(slot0) / static_cast<uint32_t>(job.heads);
+  } else {
+    slot0 = key0 / job.n_tokens;
+    b0 = slot0 / job.heads;
+  }
+  const int64_t t00 = key0 - slot0 * job.n_tokens;
+  const int64_t h0 = slot0 - b0 * job.heads;
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
+    const int off = nt * 16 + n;
+    L.valid[nt] = key0 + off < total;
+    int64_t slot, t, b, h;
+    if (job.n_tokens >= Geo<D>::KT) {
+      // at most one slot boundary inside the tile
+      t = t00 + off;
+      slot = slot0;
+      b = b0;
+      h = h0;
+      if (t >= job.n_tokens) {
+        t -= job.n_tokens;
+        ++slot;
+        if (++h == job.heads) { h = 0; ++b; }
+      }
+    } else {
+      const int64_t key = L.valid[nt] ? key0 + off : 0;
+      slot = key / job.n_tokens;
+      t = key - slot * job.n_tokens;
+      b = slot / job.heads;
+      h = slot - b * job.heads;
+    }
+    L.src[nt] = b * job.batch_stride + h * job.head_stride + t * job.token_stride;
+    L.row[nt] = slot * job.capacity + job.token_offset + t;
+  }
+  return L;
+}
+
+template <int D, bool BF16>
+__device__ __forceinline__ void load_keys(const KeyJob &job, const TileLoc<D> &L, int g, RawKeys<D, BF16> &R) {
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt)
+#pragma unroll
+    for (int k = 0; k < Geo<D>::KS; ++k) {
+      const int64_t off = L.src[nt] + 32 * k + 8 * g;
+      if (BF16) {
+        R.v[nt][k][0] = L.valid[nt] ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(job.k) + off)
+                                    : make_uint4(0, 0, 0, 0);
+      } else {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(job.k) + off);
+        R.v[nt][k][0] = L.valid[nt] ? p[0] : make_uint4(0, 0, 0, 0);
+        R.v[nt][k][1] = L.valid[nt] ? p[1] : make_uint4(0, 0, 0, 0);
+      }
+    }
+}
+
+// Keys as B operands.  n = ||x|| (lanes n, n+16, n+32, n+48 hold one key).
+// bf16: x' = 2^s x with n 2^s in [128, 256), an exact f16 vector (uh; ul
+// stays zero), and yscale = 1 / (n 2^s) turns the rotation product (with
+// 2^8 Pi) into y' = 2^8 y.  fp32: u' = 2^8 x / n split into hi/lo and
+// yscale = 2^-8.
+template <int D, bool BF16>
+__device__ __forceinline__ void prepare_keys(const RawKeys<D, BF16> &R, float (&nrm)[Geo<D>::NT],
+                                             float (&yscale)[Geo<D>::NT], Ops<D> &uh, Ops<D> &ul) {
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
+    float x[Geo<D>::KS][8];
+#pragma unroll
+    for (int k = 0; k < Geo<D>::KS; ++k) {
+      if (BF16) {
+        const uint32_t wv[4] = {R.v[nt][k][0].x, R.v[nt][k][0].y, R.v[nt][k][0].z, R.v[nt][k][0].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[k][2 * j] = __uint_as_float(wv[j] << 16);
+          x[k][2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
+        }
+      } else {
+        const uint32_t wv[8] = {R.v[nt][k][0].x, R.v[nt][k][0].y, R.v[nt][k][0].z, R.v[nt][k][0].w,
+                                R.v[nt][k][1].x, R.v[nt][k][1].y, R.v[nt][k][1].z, R.v[nt][k][1].w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[k][j] = __uint_as_float(wv[j]);
+      }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int k = 0; k < Geo<D>::KS; ++k)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) ss = fmaf(x[k][s], x[k][s], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float n = sqrtf(ss);
+    nrm[nt] = n;
+    if (BF16) {
+      int e = 0;
+      (void)frexpf(n, &e);                                       // n = f 2^e, f in [0.5, 1)
+      e = max(-100, min(e, 120));
+      const float sc = n > 0.0f ? ldexpf(1.0f, 8 - e) : 0.0f;   // n sc in [128, 256)
+      yscale[nt] = n > 0.0f ? 1.0f / (n * sc) : 0.0f;
+#pragma unroll
+      for (int k = 0; k < Geo<D>::KS; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uh[nt][k].w[j] = pack_f16(x[k][2 * j] * sc, x[k][2 * j + 1] * sc);
+          ul[nt][k].w[j] = 0u;
+        }
+    } else {
+      const float inv = n > 0.0f ? kUp / n : 0.0f;
+      yscale[nt] = kDown8;
+#pragma unroll
+      for (int k = 0; k < Geo<D>::KS; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          split_pair(x[k][2 * j] * inv, x[k][2 * j + 1] * inv, uh[nt][k].w[j], ul[nt][k].w[j]);
+    }
+  }
+}
+
+// Index stage state across the coordinate tiles of one key tile
+template <int D, int W>
+struct IndexState {
+  static constexpr int NB = (1 << W) - 1;
+  float bnd[NB], cen[NB + 1];                // scaled by 2^8
+  uint32_t wv[W][Geo<D>::NT];                // words being built, most significant bit first
+  float esq[Geo<D>::NT];                     // ||2^8 e||^2 (this lane's part)
+};
+
+template <int D, int W>
+__device__ __forceinline__ void index_begin(const KeyJob &job, IndexState<D, W> &S) {
+#pragma unroll
+  for (int i = 0; i < IndexState<D, W>::NB; ++i) S.bnd[i] = job.boundaries[i] * kUp;
+#pragma unroll
+  for (int i = 0; i <= IndexState<D, W>::NB; ++i) S.cen[i] = job.centroids[i] * kUp;
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt) S.esq[nt] = 0.0f;
+}
+
+// Rotated tile t of the key tile: acc = (2^8 Pi rows of tile t) x (key
+// operand); y' = acc * yscale = 2^8 y.  Indices go into the words, e' = y' - c'
+// (2^8 e: exact scaling) into the sketch's B operand (slots 4 (t % 2) + i of
+// k-step t / 2), e'^2 into esq.  The index is the thermometer count of the
+// comparisons; bit p of it is the xor of the comparisons q with
+// (q + 1) % 2^p == 0.
+template <int D, int W, bool BF16>
+__device__ __forceinline__ void index_tile(int t, const uint8_t *slab, const Ops<D> &uh, const Ops<D> &ul,
+                                           const float (&yscale)[Geo<D>::NT], IndexState<D, W> &S, Ops<D> &bh,
+                                           Ops<D> &bl) {
+  constexpr int NT = Geo<D>::NT;
+  constexpr int NB = IndexState<D, W>::NB;
+  v4f acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < Geo<D>::KS; ++k) {
+    const v8h ah = lds_op(slab + (2 * k) * 1024);
+    const v8h al = lds_op(slab + (2 * k + 1) * 1024);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(uh[nt][k]), acc[nt], 0, 0, 0);
+      if (!BF16) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(ul[nt][k]), acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_v8h(uh[nt][k]), acc[nt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float e[4];
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      const float y = acc[nt][i] * yscale[nt];
+      uint64_t c[NB];
+      float cv = S.cen[0];
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const bool gt = y > S.bnd[q];
+        c[q] = lane_mask(gt);
+        cv = gt ? S.cen[q + 1] : cv;
+      }
+#pragma unroll
+      for (int p = 0; p < W; ++p) {
+        uint64_t bit = 0;
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+          if (((q + 1) & ((1 << p) - 1)) == 0) bit ^= c[q];
+        S.wv[p][nt] = push_bit(S.wv[p][nt], bit);
+      }
+      e[i] = y - cv;
+      S.esq[nt] = fmaf(e[i], e[i], S.esq[nt]);
+    }
+    split_pair(e[0], e[1], bh[nt][t >> 1].w[2 * (t & 1)], bl[nt][t >> 1].w[2 * (t & 1)]);
+    split_pair(e[2], e[3], bh[nt][t >> 1].w[2 * (t & 1) + 1], bl[nt][t >> 1].w[2 * (t & 1) + 1]);
+  }
+}
+
+// Word group wl of the coordinates: its tiles (8, or 4 for a trailing group)
+// from the last down, so the bits arrive most significant first.  `group`
+// points at this lane's bytes of the group's first slab.
+template <int D, int W, bool BF16>
+__device__ __forceinline__ void index_group(int wl, const uint8_t *group, int g, const Ops<D> &uh, const Ops<D> &ul,
+                                            const float (&yscale)[Geo<D>::NT], IndexState<D, W> &S,
+                                            uint32_t (&cw)[W][Geo<D>::NT][Geo<D>::WPL], Ops<D> &bh, Ops<D> &bl) {
+  constexpr int NT = Geo<D>::NT;
+  const int cnt = wl < Geo<D>::FD ? 8 : 4;
+#pragma unroll
+  for (int p = 0; p < W; ++p)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) S.wv[p][nt] = 0u;
+#pragma unroll
+  for (int j = cnt - 1; j >= 0; --j) index_tile<D, W, BF16>(8 * wl + j, group + j * Geo<D>::SLAB, uh, ul, yscale, S, bh, bl);
+#pragma unroll
+  for (int p = 0; p < W; ++p)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      uint32_t v = S.wv[p][nt];
+      if (cnt == 4) {
+        // trailing group: lane groups g and g ^ 1 each hold half of one word
+        v <<= 16 * (g & 1);
+        v |= __shfl_xor(v, 16);
+      }
+      cw[p][nt][wl] = v;
+    }
+}
+
+template <int D, int W>
+__device__ __forceinline__ void index_end(const IndexState<D, W> &S, const float (&nrm)[Geo<D>::NT],
+                                          float (&gam)[Geo<D>::NT]) {
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
+    float esq = S.esq[nt];
+    esq += __shfl_xor(esq, 16);
+    esq += __shfl_xor(esq, 32);
+    gam[nt] = nrm[nt] * (sqrtf(esq) * kDown8);
+  }
+}
+
+// One 16-row sketch slab tz: z = slab x (e' or the key operand), sign bits
+// into sw at 4 (tz % 8) + i (trailing group: 4 (tz % 4) + i, then the half
+// words merge); a word is stored as soon as its group is complete.
+template <int D, bool THREE>
+__device__ __forceinline__ void sketch_slab(const KeyJob &job, const uint8_t *slab, int tz, int FM, int g,
+                                            const Ops<D> &bh, const Ops<D> &bl, const float (&nrm)[Geo<D>::NT],
+                                            const TileLoc<D> &L, uint32_t (&sw)[Geo<D>::NT]) {
+  constexpr int NT = Geo<D>::NT;
+  v4f z[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) z[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < Geo<D>::KS; ++k) {
+    const v8h ah = lds_op(slab + (2 * k) * 1024);
+    const v8h al = lds_op(slab + (2 * k + 1) * 1024);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(bh[nt][k]), z[nt], 0, 0, 0);
+      if (THREE) z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(bl[nt][k]), z[nt], 0, 0, 0);
+      z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_v8h(bh[nt][k]), z[nt], 0, 0, 0);
+    }
+  }
+  const bool full = tz < 8 * FM;
+  const int sub = full ? (tz & 7) : (tz & 3);
+  const int64_t srow_bytes = job.m / 8;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const bool zero_key = !(nrm[nt] > 0.0f);
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bits |= static_cast<uint32_t>(z[nt][i] >= 0.0f || zero_key) << i;
+    sw[nt] |= bits << (4 * sub);
+  }
+  if (full && sub == 7) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (L.valid[nt]) reinterpret_cast<uint32_t *>(job.signs + L.row[nt] * srow_bytes)[4 * (tz >> 3) + g] = sw[nt];
+      sw[nt] = 0u;
+    }
+  } else if (!full && sub == 3) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      uint32_t v = sw[nt] << (16 * (g & 1));
+      v |= __shfl_xor(v, 16);
+      if (L.valid[nt] && (g & 1) == 0)
+        reinterpret_cast<uint32_t *>(job.signs + L.row[nt] * srow_bytes)[4 * FM + (g >> 1)] = v;
+      sw[nt] = 0u;
+    }
+  }
+}
+
+template <int D, int W>
+__device__ __forceinline__ void store_codes_norms(const KeyJob &job, const TileLoc<D> &L, int g,
+                                                  const uint32_t (&cw)[W > 0 ? W : 1][Geo<D>::NT][Geo<D>::WPL],
+                                                  const float (&nrm)[Geo<D>::NT], const float (&gam)[Geo<D>::NT]) {
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
+    if (!L.valid[nt]) continue;
+    if constexpr (W > 0) {
+      uint8_t *crow = job.codes + L.row[nt] * (W * D / 8);
+#pragma unroll
+      for (int p = 0; p < W; ++p) {
+        uint32_t *plane = reinterpret_cast<uint32_t *>(crow + p * (D / 8));
+#pragma unroll
+        for (int wl = 0; wl < Geo<D>::FD; ++wl) plane[4 * wl + g] = cw[p][nt][wl];
+        if constexpr (Geo<D>::TD % 8 != 0)
+          if ((g & 1) == 0) plane[4 * Geo<D>::FD + (g >> 1)] = cw[p][nt][Geo<D>::FD];
+      }
+    }
+    if (g == 0) {
+      job.norm[L.row[nt]] = nrm[nt];
+      if constexpr (W > 0) job.rnorm[L.row[nt]] = gam[nt];
+    }
+  }
+}
+
+// Wave-wide copy of `bytes` (a multiple of 1 KiB) of operands into LDS,
+// 1 KiB per instruction, waves taking turns.
+__device__ __forceinline__ void copy_to_lds(const uint8_t *src, uint8_t *dst, int bytes, int wave, int lane) {
+  for (int off = wave * 1024; off < bytes; off += kWaves * 1024)
+    __builtin_amdgcn_global_load_lds(static_cast<const void *>(src + off + 16 * lane), (lds_u8 *)(dst + off), 16, 0,
+                                     0);
+}
+
+template <int D>
+__device__ __forceinline__ void key_operand_as_sketch_input(const Ops<D> &uh, const Ops<D> &ul, Ops<D> &bh,
+                                                            Ops<D> &bl, float (&gam)[Geo<D>::NT]) {
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
+    gam[nt] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < Geo<D>::KS; ++k) {
+      bh[nt][k] = uh[nt][k];
+      bl[nt][k] = ul[nt][k];
+    }
+  }
+}
+
+// ---- resident operands: the whole operand set sits in LDS; every wave then
+// walks its own key tiles (no block synchronisation), the next tile's keys
+// loading while the current one is computed.
+template <int D, int W, bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quantize_keys_resident_kernel(
+    KeyJob job, int64_t n_tiles) {
+  using Gm = Geo<D>;
+  constexpr int NT = Gm::NT;
+  constexpr bool THREE = W > 0 || !BF16;   // the sketch's B operand has a low part
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int TM = job.m / 16, FM = TM / 8;
+  const int pi_slabs = W > 0 ? Gm::TD : 0;
+  copy_to_lds(job.ops, smem, (pi_slabs + TM) * Gm::SLAB, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const uint8_t *pi_lds = smem + 16 * lane;
+  const uint8_t *sk_lds = smem + pi_slabs * Gm::SLAB + 16 * lane;
+
+  int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+  if (tile >= n_tiles) return;
+  TileLoc<D> L = locate<D>(job, tile * Gm::KT, n);
+  RawKeys<D, BF16> R;
+  load_keys<D, BF16>(job, L, g, R);
+  for (; tile < n_tiles; tile += stride) {
+    float nrm[NT], yscale[NT];
+    Op uh[NT][Gm::KS], ul[NT][Gm::KS];
+    prepare_keys<D, BF16>(R, nrm, yscale, uh, ul);
+    // prefetch the next tile
+    const TileLoc<D> Lc = L;
+    if (tile + stride < n_tiles) {
+      L = locate<D>(job, (tile + stride) * Gm::KT, n);
+      load_keys<D, BF16>(job, L, g, R);
+    }
+    uint32_t cw[W > 0 ? W : 1][NT][Gm::WPL];
+    float gam[NT];
+    Op bh[NT][Gm::KS], bl[NT][Gm::KS];
+    if constexpr (W > 0) {
+      IndexState<D, W> S;
+      index_begin<D, W>(job, S);
+#pragma unroll
+      for (int wl = 0; wl < Gm::WPL; ++wl)
+        index_group<D, W, BF16>(wl, pi_lds + 8 * wl * Gm::SLAB, g, uh, ul, yscale, S, cw, bh, bl);
+      index_end<D, W>(S, nrm, gam);
+    } else {
+      key_operand_as_sketch_input<D>(uh, ul, bh, bl, gam);
+    }
+    uint32_t sw[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sw[nt] = 0u;
+    for (int tz = 0; tz < TM; ++tz) sketch_slab<D, THREE>(job, sk_lds + tz * Gm::SLAB, tz, FM, g, bh, bl, nrm, Lc, sw);
+    store_codes_norms<D, W>(job, Lc, g, cw, nrm, gam);
+  }
+}
+
+// ---- streamed operands (sets larger than LDS): a block quantises one tile
+// of 8 x 32 (d = 256: 8 x 16) keys.  The rotation slabs come through LDS one
+// word group (8 slabs, at most 128 KiB) at a time, the sketch slabs in
+// double-buffered chunks of 2 or 4 slabs.
+template <int D, int W, bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quantize_keys_stream_kernel(
+    KeyJob job) {
+  using Gm = Geo<D>;
+  constexpr int NT = Gm::NT;
+  constexpr bool THREE = W > 0 || !BF16;
+  constexpr int CH = chunk_slabs(D);
+  constexpr int CHUNK = CH * Gm::SLAB;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int TM = job.m / 16, FM = TM / 8;
+  const int64_t key0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * Gm::KT;
+  const TileLoc<D> L = locate<D>(job, key0, n);
+  const int pi_slabs = W > 0 ? Gm::TD : 0;
+  if (W > 0) copy_to_lds(job.ops, smem, std::min(8, Gm::TD) * Gm::SLAB, wave, lane);
+  float nrm[NT], yscale[NT];
+  Op uh[NT][Gm::KS], ul[NT][Gm::KS];
+  {
+    RawKeys<D, BF16> R;
+    load_keys<D, BF16>(job, L, g, R);
+    prepare_keys<D, BF16>(R, nrm, yscale, uh, ul);
+  }
+  uint32_t cw[W > 0 ? W : 1][NT][Gm::WPL];
+  float gam[NT];
+  Op bh[NT][Gm::KS], bl[NT][Gm::KS];
+  if constexpr (W > 0) {
+    IndexState<D, W> S;
+    index_begin<D, W>(job, S);
+#pragma unroll
+    for (int wl = 0; wl < Gm::WPL; ++wl) {
+      if (wl > 0) {
+        __syncthreads();   // every wave is done with the previous group
+        copy_to_lds(job.ops + static_cast<int64_t>(8 * wl) * Gm::SLAB, smem,
+                    std::min(8, Gm::TD - 8 * wl) * Gm::SLAB, wave, lane);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      index_group<D, W, BF16>(wl, smem + 16 * lane, g, uh, ul, yscale, S, cw, bh, bl);
+    }
+    index_end<D, W>(S, nrm, gam);
+    __syncthreads();   // every wave is done with the rotation slabs
+  } else {
+    key_operand_as_sketch_input<D>(uh, ul, bh, bl, gam);
+  }
+  const int n_chunks = TM / CH;
+  auto stage = [&](int c) {
+    copy_to_lds(job.ops + static_cast<int64_t>(pi_slabs + c * CH) * Gm::SLAB, smem + (c & 1) * CHUNK, CHUNK, wave,
+                lane);
+  };
+  stage(0);
+  uint32_t sw[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) sw[nt] = 0u;
+  for (int c = 0; c < n_chunks; ++c) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c + 1 < n_chunks) stage(c + 1);
+    const uint8_t *buf = smem + (c & 1) * CHUNK + 16 * lane;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      sketch_slab<D, THREE>(job, buf + j * Gm::SLAB, c * CH + j, FM, g, bh, bl, nrm, L, sw);
+  }
+  store_codes_norms<D, W>(job, L, g, cw, nrm, gam);
+}
+
+constexpr size_t kLdsMax = 160 * 1024;
+
+template <int D, int W>
+size_t stream_smem() {
+  using Gm = Geo<D>;
+  const size_t sketch = static_cast<size_t>(2) * chunk_slabs(D) * Gm::SLAB;
+  const size_t rot = W > 0 ? static_cast<size_t>(std::min(8, Gm::TD)) * Gm::SLAB : 0;
+  return std::max(sketch, rot);
+}
+
+template <int D, int W, bool BF16>
+hipError_t launch_dwt(const KeyJob &job, hipStream_t stream) {
+  using Gm = Geo<D>;
+  const int64_t total = job.n_slots * job.n_tokens;
+  const int64_t n_tiles = (total + Gm::KT - 1) / Gm::KT;
+  const size_t ops = key_operand_bytes(D, W, job.m);
+  bool resident = false;
+  if constexpr (D <= 128) resident = ops <= kLdsMax;
+  if (resident) {
+    auto kern = quantize_keys_resident_kernel<D <= 128 ? D : 128, W, BF16>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ops));
+    if (e != hipSuccess) return e;
+    constexpr int64_t kCUs = 256;   // one resident block per compute unit
+    const int64_t blocks = std::min<int64_t>(kCUs, (n_tiles + kWaves - 1) / kWaves);
+    kern<<<static_cast<unsigned>(blocks), kThreads, ops, stream>>>(job, n_tiles);
+  } else {
+    auto kern = quantize_keys_stream_kernel<D, W, BF16>;
+    const size_t smem = stream_smem<D, W>();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    if (e != hipSuccess) return e;
+    const int64_t blocks = (n_tiles + kWaves - 1) / kWaves;
+    kern<<<static_cast<unsigned>(blocks), kThreads, smem, stream>>>(job);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int W>
+hipError_t launch_dw(const KeyJob &job, hipStream_t stream) {
+  return job.dtype == AQKV_BF16 ? launch_dwt<D, W, true>(job, stream) : launch_dwt<D, W, false>(job, stream);
+}
+
+template <int D>
+hipError_t launch_d(const KeyJob &job, hipStream_t stream) {
+  switch (job.w) {
+    case 0: return launch_dw<D, 0>(job, stream);
+    case 1: return launch_dw<D, 1>(job, stream);
+    case 2: return launch_dw<D, 2>(job, stream);
+    default: return launch_dw<D, 3>(job, stream);
+  }
+}
+
+}  // namespace
+
+size_t key_operand_bytes(int d, int w, int m) {
+  const int slabs = (w > 0 ? d / 16 : 0) + m / 16;
+  return static_cast<size_t>(slabs) * (d / 32) * 2048;
+}
+
+hipError_t launch_key_operands(const float *rotation, const float *sketch, uint8_t *ops, int d, int w, int m,
+                               hipStream_t stream) {
+  const int64_t total = static_cast<int64_t>(key_operand_bytes(d, w, m) / 4);   // one thread per f16 pair
+  key_operands_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(rotation, sketch, ops, d, w,
+                                                                                      m);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_keys_mfma(const KeyJob &job, hipStream_t stream) {
+  switch (job.d) {
+    case 64: return launch_d<64>(job, stream);
+    case 128: return launch_d<128>(job, stream);
+    default: return launch_d<256>(job, stream);
+  }
+}
+
+}  // namespace aqkv

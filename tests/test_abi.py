@@ -55,8 +55,11 @@ def test_cache_layout_and_bad_configs():
 
 def test_workspace_sizes():
     cfg = aqkv.config(128, 2, 128)
-    assert aqkv.quantize_keys_workspace_bytes(cfg) >= 128 * 128 * 4
-    assert aqkv.quantize_keys_workspace_bytes(aqkv.config(128, 0, 256)) == 0
+    # ready-made matrix-core operands: one 16-row slab per tile of Pi (w > 0) and
+    # of the sketch, (d / 32) k-steps x (hi, lo) x 1 KiB each
+    for d, w, m in [(128, 2, 128), (128, 0, 256), (256, 3, 256), (64, 1, 64), (128, 0, 192)]:
+        slabs = (d // 16 if w > 0 else 0) + m // 16
+        assert aqkv.quantize_keys_workspace_bytes(aqkv.config(d, w, m)) == slabs * (d // 32) * 2048
     ws = aqkv.decode_workspace_bytes(cfg, 8, 32, 8, 131072)
     assert ws > 0 and ws % 256 == 0
     assert aqkv.decode_workspace_bytes(cfg, 1, 32, 5, 100) == 0   # Hq % Hkv != 0

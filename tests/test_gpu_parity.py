@@ -72,6 +72,29 @@ def test_quantize_keys_parity(d, w, m, dtype):
     say(f"index window: {tot_win} coords, {tot_mis_win} differ inside it")
 
 
+@pytest.mark.parametrize("d,w,m,nt", [(128, 2, 128, 1), (128, 2, 128, 7), (256, 3, 256, 5), (128, 0, 512, 3)])
+def test_quantize_keys_small_append_many_slots(d, w, m, nt):
+    """Decode-time appends: a few tokens for each of many slots, so one key
+    tile spans several slots (and heads of several batches)."""
+    torch, dev = torch_dev()
+    say("small append", d, w, m, nt)
+    B, H, off = 3, 5, 40
+    k = _as_dtype(_kv(B, H, nt, d, seed=100 + nt), "bf16")
+    hl = host_layer(d, w, m, layer=2)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    cache = aqkv.Cache.allocate(cfg, B * H, 64)
+    aqkv.quantize_keys(cfg, layer, to_device_kv(k, "bf16"), cache, token_offset=off)
+    torch.cuda.synchronize()
+    for s in range(B * H):
+        b, h = divmod(s, H)
+        gpu = read_planes(cache, s, off, off + nt)
+        qk, _, _, _ = oracle_rows(hl, k[b, h], np.zeros((nt, d), np.float32))
+        par = compare_keys(hl, k[b, h], qk, gpu)
+        assert par.idx_mismatch_outside == 0 and par.sign_mismatch_outside == 0, par
+        np.testing.assert_allclose(gpu["norm"], qk.norm, rtol=2e-6, atol=0)
+
+
 @pytest.mark.parametrize("d,vb,dtype", [(128, 2, "bf16"), (128, 2, "fp32"), (256, 2, "bf16"), (64, 4, "fp32"),
                                         (128, 4, "bf16")])
 def test_quantize_values_bit_exact(d, vb, dtype):
