@@ -26,7 +26,7 @@
 //       16 (tt % 2) + 4 i + 2 (g % 2) + tt / 2 of word 4 G + g / 2, i.e. bit
 //       16 (g % 2) + 4 tt + i
 // (G full groups).  A lane builds its code words most significant bit first,
-// one carry-add per bit, with no cross-lane traffic (a trailing group merges
+// w = 2 w + bit, with no cross-lane traffic (a trailing group merges
 // two half words).  The residual e a lane holds for tiles 2k and 2k+1 is, as
 // is, its B operand for k-step k of the sketch product, whose weight columns
 // follow the same permutation.  No fp key and no reconstruction is formed.
@@ -48,6 +48,8 @@ namespace {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kThreads = 512;
@@ -73,31 +75,27 @@ __host__ __device__ inline int permuted_row(int t, int r, int tiles) {
 
 // (a, b) -> high parts hi2 = (f16(a), f16(b)) and low parts
 // lo2 = (f16(a - hi_a), f16(b - hi_b)); a - hi is exact in fp32 and rounded
-// once.  The asm takes a and b as register operands, so both parts derive
-// from the same rounded fp32 values (the compiler may not fold a product
-// into a mixed-precision instruction for one part only).
+// once.  a and b are pinned in registers first (an empty asm, no
+// instruction), so both parts derive from the same rounded fp32 values: the
+// compiler may otherwise fold the product that made a into a mixed-precision
+// conversion for one part only.  No instruction is written in asm here: the
+// compiler must see every VALU write to keep its wait states against
+// in-flight matrix instructions.
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi2, uint32_t &lo2) {
-  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(hi2) : "v"(a), "v"(b));
-  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixhi_f16 %0, %3, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
-      : "=&v"(lo2)
-      : "v"(a), "v"(hi2), "v"(b));
+  asm volatile("" : "+v"(a), "+v"(b));
+  const v2h h = __builtin_convertvector((v2f){a, b}, v2h);
+  const v2f r = {a - static_cast<float>(h[0]), b - static_cast<float>(h[1])};
+  hi2 = __builtin_bit_cast(uint32_t, h);
+  lo2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, v2h));
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
-  uint32_t r;
-  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
+  asm volatile("" : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2h));
 }
 
-// w = 2 w + (this lane's bit of mask): one carry-add
-__device__ __forceinline__ uint32_t push_bit(uint32_t w, uint64_t mask) {
-  uint32_t r;
-  asm("v_addc_co_u32_e64 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(w), "s"(mask) : "vcc");
-  return r;
-}
-
-__device__ __forceinline__ uint64_t lane_mask(bool c) { return __builtin_amdgcn_ballot_w64(c); }
+// w = 2 w + bit
+__device__ __forceinline__ uint32_t push_bit(uint32_t w, bool bit) { return w + w + static_cast<uint32_t>(bit); }
 
 // ---------------------------------------------------------------- operands
 
@@ -306,6 +304,22 @@ __device__ __forceinline__ void prepare_keys(const RawKeys<D, BF16> &R, float (&
   }
 }
 
+// The A operands (hi, lo per k-step) of one 16-row slab, fetched from LDS one
+// slab ahead of their use so the matrix products do not wait on LDS latency
+template <int D>
+struct SlabOps {
+  v8h a[Geo<D>::KS][2];
+};
+
+template <int D>
+__device__ __forceinline__ void fetch_slab(SlabOps<D> &A, const uint8_t *slab) {
+#pragma unroll
+  for (int k = 0; k < Geo<D>::KS; ++k) {
+    A.a[k][0] = lds_op(slab + (2 * k) * 1024);
+    A.a[k][1] = lds_op(slab + (2 * k + 1) * 1024);
+  }
+}
+
 // Index stage state across the coordinate tiles of one key tile
 template <int D, int W>
 struct IndexState {
@@ -316,11 +330,15 @@ struct IndexState {
 };
 
 template <int D, int W>
-__device__ __forceinline__ void index_begin(const KeyJob &job, IndexState<D, W> &S) {
+__device__ __forceinline__ void index_codebook(const KeyJob &job, IndexState<D, W> &S) {
 #pragma unroll
   for (int i = 0; i < IndexState<D, W>::NB; ++i) S.bnd[i] = job.boundaries[i] * kUp;
 #pragma unroll
   for (int i = 0; i <= IndexState<D, W>::NB; ++i) S.cen[i] = job.centroids[i] * kUp;
+}
+
+template <int D, int W>
+__device__ __forceinline__ void index_begin(IndexState<D, W> &S) {
 #pragma unroll
   for (int nt = 0; nt < Geo<D>::NT; ++nt) S.esq[nt] = 0.0f;
 }
@@ -332,7 +350,7 @@ __device__ __forceinline__ void index_begin(const KeyJob &job, IndexState<D, W> 
 // comparisons; bit p of it is the xor of the comparisons q with
 // (q + 1) % 2^p == 0.
 template <int D, int W, bool BF16>
-__device__ __forceinline__ void index_tile(int t, const uint8_t *slab, const Ops<D> &uh, const Ops<D> &ul,
+__device__ __forceinline__ void index_tile(int t, const SlabOps<D> &A, const Ops<D> &uh, const Ops<D> &ul,
                                            const float (&yscale)[Geo<D>::NT], IndexState<D, W> &S, Ops<D> &bh,
                                            Ops<D> &bl) {
   constexpr int NT = Geo<D>::NT;
@@ -342,8 +360,8 @@ __device__ __forceinline__ void index_tile(int t, const uint8_t *slab, const Ops
   for (int nt = 0; nt < NT; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < Geo<D>::KS; ++k) {
-    const v8h ah = lds_op(slab + (2 * k) * 1024);
-    const v8h al = lds_op(slab + (2 * k + 1) * 1024);
+    const v8h ah = A.a[k][0];
+    const v8h al = A.a[k][1];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(uh[nt][k]), acc[nt], 0, 0, 0);
@@ -357,17 +375,16 @@ __device__ __forceinline__ void index_tile(int t, const uint8_t *slab, const Ops
 #pragma unroll
     for (int i = 3; i >= 0; --i) {
       const float y = acc[nt][i] * yscale[nt];
-      uint64_t c[NB];
+      bool c[NB];
       float cv = S.cen[0];
 #pragma unroll
       for (int q = 0; q < NB; ++q) {
-        const bool gt = y > S.bnd[q];
-        c[q] = lane_mask(gt);
-        cv = gt ? S.cen[q + 1] : cv;
+        c[q] = y > S.bnd[q];
+        cv = c[q] ? S.cen[q + 1] : cv;
       }
 #pragma unroll
       for (int p = 0; p < W; ++p) {
-        uint64_t bit = 0;
+        bool bit = false;
 #pragma unroll
         for (int q = 0; q < NB; ++q)
           if (((q + 1) & ((1 << p) - 1)) == 0) bit ^= c[q];
@@ -394,8 +411,13 @@ __device__ __forceinline__ void index_group(int wl, const uint8_t *group, int g,
   for (int p = 0; p < W; ++p)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) S.wv[p][nt] = 0u;
+  SlabOps<D> A[2];
+  fetch_slab<D>(A[(cnt - 1) & 1], group + (cnt - 1) * Geo<D>::SLAB);
 #pragma unroll
-  for (int j = cnt - 1; j >= 0; --j) index_tile<D, W, BF16>(8 * wl + j, group + j * Geo<D>::SLAB, uh, ul, yscale, S, bh, bl);
+  for (int j = cnt - 1; j >= 0; --j) {
+    if (j > 0) fetch_slab<D>(A[(j - 1) & 1], group + (j - 1) * Geo<D>::SLAB);
+    index_tile<D, W, BF16>(8 * wl + j, A[j & 1], uh, ul, yscale, S, bh, bl);
+  }
 #pragma unroll
   for (int p = 0; p < W; ++p)
 #pragma unroll
@@ -406,6 +428,7 @@ __device__ __forceinline__ void index_group(int wl, const uint8_t *group, int g,
         v <<= 16 * (g & 1);
         v |= __shfl_xor(v, 16);
       }
+      asm volatile("" : "+v"(v));   // materialise the word now (see the resident kernel)
       cw[p][nt][wl] = v;
     }
 }
@@ -426,7 +449,7 @@ __device__ __forceinline__ void index_end(const IndexState<D, W> &S, const float
 // into sw at 4 (tz % 8) + i (trailing group: 4 (tz % 4) + i, then the half
 // words merge); a word is stored as soon as its group is complete.
 template <int D, bool THREE>
-__device__ __forceinline__ void sketch_slab(const KeyJob &job, const uint8_t *slab, int tz, int FM, int g,
+__device__ __forceinline__ void sketch_slab(const KeyJob &job, const SlabOps<D> &A, int tz, int FM, int g,
                                             const Ops<D> &bh, const Ops<D> &bl, const float (&nrm)[Geo<D>::NT],
                                             const TileLoc<D> &L, uint32_t (&sw)[Geo<D>::NT]) {
   constexpr int NT = Geo<D>::NT;
@@ -435,8 +458,8 @@ __device__ __forceinline__ void sketch_slab(const KeyJob &job, const uint8_t *sl
   for (int nt = 0; nt < NT; ++nt) z[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < Geo<D>::KS; ++k) {
-    const v8h ah = lds_op(slab + (2 * k) * 1024);
-    const v8h al = lds_op(slab + (2 * k + 1) * 1024);
+    const v8h ah = A.a[k][0];
+    const v8h al = A.a[k][1];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(bh[nt][k]), z[nt], 0, 0, 0);
@@ -520,22 +543,71 @@ __device__ __forceinline__ void key_operand_as_sketch_input(const Ops<D> &uh, co
   }
 }
 
+// z[tz] += sketch slab tz, k-step k (this lane's bytes of the slab at `slab`)
+// x the B operand (hi, and lo when THREE) of that k-step, for every key block
+template <int D, bool THREE>
+__device__ __forceinline__ void sketch_kstep(v4f (&z)[Geo<D>::NT], const uint8_t *slab, int k, const Op (&bh)[Geo<D>::NT],
+                                             const Op (&bl)[Geo<D>::NT]) {
+  const v8h ah = lds_op(slab + (2 * k) * 1024);
+  const v8h al = lds_op(slab + (2 * k + 1) * 1024);
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
+    z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(bh[nt]), z[nt], 0, 0, 0);
+    if (THREE) z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(bl[nt]), z[nt], 0, 0, 0);
+    z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_v8h(bh[nt]), z[nt], 0, 0, 0);
+  }
+}
+
+// Sign words from the finished sketch accumulators z[TMS][NT] (TMS slabs;
+// full groups of 8 slabs give one word per lane group, a trailing group of 4
+// a half word per lane group), stored at once.
+template <int D, int TMS>
+__device__ __forceinline__ void store_signs(const KeyJob &job, const v4f (&z)[TMS][Geo<D>::NT], int g,
+                                            const float (&nrm)[Geo<D>::NT], const TileLoc<D> &L) {
+  constexpr int FM = TMS / 8;
+  constexpr int WM = FM + (TMS % 8 ? 1 : 0);
+  const int64_t srow_bytes = job.m / 8;
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
+    const bool zero_key = !(nrm[nt] > 0.0f);
+#pragma unroll
+    for (int wl = 0; wl < WM; ++wl) {
+      const int cnt = wl < FM ? 8 : 4;
+      uint32_t v = 0u;
+#pragma unroll
+      for (int j = cnt - 1; j >= 0; --j)
+#pragma unroll
+        for (int i = 3; i >= 0; --i) v = push_bit(v, z[8 * wl + j][nt][i] >= 0.0f || zero_key);
+      if (cnt == 4) {
+        v <<= 16 * (g & 1);
+        v |= __shfl_xor(v, 16);
+      }
+      if (L.valid[nt] && (cnt == 8 || (g & 1) == 0))
+        reinterpret_cast<uint32_t *>(job.signs + L.row[nt] * srow_bytes)[cnt == 8 ? 4 * wl + g : 4 * FM + (g >> 1)] = v;
+    }
+  }
+}
+
 // ---- resident operands: the whole operand set sits in LDS; every wave then
 // walks its own key tiles (no block synchronisation), the next tile's keys
-// loading while the current one is computed.
-template <int D, int W, bool BF16>
+// loading while the current one is computed.  Within a tile the sketch is
+// accumulated k-step by k-step for all TMS slabs (z stays in registers) right
+// after the two coordinate tiles of that k-step are rotated and indexed, so
+// matrix products and vector work interleave; only one k-step of the
+// residual operand is ever live.
+template <int D, int W, bool BF16, int TMS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quantize_keys_resident_kernel(
     KeyJob job, int64_t n_tiles) {
   using Gm = Geo<D>;
   constexpr int NT = Gm::NT;
+  constexpr int KS = Gm::KS;
   constexpr bool THREE = W > 0 || !BF16;   // the sketch's B operand has a low part
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int TM = job.m / 16, FM = TM / 8;
-  const int pi_slabs = W > 0 ? Gm::TD : 0;
-  copy_to_lds(job.ops, smem, (pi_slabs + TM) * Gm::SLAB, wave, lane);
+  constexpr int pi_slabs = W > 0 ? Gm::TD : 0;
+  copy_to_lds(job.ops, smem, (pi_slabs + TMS) * Gm::SLAB, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const uint8_t *pi_lds = smem + 16 * lane;
@@ -544,12 +616,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   int64_t tile = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
   if (tile >= n_tiles) return;
+  IndexState<D, W> S;
+  if constexpr (W > 0) index_codebook<D, W>(job, S);
   TileLoc<D> L = locate<D>(job, tile * Gm::KT, n);
   RawKeys<D, BF16> R;
   load_keys<D, BF16>(job, L, g, R);
   for (; tile < n_tiles; tile += stride) {
     float nrm[NT], yscale[NT];
-    Op uh[NT][Gm::KS], ul[NT][Gm::KS];
+    Op uh[NT][KS], ul[NT][KS];
     prepare_keys<D, BF16>(R, nrm, yscale, uh, ul);
     // prefetch the next tile
     const TileLoc<D> Lc = L;
@@ -557,23 +631,78 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       L = locate<D>(job, (tile + stride) * Gm::KT, n);
       load_keys<D, BF16>(job, L, g, R);
     }
+    v4f z[TMS][NT];
+#pragma unroll
+    for (int tz = 0; tz < TMS; ++tz)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) z[tz][nt] = v4f{0.f, 0.f, 0.f, 0.f};
     uint32_t cw[W > 0 ? W : 1][NT][Gm::WPL];
     float gam[NT];
-    Op bh[NT][Gm::KS], bl[NT][Gm::KS];
     if constexpr (W > 0) {
-      IndexState<D, W> S;
-      index_begin<D, W>(job, S);
+      index_begin<D, W>(S);
+      // k-steps from the last down: tiles 2k+1, 2k keep the word bits most
+      // significant first
 #pragma unroll
-      for (int wl = 0; wl < Gm::WPL; ++wl)
-        index_group<D, W, BF16>(wl, pi_lds + 8 * wl * Gm::SLAB, g, uh, ul, yscale, S, cw, bh, bl);
+      for (int k = KS - 1; k >= 0; --k) {
+        const int t_hi = 2 * k + 1;
+        const int wl = t_hi >> 3;
+        const bool group_top = wl < Gm::FD ? (t_hi & 7) == 7 : (t_hi & 7) == 3;
+        if (group_top) {
+#pragma unroll
+          for (int p = 0; p < W; ++p)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) S.wv[p][nt] = 0u;
+        }
+        Ops<D> bh, bl;   // only k-step k is filled and used
+        SlabOps<D> A;
+        fetch_slab<D>(A, pi_lds + t_hi * Gm::SLAB);
+        index_tile<D, W, BF16>(t_hi, A, uh, ul, yscale, S, bh, bl);
+        fetch_slab<D>(A, pi_lds + (t_hi - 1) * Gm::SLAB);
+        index_tile<D, W, BF16>(t_hi - 1, A, uh, ul, yscale, S, bh, bl);
+        if (((t_hi - 1) & 7) == 0) {
+          // bottom tile of word group wl: the words are complete
+#pragma unroll
+          for (int p = 0; p < W; ++p)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              uint32_t v = S.wv[p][nt];
+              if (wl == Gm::FD) {
+                v <<= 16 * (g & 1);
+                v |= __shfl_xor(v, 16);
+              }
+              // materialise the word now (empty asm): left alone, the compiler
+              // sinks the bit assembly to the stores and keeps every comparison
+              // mask alive until then
+              asm volatile("" : "+v"(v));
+              cw[p][nt][wl] = v;
+            }
+        }
+        Op kh[NT], kl[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          kh[nt] = bh[nt][k];
+          kl[nt] = bl[nt][k];
+        }
+#pragma unroll
+        for (int tz = 0; tz < TMS; ++tz) sketch_kstep<D, THREE>(z[tz], sk_lds + tz * Gm::SLAB, k, kh, kl);
+      }
       index_end<D, W>(S, nrm, gam);
     } else {
-      key_operand_as_sketch_input<D>(uh, ul, bh, bl, gam);
-    }
-    uint32_t sw[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) sw[nt] = 0u;
-    for (int tz = 0; tz < TM; ++tz) sketch_slab<D, THREE>(job, sk_lds + tz * Gm::SLAB, tz, FM, g, bh, bl, nrm, Lc, sw);
+      for (int nt = 0; nt < NT; ++nt) gam[nt] = 0.0f;
+#pragma unroll
+      for (int k = KS - 1; k >= 0; --k) {
+        Op kh[NT], kl[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          kh[nt] = uh[nt][k];
+          kl[nt] = ul[nt][k];
+        }
+#pragma unroll
+        for (int tz = 0; tz < TMS; ++tz) sketch_kstep<D, THREE>(z[tz], sk_lds + tz * Gm::SLAB, k, kh, kl);
+      }
+    }
+    store_signs<D, TMS>(job, z, g, nrm, Lc);
     store_codes_norms<D, W>(job, Lc, g, cw, nrm, gam);
   }
 }
@@ -611,7 +740,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   Op bh[NT][Gm::KS], bl[NT][Gm::KS];
   if constexpr (W > 0) {
     IndexState<D, W> S;
-    index_begin<D, W>(job, S);
+    index_codebook<D, W>(job, S);
+    index_begin<D, W>(S);
 #pragma unroll
     for (int wl = 0; wl < Gm::WPL; ++wl) {
       if (wl > 0) {
@@ -642,9 +772,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
     if (c + 1 < n_chunks) stage(c + 1);
     const uint8_t *buf = smem + (c & 1) * CHUNK + 16 * lane;
+    SlabOps<D> A[2];
+    fetch_slab<D>(A[0], buf);
 #pragma unroll
-    for (int j = 0; j < CH; ++j)
-      sketch_slab<D, THREE>(job, buf + j * Gm::SLAB, c * CH + j, FM, g, bh, bl, nrm, L, sw);
+    for (int j = 0; j < CH; ++j) {
+      if (j + 1 < CH) fetch_slab<D>(A[(j + 1) & 1], buf + (j + 1) * Gm::SLAB);
+      sketch_slab<D, THREE>(job, A[j & 1], c * CH + j, FM, g, bh, bl, nrm, L, sw);
+    }
   }
   store_codes_norms<D, W>(job, L, g, cw, nrm, gam);
 }
@@ -665,10 +799,16 @@ hipError_t launch_dwt(const KeyJob &job, hipStream_t stream) {
   const int64_t total = job.n_slots * job.n_tokens;
   const int64_t n_tiles = (total + Gm::KT - 1) / Gm::KT;
   const size_t ops = key_operand_bytes(D, W, job.m);
+  const int tm = job.m / 16;
+  // resident: d <= 128, every operand in LDS, at most 16 sketch slabs in registers
   bool resident = false;
-  if constexpr (D <= 128) resident = ops <= kLdsMax;
+  if constexpr (D <= 128) resident = ops <= kLdsMax && tm <= 16;
   if (resident) {
-    auto kern = quantize_keys_resident_kernel<D <= 128 ? D : 128, W, BF16>;
+    constexpr int DR = D <= 128 ? D : 128;
+    auto kern = tm == 4 ? quantize_keys_resident_kernel<DR, W, BF16, 4>
+              : tm == 8 ? quantize_keys_resident_kernel<DR, W, BF16, 8>
+              : tm == 12 ? quantize_keys_resident_kernel<DR, W, BF16, 12>
+                         : quantize_keys_resident_kernel<DR, W, BF16, 16>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(ops));
     if (e != hipSuccess) return e;
