@@ -26,6 +26,9 @@ HIP_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # never emit packed fp32 ALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix instructions read and write their accumulators in VGPRs (no AGPR copies
+    # around the VALU work that shares them)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 

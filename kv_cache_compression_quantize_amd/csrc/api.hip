@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "internal.h"
 
 using namespace aqkv;
@@ -77,7 +79,10 @@ DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int6
   const size_t heads = static_cast<size_t>(n_slots) * g;
   p.acc_bytes = round_up(heads * p.n_split * d * sizeof(float), 256);
   p.ml_bytes = round_up(heads * p.n_split * 2 * sizeof(float), 256);
-  p.total_bytes = p.acc_bytes + p.ml_bytes;
+  p.pack_bytes = p.mfma ? round_up(decode_mfma_pack_bytes(d, w, g, m, n_slots), 256) : 0;
+  p.const_bytes = p.mfma ? round_up(heads * 4 * sizeof(float), 256) : 0;
+  p.odd_bytes = p.mfma ? round_up(static_cast<size_t>(n_slots) * sizeof(int), 256) : 0;
+  p.total_bytes = p.acc_bytes + p.ml_bytes + p.pack_bytes + p.const_bytes + p.odd_bytes;
   return p;
 }
 
@@ -314,9 +319,19 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   job.scores = scores;
   job.out = out;
   job.part_acc = static_cast<float *>(workspace);
-  job.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) + plan.acc_bytes);
+  char *ws = static_cast<char *>(workspace);
+  job.part_ml = reinterpret_cast<float *>(ws + plan.acc_bytes);
+  job.qpack = reinterpret_cast<uint8_t *>(ws + plan.acc_bytes + plan.ml_bytes);
+  job.qconst = reinterpret_cast<float *>(ws + plan.acc_bytes + plan.ml_bytes + plan.pack_bytes);
+  job.qodd = reinterpret_cast<int *>(ws + plan.acc_bytes + plan.ml_bytes + plan.pack_bytes + plan.const_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (plan.mfma) return hip_status(launch_decode_mfma(job, s));
+  if (plan.mfma) {
+    // the matrix-core decoder addresses a slot's rows of a plane with 32-bit byte offsets
+    const int64_t row_max = std::max<int64_t>({int64_t(w) * d / 8, int64_t(m) / 8, int64_t(d) * cfg->value_bits / 8,
+                                               int64_t(d) / 32 * 4});
+    if (cache->capacity * row_max >= (int64_t(1) << 31)) return AQKV_ERR_UNSUPPORTED;
+    return hip_status(launch_decode_mfma(job, s));
+  }
   return hip_status(launch_decode(job, s));
 }
 

@@ -1,0 +1,662 @@
+// Decode attention on the packed cache with CDNA4 matrix cores
+// (TurboQuant article §五 estimator, §六 fused decode with online softmax;
+// A-QJL article, pure-QJL keys).  Template shared by the per-head_dim
+// instantiation files decode_fast_d*.hip.
+//
+// Scores as integer matrix products on the packed bits.  For a codebook c of
+// 2^w levels, c(idx) = c[0] + sum_A kappa_A par_A(idx) over the non-empty
+// subsets A of the w index bits, par_A = xor of those bits (a Walsh transform
+// of the codebook; for an odd-symmetric Lloyd-Max codebook only the subsets of
+// odd size have kappa_A != 0).  Hence
+//   <q_rot, c[idx_t]>    = c[0] sum(q_rot) + sum_A kappa_A <q_rot, par_A(t)>
+//   <q_sk, 2 bits_t - 1> = 2 <q_sk, bits_t> - sum(q_sk)
+// and every score is a fixed combination of dot products between query rows
+// and {0,1} bit-planes of the cached keys.  decode_pack_kernel quantises the
+// query side (kappa_A q_rot, 2 q_sk) once per call to 15-bit integers split
+// into int8 hi / lo parts, laid out as ready-made matrix-core A operands.
+// v_mfma_i32_16x16x64_i8 then contracts 64 coordinates of 16 tokens for 16
+// rows = 4 heads x {mse hi, mse lo, qjl hi, qjl lo} with exact integer
+// accumulation; a key bit becomes an int8 {0,1} operand byte with one shift
+// and one mask per 4 bits (bit rows are byte-transposed for this).
+//
+// Values: out[g] = sum_t p_t (code_t scale_t + min_t).  The f16 operand
+// 1 + code/4 (2-bit codes; 1 + code/16 for 4-bit) is exact and is built with
+// one shift and one and-or from the 32-token block word that holds 8 tokens'
+// codes of one channel; the token weights a_t = p_t scale_t are split into f16
+// hi + lo rows and v_mfma_f32_16x16x32_f16 accumulates sum_t a_t (1 + code_t/4)
+// over 32 tokens; sum_t p_t (min_t - 4 scale_t) is added at the end.
+//
+// Work: block (slot, split) of 4 waves; each wave walks 32-token tiles of the
+// block's range (interleaved across waves) with its own online-softmax state.
+// Every shape parameter is a template constant, so a tile is straight-line
+// code.  Every plane of a tile goes HBM -> LDS with buffer_load_dwordx4 ... lds
+// (per-slot buffer resources, wave-uniform tile offsets) into a per-wave ring
+// of three tile buffers, so two tiles stream in while one is computed.  The
+// waves merge in LDS; combine_kernel merges the splits.
+#pragma once
+
+#include <math.h>
+
+#include "internal.h"
+
+namespace aqkv {
+namespace fast {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kTT = 32;          // tokens per wave tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;    // keep the running max unless a tile exceeds it by 2^8
+constexpr int kRegAVgprs = 48;   // query operands live in VGPRs up to this many registers, else in LDS
+
+__host__ __device__ constexpr int popc(int x) { return x ? (x & 1) + popc(x >> 1) : 0; }
+// bit A set for every non-empty subset A of the w index bits of odd size / of any size
+__host__ __device__ constexpr int odd_planes(int w) {
+  int m = 0;
+  for (int a = 1; a < (1 << w); ++a)
+    if (popc(a) & 1) m |= 1 << a;
+  return m;
+}
+__host__ __device__ constexpr int all_planes(int w) {
+  int m = 0;
+  for (int a = 1; a < (1 << w); ++a) m |= 1 << a;
+  return m;
+}
+__host__ __device__ constexpr int heads_rb(int g) { return (g + 3) / 4; }
+// chunks (64 K-slots each) the pack kernel lays out per row block: all planes + signs
+__host__ __device__ constexpr int chunks_max(int d, int w, int m) { return ((1 << w) - 1) * (d / 64) + m / 64; }
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// v_mul_legacy_f32: 0 * x = 0 for every x (Inf and NaN included)
+__device__ float fmul_legacy(float a, float b) __asm("llvm.amdgcn.fmul.legacy");
+
+// Bit-row words hold element j = 4 i + k at bit 8 k + i, so (x >> i) & 0x01010101
+// is elements 4i .. 4i+3 as int8 {0,1} bytes.  Half hf of a word (elements
+// 16 hf .. 16 hf + 15) -> the 16 operand bytes of one K-chunk.
+__device__ __forceinline__ v4i spread_half(uint32_t x, int hf) {
+  v4i r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = static_cast<int>((x >> (4 * hf + k)) & 0x01010101u);
+  return r;
+}
+
+// max over the 16 lanes of a DPP row, result in every lane of the row: one
+// v_max_f32 with a DPP source per step (the s_nop covers the VALU-write ->
+// DPP-read hazard the compiler cannot see through the asm)
+__device__ __forceinline__ float row_max16(float x) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
+      : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// Buffer resource over the rows of one cache plane of one slot (raw, untyped
+// loads; records = bytes, reads past them return 0).  Offsets are 32-bit, so a
+// slot's rows of a plane must span fewer than 2^31 bytes (the host checks this).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// Wave-wide asynchronous copy of BYTES (multiple of 16) bytes at byte offset
+// soff (wave-uniform) of a plane to LDS: lane l moves bytes 16 l .. 16 l + 15
+// of every 1 KiB piece (buffer_load_dwordx4 ... lds).
+template <int BYTES>
+__device__ __forceinline__ void copy_region(__amdgpu_buffer_rsrc_t rs, uint32_t soff, uint8_t *l, int lane) {
+#pragma unroll
+  for (int off = 0; off < BYTES; off += 1024) {
+    if (BYTES - off >= 1024 || 16 * lane < BYTES - off)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8 *)(l + off), 16, 16 * lane, static_cast<int>(soff + off), 0, 0);
+  }
+}
+template <int BYTES>
+__host__ __device__ constexpr int loads_of() { return (BYTES + 1023) / 1024; }
+
+// s_waitcnt with only the vector-memory counter limited to N (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Per-head constants the pack kernel writes next to the operands.
+struct HeadConst {
+  float sig_mse, sig_qjl, c_mse, c_qjl;
+};
+
+// value-weight pairs per lane: pair k of lane group pq is (head, group) =
+// divmod(pq + 4 k, D / 32)
+__host__ __device__ constexpr int pairs_of(int g, int d) { return (g * (d / 32) + 3) / 4; }
+
+// Tile staging: every cache plane of 32 tokens, copied whole into a per-wave
+// ring of kRing buffers (tiles t+1 .. t+kRing-1 stream in while t is computed).
+constexpr int kRing = 3;
+__host__ __device__ constexpr int tile_bytes_of(int d, int w, int mc, int vb) {
+  return kTT * (w * d / 8 + mc * 8 + 4 + (w > 0 ? 4 : 0) + d * vb / 8 + 8 * (d / 32));
+}
+// LDS bytes per block of decode_fast_kernel<D, W, m / 64, G, VB> (host and device):
+// per wave the tile ring, the softmax weights P [32 tokens][G] and the value-weight
+// operand [groups][4][2G rows][16 B]; at the end the 4-wave merge
+__host__ __device__ constexpr int wave_lds_of(int d, int w, int mc, int g, int vb) {
+  return kRing * tile_bytes_of(d, w, mc, vb) + kTT * g * 4 + (d / 32) * 4 * 2 * g * 16;
+}
+__host__ __device__ constexpr int smem_of(int d, int w, int mc, int g, int vb) {
+  const int waves = kWaves * wave_lds_of(d, w, mc, g, vb);
+  const int merge = kWaves * (g * d + 2 * g + g * (d / 32)) * 4;
+  const int nc_all = chunks_max(d, w, 64 * mc);
+  const int qa = heads_rb(g) * nc_all * 4 <= kRegAVgprs ? 0 : heads_rb(g) * nc_all * 1024;
+  return qa + (waves > merge ? waves : merge);
+}
+
+template <int D, int W, int MC, int G, int VB>
+struct Geo {
+  static constexpr int RB = heads_rb(G);
+  static constexpr int HC = D / 64;                  // K-chunks per code plane
+  static constexpr int kGroups = D / 32;
+  static constexpr int CB = W * D / 8;               // key code bytes per token
+  static constexpr int SB = MC * 8;                  // sign bytes per token (m / 8)
+  static constexpr int VBY = D * VB / 8;             // value code bytes per token
+  static constexpr int NCmax = chunks_max(D, W, 64 * MC);
+  static constexpr int kWpl = D >= 128 ? D / 128 : 1;    // plane words per lane per token
+  static constexpr int kSw = (MC + 1) / 2;               // sign words per lane per token
+  static constexpr int kPairs = pairs_of(G, D);
+  static constexpr int o_signs = kTT * CB;
+  static constexpr int o_norm = o_signs + kTT * SB;
+  static constexpr int o_rnorm = o_norm + kTT * 4;
+  static constexpr int o_vcodes = o_rnorm + (W > 0 ? kTT * 4 : 0);
+  static constexpr int o_vscale = o_vcodes + kTT * VBY;
+  static constexpr int o_vmin = o_vscale + kTT * kGroups * 4;
+  static constexpr int tile_bytes = o_vmin + kTT * kGroups * 4;
+  static_assert(tile_bytes == tile_bytes_of(D, W, MC, VB), "tile geometry");
+  static constexpr int wave_lds = wave_lds_of(D, W, MC, G, VB);
+  // load instructions per tile (each wave waits on whole tiles)
+  static constexpr int loads_per_tile = (W > 0 ? loads_of<kTT * CB>() + loads_of<kTT * 4>() : 0) +
+                                        loads_of<kTT * SB>() + loads_of<kTT * 4>() + loads_of<kTT * VBY>() +
+                                        2 * loads_of<kTT * kGroups * 4>();
+  static constexpr int nc_all = chunks_max(D, W, 64 * MC);
+  static constexpr bool reg_a_all = RB * nc_all * 4 <= kRegAVgprs;
+  static constexpr int qa_lds_bytes = reg_a_all ? 0 : RB * nc_all * 1024;
+  static constexpr int smem = smem_of(D, W, MC, G, VB);
+};
+
+template <int D, int W, int MC, int G, int VB, int PL>
+__device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, int split, uint8_t *smem) {
+  using Gm = Geo<D, W, MC, G, VB>;
+  constexpr int RB = Gm::RB, HC = Gm::HC, kGroups = Gm::kGroups, CB = Gm::CB, SB = Gm::SB, VBY = Gm::VBY;
+  constexpr int kWpl = Gm::kWpl, kSw = Gm::kSw, kPairs = Gm::kPairs;
+  constexpr int NP = popc(PL);
+  constexpr int NC = NP * HC + MC;
+  constexpr int NCmax = Gm::NCmax;
+  constexpr bool kRegA = RB * NC * 4 <= kRegAVgprs;
+  constexpr float kMag = VB == 2 ? 4.0f : 16.0f;
+  constexpr uint32_t one16 = 0x3c003c00u;   // f16 pair {1, 1}
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform in an SGPR: tile offsets and LDS bases derive from it
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, q = lane >> 4;
+  const int64_t t_begin = static_cast<int64_t>(split) * job.split_tokens;
+  const int64_t t_end = min<int64_t>(job.context, t_begin + job.split_tokens);
+  const int64_t head0 = slot * G;
+
+  // ---- query operands and per-head constants from the pack kernel
+  const uint8_t *qp = job.qpack + slot * static_cast<int64_t>(RB * NCmax * 1024);
+  uint8_t *qa_lds = smem;
+  uint8_t *wbase = smem + Gm::qa_lds_bytes + wave * Gm::wave_lds;
+  v4i aq[kRegA ? RB : 1][kRegA ? NC : 1];
+  if constexpr (kRegA) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) aq[r][c] = *reinterpret_cast<const v4i *>(qp + ((r * NCmax + c) * 64 + lane) * 16);
+  } else {
+    for (int i = tid; i < RB * NC * 64; i += kThreads) {
+      const int rc = i / 64, l = i % 64;
+      const int r = rc / NC, c = rc % NC;
+      reinterpret_cast<v4i *>(qa_lds)[i] = *reinterpret_cast<const v4i *>(qp + ((r * NCmax + c) * 64 + l) * 16);
+    }
+    __syncthreads();
+  }
+  auto A = [&](int r, int c) -> v4i {
+    if constexpr (kRegA) return aq[r][c];
+    else return *reinterpret_cast<const v4i *>(qa_lds + ((r * NC + c) * 64 + lane) * 16);
+  };
+  HeadConst hc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int g = 4 * r + q;
+    if (g < G) hc[r] = reinterpret_cast<const HeadConst *>(job.qconst)[head0 + g];
+    else hc[r] = HeadConst{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const float kappa_qjl = 1.2533141373155003f / static_cast<float>(64 * MC);   // sqrt(pi/2) / m
+  const float lscale = job.softmax_scale * kLog2e;
+
+  float *P = reinterpret_cast<float *>(wbase + kRing * Gm::tile_bytes);             // [kTT][G]
+  uint8_t *aval = wbase + kRing * Gm::tile_bytes + kTT * G * 4;                     // [grp][q][2G][16 B]
+
+  // ---- per-wave state
+  float m_ref[RB], l_part[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) { m_ref[r] = -INFINITY; l_part[r] = 0.0f; }
+  v4f cval[2 * kGroups];
+#pragma unroll
+  for (int i = 0; i < 2 * kGroups; ++i) cval[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  float corr[kPairs];
+#pragma unroll
+  for (int i = 0; i < kPairs; ++i) corr[i] = 0.0f;
+
+  // ---- per-slot plane resources (byte offsets relative to row slot * capacity)
+  const int64_t n_tiles = (t_end > t_begin) ? (t_end - t_begin + kTT - 1) / kTT : 0;
+  const int64_t r0 = slot * job.capacity;
+  const uint32_t cap = static_cast<uint32_t>(job.capacity);
+  const __amdgpu_buffer_rsrc_t rs_codes = plane_rsrc(W > 0 ? job.codes + r0 * CB : job.signs, cap * (W > 0 ? CB : 1));
+  const __amdgpu_buffer_rsrc_t rs_signs = plane_rsrc(job.signs + r0 * SB, cap * SB);
+  const __amdgpu_buffer_rsrc_t rs_norm = plane_rsrc(job.norm + r0, cap * 4);
+  const __amdgpu_buffer_rsrc_t rs_rnorm = plane_rsrc(W > 0 ? job.rnorm + r0 : job.norm + r0, cap * 4);
+  const __amdgpu_buffer_rsrc_t rs_vcodes = plane_rsrc(job.vcodes + r0 * VBY, cap * VBY);
+  const __amdgpu_buffer_rsrc_t rs_vscale = plane_rsrc(job.vscale + r0 * kGroups, cap * kGroups * 4);
+  const __amdgpu_buffer_rsrc_t rs_vmin = plane_rsrc(job.vmin + r0 * kGroups, cap * kGroups * 4);
+  auto issue = [&](int64_t tile) {
+    const uint32_t t = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t_begin + tile * kTT));
+    uint8_t *b = wbase + static_cast<int>((tile / kWaves) % kRing) * Gm::tile_bytes;
+    if constexpr (W > 0) copy_region<kTT * CB>(rs_codes, t * CB, b, lane);
+    copy_region<kTT * SB>(rs_signs, t * SB, b + Gm::o_signs, lane);
+    copy_region<kTT * 4>(rs_norm, t * 4, b + Gm::o_norm, lane);
+    if constexpr (W > 0) copy_region<kTT * 4>(rs_rnorm, t * 4, b + Gm::o_rnorm, lane);
+    copy_region<kTT * VBY>(rs_vcodes, t * VBY, b + Gm::o_vcodes, lane);
+    copy_region<kTT * kGroups * 4>(rs_vscale, t * kGroups * 4, b + Gm::o_vscale, lane);
+    copy_region<kTT * kGroups * 4>(rs_vmin, t * kGroups * 4, b + Gm::o_vmin, lane);
+  };
+
+  // weight tokens: K-slot 8 q' + i of the value product is token 4 i + q'; lane
+  // (tp, pq) handles tokens ta = 8 (tp / 4) + tp % 4 and ta + 4
+  const int ta = 8 * (n16 >> 2) + (n16 & 3), tb4 = ta + 4;
+
+  int64_t tile = wave;
+#pragma unroll
+  for (int k = 0; k < kRing - 1; ++k)
+    if (tile + k * kWaves < n_tiles) issue(tile + k * kWaves);
+  for (; tile < n_tiles; tile += kWaves) {
+    // wait for this tile: the later tiles already issued may stay in flight
+    static_assert(kRing == 3, "wait ladder below assumes two tiles in flight");
+    if (tile + kWaves < n_tiles) wait_vm<Gm::loads_per_tile>();
+    else wait_vm<0>();
+    compiler_fence();
+    if (tile + (kRing - 1) * kWaves < n_tiles) issue(tile + (kRing - 1) * kWaves);
+    const uint8_t *tb = wbase + static_cast<int>((tile / kWaves) % kRing) * Gm::tile_bytes;
+    const int64_t t0 = t_begin + tile * kTT;
+    const int nt = static_cast<int>(min<int64_t>(kTT, t_end - t0));
+
+    // ---------------- scores: 2 column tiles of 16 tokens, their matrix chains interleaved
+    v4i acc[2][RB];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < RB; ++r) acc[ct][r] = v4i{0, 0, 0, 0};
+    {
+      // this lane's words: coordinates (D/4) q .. (D/4) q + D/4 - 1 of each index
+      // plane (D = 64: half of one word) and sketch rows 16 MC q .. 16 MC q + 16 MC - 1
+      uint32_t pw[2][W > 0 ? W : 1][kWpl], sw[2][kSw];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int tok = 16 * ct + n16;
+        if constexpr (W > 0) {
+#pragma unroll
+          for (int k = 0; k < W; ++k)
+#pragma unroll
+            for (int u = 0; u < kWpl; ++u) {
+              const int word = D >= 128 ? kWpl * q + u : q / 2;
+              pw[ct][k][u] = *reinterpret_cast<const uint32_t *>(tb + tok * CB + k * (D / 8) + 4 * word);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kSw; ++u)
+          sw[ct][u] = *reinterpret_cast<const uint32_t *>(tb + Gm::o_signs + tok * SB + 4 * (((MC * q) >> 1) + u));
+      }
+      int chunk = 0;
+      if constexpr (W > 0) {
+#pragma unroll
+        for (int a = 1; a < (1 << W); ++a) {
+          if ((PL >> a) & 1) {
+#pragma unroll
+            for (int h = 0; h < HC; ++h) {
+              // chunk h = coordinates (D/4) q + 16 h .. + 15
+              const int hf = D >= 128 ? (h & 1) : (q & 1);
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct) {
+                uint32_t x = 0;
+#pragma unroll
+                for (int k = 0; k < W; ++k)
+                  if ((a >> k) & 1) x ^= pw[ct][k][D >= 128 ? h >> 1 : 0];
+                const v4i bop = spread_half(x, hf);
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+                  acc[ct][r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A(r, chunk), bop, acc[ct][r], 0, 0, 0);
+              }
+              ++chunk;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < MC; ++h) {
+        // sketch rows 16 MC q + 16 h .. + 15: word (16 MC q + 16 h) / 32, half ((16 MC q + 16 h) / 16) & 1
+        const int c = 16 * MC * q + 16 * h;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          uint32_t word;
+          int hf;
+          if constexpr (MC % 2 == 0) {
+            word = sw[ct][h >> 1];
+            hf = h & 1;
+          } else {
+            // odd MC: the lane's first row may sit in the upper half of a word
+            const int wi = (c >> 5) - ((16 * MC * q) >> 5);
+            word = sw[ct][0];
+#pragma unroll
+            for (int u = 1; u < kSw; ++u) word = (wi == u) ? sw[ct][u] : word;
+            hf = (c >> 4) & 1;
+          }
+          const v4i bop = spread_half(word, hf);
+#pragma unroll
+          for (int r = 0; r < RB; ++r)
+            acc[ct][r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A(r, chunk), bop, acc[ct][r], 0, 0, 0);
+        }
+        ++chunk;
+      }
+    }
+    float logit[2][RB], score[2][RB];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int tok = 16 * ct + n16;
+      const float nrm = reinterpret_cast<const float *>(tb + Gm::o_norm)[tok];
+      const float gam = W > 0 ? reinterpret_cast<const float *>(tb + Gm::o_rnorm)[tok] : nrm;
+      const bool valid = tok < nt;
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const int g = 4 * r + q;
+        float s = 0.0f;
+        if constexpr (W > 0)
+          s = nrm * fmaf(hc[r].sig_mse, static_cast<float>(acc[ct][r][0] * 128 + acc[ct][r][1]), hc[r].c_mse);
+        const float qjl = fmaf(hc[r].sig_qjl, static_cast<float>(acc[ct][r][2] * 128 + acc[ct][r][3]), hc[r].c_qjl);
+        s = fmaf(kappa_qjl * gam, qjl, s);
+        score[ct][r] = s;
+        logit[ct][r] = (valid && g < G) ? s * lscale : -INFINITY;
+      }
+    }
+
+    // ---------------- online softmax (lazy rescale); lane group q = head 4r + q
+    float fac[RB];
+    bool changed = false;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const float tmax = row_max16(fmaxf(logit[0][r], logit[1][r]));
+      float f = 1.0f;
+      if (tmax > m_ref[r] + kLazy) {
+        f = __builtin_amdgcn_exp2f(m_ref[r] - tmax);       // 0 on the first update (m_ref = -inf)
+        m_ref[r] = tmax;
+        changed = true;
+      }
+      fac[r] = f;
+      const int g = 4 * r + q;
+      float psum = 0.0f;
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        // exp2(-inf) = 0 for masked tokens; m_ref is finite for every real head here
+        const float p = __builtin_amdgcn_exp2f(logit[ct][r] - m_ref[r]);
+        psum += p;
+        if (g < G) P[(16 * ct + n16) * G + g] = p;
+      }
+      l_part[r] = l_part[r] * f + psum;
+    }
+    if (job.scores) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const int g = 4 * r + q, tok = 16 * ct + n16;
+          if (g < G && tok < nt) job.scores[(head0 + g) * job.context + t0 + tok] = score[ct][r];
+        }
+    }
+    if (__any(changed)) {
+      // factor of head g lives in lane 16 * (g % 4), row block g / 4
+      float fh[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) fh[g] = __shfl(fac[g / 4], 16 * (g % 4));
+      // value rows of lane group q: heads 2q, 2q+1 (hi, lo)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float fv = 1.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) fv = (g == 2 * q + e) ? fh[g] : fv;
+#pragma unroll
+        for (int i = 0; i < 2 * kGroups; ++i) {
+          cval[i][2 * e] *= fv;
+          cval[i][2 * e + 1] *= fv;
+        }
+      }
+      // correction sums: pair k of lane group q is (head, group) = divmod(q + 4 k, kGroups)
+#pragma unroll
+      for (int k = 0; k < kPairs; ++k) {
+        const int pair = q + 4 * k;
+        float fv = 1.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) fv = (g == pair / kGroups) ? fh[g] : fv;
+        corr[k] *= fv;
+      }
+    }
+    compiler_fence();
+
+    // ---------------- value weights a = p * scale (f16 hi + lo), correction sums
+    {
+      const int qd = n16 & 3, i0 = 2 * (n16 >> 2);
+      const float *vs = reinterpret_cast<const float *>(tb + Gm::o_vscale);
+      const float *vm = reinterpret_cast<const float *>(tb + Gm::o_vmin);
+      float pa[G], pb[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        pa[g] = P[ta * G + g];
+        pb[g] = P[tb4 * G + g];
+      }
+#pragma unroll
+      for (int k = 0; k < kPairs; ++k) {
+        const int pair = q + 4 * k;
+        if (pair < G * kGroups) {
+          const int g = pair / kGroups, grp = pair % kGroups;
+          const float sa = vs[ta * kGroups + grp], sb = vs[tb4 * kGroups + grp];
+          const float ma = vm[ta * kGroups + grp], mb = vm[tb4 * kGroups + grp];
+          // legacy multiply: 0 * x = 0 for any x, so masked tokens (p = 0) ignore
+          // whatever their cache rows hold
+          float aa = fmul_legacy(pa[g], sa);
+          float ab = fmul_legacy(pb[g], sb);
+          // pin the fp32 weights so both uses of the f16 high part round the same value
+          asm volatile("" : "+v"(aa), "+v"(ab));
+          corr[k] += fmul_legacy(pa[g], fmaf(-kMag, sa, ma));
+          corr[k] += fmul_legacy(pb[g], fmaf(-kMag, sb, mb));
+          const _Float16 ha = static_cast<_Float16>(aa), hb = static_cast<_Float16>(ab);
+          const _Float16 la = static_cast<_Float16>(aa - static_cast<float>(ha));
+          const _Float16 lb = static_cast<_Float16>(ab - static_cast<float>(hb));
+          uint8_t *dst = aval + ((grp * 4 + qd) * (2 * G) + 2 * g) * 16 + 2 * i0;
+          *reinterpret_cast<uint32_t *>(dst) =
+              static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ha)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hb)) << 16);
+          *reinterpret_cast<uint32_t *>(dst + 16) =
+              static_cast<uint32_t>(__builtin_bit_cast(uint16_t, la)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lb)) << 16);
+        }
+      }
+    }
+    compiler_fence();
+
+    // ---------------- value products: 32 tokens x 16 channels per matrix instruction
+    {
+      const uint8_t *vc = tb + Gm::o_vcodes;
+#pragma unroll
+      for (int grp = 0; grp < kGroups; ++grp) {
+        // rows >= 2G of the weight operand are zero
+        v8h aop = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+        if (G == 8 || n16 < 2 * G) aop = *reinterpret_cast<const v8h *>(aval + ((grp * 4 + q) * (2 * G) + n16) * 16);
+        // block word(s) of column n16: tokens 4 i + q of channels 32 grp + 16 h + n16;
+        // operand dword k = K-slots (8q + 2k, 8q + 2k + 1) = i (2k, 2k + 1)
+        uint32_t wv[2];
+        if constexpr (VB == 2) {
+          wv[0] = reinterpret_cast<const uint32_t *>(vc)[(16 * grp + n16) * 4 + q];
+        } else {
+          const uint2 t2 = reinterpret_cast<const uint2 *>(vc)[(16 * grp + n16) * 4 + q];
+          wv[0] = t2.x;
+          wv[1] = t2.y;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          v4i bw;
+          if constexpr (VB == 2) {
+            // h = 0: code of i = 2k at bits 2k, of 2k+1 at 16 + 2k; h = 1: 8 bits higher
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t sh = h == 0 ? (wv[0] << (8 - 2 * k)) : (wv[0] >> (2 * k));
+              bw[k] = static_cast<int>((sh & 0x03000300u) | one16);
+            }
+          } else {
+            // code of i = 2k at bits 4k, of 2k+1 at 16 + 4k -> mantissa bits 6..9
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t sh = k < 2 ? (wv[h] << (6 - 4 * k)) : (wv[h] >> (4 * k - 6));
+              bw[k] = static_cast<int>((sh & 0x03c003c0u) | one16);
+            }
+          }
+          const v8h bop = __builtin_bit_cast(v8h, bw);
+          cval[2 * grp + h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cval[2 * grp + h], 0, 0, 0);
+        }
+      }
+    }
+    compiler_fence();
+  }
+
+  // ---------------- per-wave results -> LDS, merge the 4 waves
+  __syncthreads();
+  float *mrg = reinterpret_cast<float *>(smem + Gm::qa_lds_bytes);    // [wave][G][D]
+  float *mrg_ml = mrg + kWaves * G * D;                               // [wave][G][2]
+  float *mrg_corr = mrg_ml + kWaves * G * 2;                          // [wave][G * kGroups]
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const float l = row_sum16(l_part[r]);
+    const int g = 4 * r + q;
+    if (g < G && n16 == 0) {
+      mrg_ml[(wave * G + g) * 2 + 0] = m_ref[r];
+      mrg_ml[(wave * G + g) * 2 + 1] = l;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const float c = row_sum16(corr[k]);
+    const int pair = q + 4 * k;
+    if (n16 == 0 && pair < G * kGroups) mrg_corr[wave * G * kGroups + pair] = c;
+  }
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int g = 2 * q + e;
+    if (g < G) {
+#pragma unroll
+      for (int grp = 0; grp < kGroups; ++grp) {
+        const float cg = mrg_corr[wave * G * kGroups + g * kGroups + grp];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ch = 32 * grp + 16 * h + n16;
+          const v4f c = cval[2 * grp + h];
+          mrg[(wave * G + g) * D + ch] = kMag * (c[2 * e] + c[2 * e + 1]) + cg;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int g = i / D, j = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv)
+      if (mrg_ml[(wv * G + g) * 2 + 1] > 0.0f) M = fmaxf(M, mrg_ml[(wv * G + g) * 2]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) {
+      const float lw = mrg_ml[(wv * G + g) * 2 + 1];
+      if (lw > 0.0f) {
+        const float f = exp2f(mrg_ml[(wv * G + g) * 2] - M);
+        L = fmaf(lw, f, L);
+        O = fmaf(mrg[(wv * G + g) * D + j], f, O);
+      }
+    }
+    const int64_t ph = (head0 + g) * job.n_split + split;
+    job.part_acc[ph * D + j] = O;
+    if (j == 0) {
+      job.part_ml[ph * 2 + 0] = M;
+      job.part_ml[ph * 2 + 1] = L;
+    }
+  }
+}
+
+// waves per SIMD the register allocation aims for (12 or 8 per CU)
+__host__ __device__ constexpr int waves_per_simd(int d, int g) { return (g >= 8 || d >= 256) ? 2 : 3; }
+
+template <int D, int W, int MC, int G, int VB>
+__global__ __launch_bounds__(kThreads, waves_per_simd(D, G)) void decode_fast_kernel(DecodeJob job) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int64_t slot = blockIdx.x / job.n_split;
+  const int split = static_cast<int>(blockIdx.x % job.n_split);
+  if constexpr (W >= 2) {
+    // the pack kernel laid out the odd planes only when the codebook is odd-symmetric
+    if (job.qodd[slot]) decode_body<D, W, MC, G, VB, odd_planes(W)>(job, slot, split, smem);
+    else decode_body<D, W, MC, G, VB, all_planes(W)>(job, slot, split, smem);
+  } else {
+    decode_body<D, W, MC, G, VB, all_planes(W)>(job, slot, split, smem);
+  }
+}
+
+template <int D, int W, int MC, int G, int VB>
+hipError_t launch_fast(const DecodeJob &job, hipStream_t stream) {
+  using Gm = Geo<D, W, MC, G, VB>;
+  auto kern = decode_fast_kernel<D, W, MC, G, VB>;
+  if (Gm::smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Gm::smem);
+    if (e != hipSuccess) return e;
+  }
+  kern<<<static_cast<unsigned>(job.n_split * job.n_slots), kThreads, Gm::smem, stream>>>(job);
+  return hipGetLastError();
+}
+
+template <int D, int W, int MC, int G>
+hipError_t launch_fast_g(const DecodeJob &job, hipStream_t stream) {
+  return job.vb == 2 ? launch_fast<D, W, MC, G, 2>(job, stream) : launch_fast<D, W, MC, G, 4>(job, stream);
+}
+
+template <int D, int W, int MC>
+hipError_t launch_fast_m(const DecodeJob &job, hipStream_t stream) {
+  switch (job.g) {
+    case 1: return launch_fast_g<D, W, MC, 1>(job, stream);
+    case 2: return launch_fast_g<D, W, MC, 2>(job, stream);
+    case 4: return launch_fast_g<D, W, MC, 4>(job, stream);
+    default: return launch_fast_g<D, W, MC, 8>(job, stream);
+  }
+}
+
+}  // namespace fast
+}  // namespace aqkv
