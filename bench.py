@@ -168,14 +168,17 @@ def time_calls(path, reps: int) -> dict:
 
 
 def time_decode_cold(path, reps: int) -> float:
-    """Decode duration with the last-level cache flushed before every launch
-    (a 512 MiB write between launches), HIP events around the decode only."""
+    """Decode duration with the last-level cache (256 MB Infinity Cache) cleared
+    of the cache's bytes before every launch by reading a 1 GiB buffer: a read
+    leaves only clean lines behind, so the timed kernel pays no write-backs of
+    the flush itself.  HIP events around the decode only."""
     import torch
     stream = torch.cuda.current_stream()
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+    flush = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda:0")
+    sink = torch.empty((), dtype=torch.float32, device="cuda:0")
     ts = []
     for _ in range(reps):
-        flush.fill_(1.0)
+        torch.sum(flush, dim=0, out=sink)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)

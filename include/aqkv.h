@@ -37,26 +37,30 @@
  *   launch failure reported by the HIP runtime returns AQKV_ERR_HIP.  Nothing
  *   prints, aborts or throws across this interface.
  *
- * Cache layout (one plane per array, rows contiguous; slot s = b * H + h of
- * the K/V view; token t of slot s is row s * capacity + t; capacity is a
- * multiple of 32):
+ * Cache layout: block records.  The tokens of a slot (slot s = b * H + h of
+ * the K/V view) are grouped in blocks of 32 (capacity is a multiple of 32);
+ * block c of slot s is one contiguous record at byte
+ * (s * capacity / 32 + c) * block_bytes of the cache buffer, so a decoder
+ * streams each 32-token block with a few large contiguous reads.  A record
+ * holds seven fields one after the other, each 32 token rows of its own row
+ * format (offsets and sizes from aqkv_cache_layout):
  *   bit rows   32-bit little-endian words of 32 consecutive elements; element
  *              j = 4 i + k of a word (i in 0..7, k in 0..3) is bit 8 k + i.
  *   key_codes  w * d / 8 bytes per row: w bit rows of d bits; row p holds bit
- *              p of every coordinate's index.  (NULL allowed when w == 0.)
+ *              p of every coordinate's index.  (absent when w == 0.)
  *   key_signs  m / 8 bytes per row: one bit row, bit 1 = non-negative
  *              projection.
  *   key_norm   fp32 ||x|| per row.
- *   key_rnorm  fp32 ||r|| per row (NULL allowed when w == 0).
- *   val_codes  d * value_bits / 8 bytes per row, stored in blocks of 32 rows
- *              (tokens 32 c .. 32 c + 31 of a slot).  In a block, channel
- *              32 g + 16 h + n (group g, half h, column n) of token 4 i + r
- *              (r in 0..3, i in 0..7) is at
+ *   key_rnorm  fp32 ||r|| per row (absent when w == 0).
+ *   val_codes  d * value_bits / 8 bytes per row; the 32 rows of a record are
+ *              one code block in which channel 32 g + 16 h + n (group g, half
+ *              h, column n) of token 4 i + r (r in 0..3, i in 0..7) is at
  *                value_bits 2: word (16 g + n) * 4 + r, bits 8 h + 16 (i & 1) + 2 (i >> 1);
  *                value_bits 4: word ((16 g + n) * 4 + r) * 2 + h, bits 16 (i & 1) + 4 (i >> 1).
  *   val_scale  fp32 [d / value_group] per row.
  *   val_min    fp32 [d / value_group] per row.
- * Every plane pointer must be 16-byte aligned.
+ * The cache buffer must be 16-byte aligned (every block_bytes is a multiple
+ * of 16).
  */
 #ifndef AQKV_H
 #define AQKV_H
@@ -100,15 +104,9 @@ typedef struct {
   const float *boundaries; /* (dev) [2^w - 1] ascending fp32; required iff mse_bits > 0 */
 } aqkv_layer;
 
-/* The compressed cache planes (layout above). */
+/* The compressed cache: n_slots * capacity / 32 block records (layout above). */
 typedef struct {
-  uint8_t *key_codes;
-  uint8_t *key_signs;
-  float *key_norm;
-  float *key_rnorm;
-  uint8_t *val_codes;
-  float *val_scale;
-  float *val_min;
+  uint8_t *blocks;   /* (dev) the records, 16-byte aligned */
   int64_t n_slots;   /* batch * kv heads */
   int64_t capacity;  /* token rows per slot, a multiple of 32 */
 } aqkv_cache;
@@ -124,20 +122,28 @@ typedef struct {
   int64_t batch_stride, head_stride, token_stride;
 } aqkv_kv_view;
 
-/* Bytes per token row of each cache plane for a configuration. */
+/* One 64-bit number per cache field. */
 typedef struct {
   int64_t key_codes, key_signs, key_norm, key_rnorm, val_codes, val_scale, val_min;
-} aqkv_row_bytes;
+} aqkv_fields;
+
+/* Block-record geometry for a configuration. */
+typedef struct {
+  aqkv_fields row_bytes;  /* bytes per token row of each field (0 = absent) */
+  aqkv_fields offset;     /* byte offset of each field inside a record */
+  int64_t block_bytes;    /* bytes of one 32-token record = 32 * sum(row_bytes) */
+} aqkv_layout;
 
 /* ---------------------------------------------------------------- host only */
 
 /* Human-readable name of a status code (static string). */
 const char *aqkv_status_string(aqkv_status status);
 
-/* Checks a configuration and reports the per-row byte sizes of every plane
- * (out may be NULL to only validate).  AQKV_ERR_SHAPE for unsupported
- * head_dim / mse_bits / sketch_dim / value_bits / value_group. */
-aqkv_status aqkv_cache_layout(const aqkv_config *cfg, aqkv_row_bytes *out);
+/* Checks a configuration and reports the block-record geometry (out may be
+ * NULL to only validate).  AQKV_ERR_SHAPE for unsupported head_dim /
+ * mse_bits / sketch_dim / value_bits / value_group.  A cache of n_slots x
+ * capacity tokens takes n_slots * capacity / 32 * block_bytes bytes. */
+aqkv_status aqkv_cache_layout(const aqkv_config *cfg, aqkv_layout *out);
 
 /* Lloyd-Max codebook for one coordinate of a uniformly random unit vector in
  * R^head_dim (TurboQuant §二: the rotated coordinates share one scaled-Beta

@@ -42,9 +42,7 @@ class LayerParams(C.Structure):
 
 
 class CacheDesc(C.Structure):
-    _fields_ = [("key_codes", C.c_void_p), ("key_signs", C.c_void_p), ("key_norm", C.c_void_p),
-                ("key_rnorm", C.c_void_p), ("val_codes", C.c_void_p), ("val_scale", C.c_void_p),
-                ("val_min", C.c_void_p), ("n_slots", C.c_int64), ("capacity", C.c_int64)]
+    _fields_ = [("blocks", C.c_void_p), ("n_slots", C.c_int64), ("capacity", C.c_int64)]
 
 
 class KvView(C.Structure):
@@ -53,16 +51,22 @@ class KvView(C.Structure):
                 ("token_stride", C.c_int64)]
 
 
-class RowBytes(C.Structure):
-    _fields_ = [("key_codes", C.c_int64), ("key_signs", C.c_int64), ("key_norm", C.c_int64),
-                ("key_rnorm", C.c_int64), ("val_codes", C.c_int64), ("val_scale", C.c_int64),
-                ("val_min", C.c_int64)]
+FIELDS = ("key_codes", "key_signs", "key_norm", "key_rnorm", "val_codes", "val_scale", "val_min")
+FLOAT_FIELDS = ("key_norm", "key_rnorm", "val_scale", "val_min")
+
+
+class Fields(C.Structure):
+    _fields_ = [(name, C.c_int64) for name in FIELDS]
+
+
+class LayoutDesc(C.Structure):
+    _fields_ = [("row_bytes", Fields), ("offset", Fields), ("block_bytes", C.c_int64)]
 
 
 _P = C.POINTER
 _SIGS = {
     "aqkv_status_string": (C.c_char_p, [C.c_int]),
-    "aqkv_cache_layout": (C.c_int, [_P(Config), _P(RowBytes)]),
+    "aqkv_cache_layout": (C.c_int, [_P(Config), _P(LayoutDesc)]),
     "aqkv_build_codebook": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "aqkv_build_rotation": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p]),
     "aqkv_quantize_keys_workspace_bytes": (C.c_size_t, [_P(Config)]),
@@ -134,9 +138,13 @@ def config(head_dim: int, mse_bits: int, sketch_dim: int, value_bits: int = 2, v
 
 
 def cache_layout(cfg: Config) -> dict:
-    rb = RowBytes()
-    _check(lib().aqkv_cache_layout(C.byref(cfg), C.byref(rb)), "aqkv_cache_layout")
-    return {name: getattr(rb, name) for name, _ in RowBytes._fields_}
+    """{"row": bytes per token of each field, "offset": byte offset of each field
+    in a 32-token block record, "block_bytes": bytes of one record}."""
+    lo = LayoutDesc()
+    _check(lib().aqkv_cache_layout(C.byref(cfg), C.byref(lo)), "aqkv_cache_layout")
+    return {"row": {n: getattr(lo.row_bytes, n) for n in FIELDS},
+            "offset": {n: getattr(lo.offset, n) for n in FIELDS},
+            "block_bytes": lo.block_bytes}
 
 
 def build_codebook(head_dim: int, bits: int):
@@ -180,39 +188,58 @@ class Layer:
 
 @dataclass
 class Cache:
-    """The seven cache planes as uint8 / float32 torch tensors."""
+    """The cache buffer: n_slots * capacity / 32 block records of block_bytes
+    bytes (a uint8 torch tensor [records, block_bytes]); field views and row
+    copies for tests and tools."""
     cfg: Config
     n_slots: int
     capacity: int
-    key_codes: object
-    key_signs: object
-    key_norm: object
-    key_rnorm: object
-    val_codes: object
-    val_scale: object
-    val_min: object
+    blocks: object
+    layout: dict
 
     @staticmethod
     def allocate(cfg: Config, n_slots: int, capacity: int, device="cuda") -> "Cache":
-        """Planes for n_slots x capacity tokens (capacity rounded up to a multiple of 32)."""
+        """Records for n_slots x capacity tokens (capacity rounded up to a multiple of 32)."""
         import torch
-        rb = cache_layout(cfg)
+        lo = cache_layout(cfg)
         capacity = (capacity + 31) // 32 * 32
-        rows = n_slots * capacity
+        blocks = torch.empty((n_slots * capacity // 32, lo["block_bytes"]), dtype=torch.uint8, device=device)
+        return Cache(cfg, n_slots, capacity, blocks, lo)
 
-        def u8(nb):
-            return torch.empty((rows, max(nb, 0)), dtype=torch.uint8, device=device) if nb > 0 else None
+    def field(self, name: str):
+        """Strided view [records, 32, row] of one field (uint8, or float32 for the norms,
+        scales and minima); None when the configuration has no such field."""
+        rb, off, bb = self.layout["row"][name], self.layout["offset"][name], self.layout["block_bytes"]
+        if rb == 0:
+            return None
+        n_rec = self.blocks.shape[0]
+        if name in FLOAT_FIELDS:
+            f = self.blocks.view(-1).view(dtype=__import__("torch").float32)
+            return f.as_strided((n_rec, 32, rb // 4), (bb // 4, rb // 4, 1), off // 4)
+        return self.blocks.view(-1).as_strided((n_rec, 32, rb), (bb, rb, 1), off)
 
-        def f32(nb):
-            return torch.empty((rows, nb // 4), dtype=torch.float32, device=device) if nb > 0 else None
+    def rows(self, name: str, row0: int, n: int):
+        """Copy of cache rows row0 .. row0 + n - 1 (row = slot * capacity + token) of a field:
+        [n, row] (uint8 or float32), [n] for the single-float norms."""
+        f = self.field(name)
+        if f is None:
+            return None
+        out = f.flatten(0, 1)[row0:row0 + n].clone()
+        return out.reshape(-1) if out.shape[-1] == 1 else out
 
-        return Cache(cfg, n_slots, capacity, u8(rb["key_codes"]), u8(rb["key_signs"]),
-                     f32(rb["key_norm"]).view(-1), (f32(rb["key_rnorm"]).view(-1) if rb["key_rnorm"] else None),
-                     u8(rb["val_codes"]), f32(rb["val_scale"]), f32(rb["val_min"]))
+    def set_rows(self, name: str, row0: int, values):
+        """Write values [n, row] (or [n] for single-float fields) into cache rows row0 .. row0 + n - 1."""
+        f = self.field(name)
+        n = values.shape[0]
+        r = row0
+        while r < row0 + n:
+            rec, i = divmod(r, 32)
+            k = min(32 - i, row0 + n - r)
+            f[rec, i:i + k] = values[r - row0:r - row0 + k].reshape(k, -1)
+            r += k
 
     def desc(self) -> CacheDesc:
-        return CacheDesc(_ptr(self.key_codes), _ptr(self.key_signs), _ptr(self.key_norm), _ptr(self.key_rnorm),
-                         _ptr(self.val_codes), _ptr(self.val_scale), _ptr(self.val_min), self.n_slots, self.capacity)
+        return CacheDesc(_ptr(self.blocks), self.n_slots, self.capacity)
 
 
 def kv_view(t) -> KvView:

@@ -41,7 +41,7 @@ aqkv_status check_view(const aqkv_kv_view *v, int d) {
 aqkv_status check_cache_shape(const aqkv_cache *c) {
   if (!c) return AQKV_ERR_NULL;
   if (c->n_slots < 0 || c->capacity < 0) return AQKV_ERR_SHAPE;
-  if (c->capacity % 32) return AQKV_ERR_SHAPE;   // value codes live in 32-token blocks
+  if (c->capacity % kBlockRows) return AQKV_ERR_SHAPE;   // whole 32-token block records
   return AQKV_OK;
 }
 
@@ -49,6 +49,16 @@ aqkv_status check_plane(const void *p) {
   if (!p) return AQKV_ERR_NULL;
   if (!aligned(p, 16)) return AQKV_ERR_ALIGN;
   return AQKV_OK;
+}
+
+aqkv_status check_blocks(const aqkv_cache *c) {
+  if (!c->blocks) return AQKV_ERR_NULL;
+  if (!aligned(c->blocks, 16)) return AQKV_ERR_ALIGN;
+  return AQKV_OK;
+}
+
+BlockLayout layout_of(const aqkv_config *cfg) {
+  return block_layout(cfg->head_dim, cfg->mse_bits, cfg->sketch_dim, cfg->value_bits);
 }
 
 aqkv_status hip_status(hipError_t e) { return e == hipSuccess ? AQKV_OK : AQKV_ERR_HIP; }
@@ -105,18 +115,27 @@ const char *aqkv_status_string(aqkv_status s) {
   return "unknown status";
 }
 
-aqkv_status aqkv_cache_layout(const aqkv_config *cfg, aqkv_row_bytes *out) {
+aqkv_status aqkv_cache_layout(const aqkv_config *cfg, aqkv_layout *out) {
   aqkv_status st = check_config(cfg);
   if (st != AQKV_OK) return st;
   if (out) {
-    const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
-    out->key_codes = static_cast<int64_t>(w) * d / 8;
-    out->key_signs = m / 8;
-    out->key_norm = 4;
-    out->key_rnorm = w > 0 ? 4 : 0;
-    out->val_codes = static_cast<int64_t>(d) * cfg->value_bits / 8;
-    out->val_scale = 4 * (d / cfg->value_group);
-    out->val_min = 4 * (d / cfg->value_group);
+    const BlockLayout L = layout_of(cfg);
+    aqkv_fields *rb = &out->row_bytes, *of = &out->offset;
+    rb->key_codes = L.row[F_CODES];
+    rb->key_signs = L.row[F_SIGNS];
+    rb->key_norm = L.row[F_NORM];
+    rb->key_rnorm = L.row[F_RNORM];
+    rb->val_codes = L.row[F_VCODES];
+    rb->val_scale = L.row[F_VSCALE];
+    rb->val_min = L.row[F_VMIN];
+    of->key_codes = L.off[F_CODES];
+    of->key_signs = L.off[F_SIGNS];
+    of->key_norm = L.off[F_NORM];
+    of->key_rnorm = L.off[F_RNORM];
+    of->val_codes = L.off[F_VCODES];
+    of->val_scale = L.off[F_VSCALE];
+    of->val_min = L.off[F_VMIN];
+    out->block_bytes = L.rec;
   }
   return AQKV_OK;
 }
@@ -153,12 +172,7 @@ aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, 
     if ((st = check_plane(layer->rotation)) != AQKV_OK) return st;
     if (!layer->centroids || !layer->boundaries) return AQKV_ERR_NULL;
   }
-  if ((st = check_plane(cache->key_signs)) != AQKV_OK) return st;
-  if ((st = check_plane(cache->key_norm)) != AQKV_OK) return st;
-  if (w > 0) {
-    if ((st = check_plane(cache->key_codes)) != AQKV_OK) return st;
-    if ((st = check_plane(cache->key_rnorm)) != AQKV_OK) return st;
-  }
+  if ((st = check_blocks(cache)) != AQKV_OK) return st;
   const size_t need = key_workspace_bytes(d, w, m);
   if (!workspace || workspace_bytes < need) return AQKV_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return AQKV_ERR_ALIGN;
@@ -185,10 +199,12 @@ aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, 
   job.ops = ops;
   job.centroids = layer->centroids;
   job.boundaries = layer->boundaries;
-  job.codes = cache->key_codes;
-  job.signs = cache->key_signs;
-  job.norm = cache->key_norm;
-  job.rnorm = cache->key_rnorm;
+  const BlockLayout L = layout_of(cfg);
+  job.codes = cache->blocks + L.off[F_CODES];
+  job.signs = cache->blocks + L.off[F_SIGNS];
+  job.norm = cache->blocks + L.off[F_NORM];
+  job.rnorm = cache->blocks + L.off[F_RNORM];
+  job.rec = L.rec;
   return hip_status(launch_quantize_keys_mfma(job, s));
 }
 
@@ -202,9 +218,7 @@ aqkv_status aqkv_quantize_values(const aqkv_config *cfg, const aqkv_kv_view *v, 
   if (v->batch * v->heads != cache->n_slots) return AQKV_ERR_SHAPE;
   if (token_offset < 0) return AQKV_ERR_SHAPE;
   if (token_offset + v->tokens > cache->capacity) return AQKV_ERR_CAPACITY;
-  if ((st = check_plane(cache->val_codes)) != AQKV_OK) return st;
-  if ((st = check_plane(cache->val_scale)) != AQKV_OK) return st;
-  if ((st = check_plane(cache->val_min)) != AQKV_OK) return st;
+  if ((st = check_blocks(cache)) != AQKV_OK) return st;
   if (v->tokens == 0 || cache->n_slots == 0) return AQKV_OK;
   ValueJob job{};
   job.v = v->data;
@@ -220,9 +234,11 @@ aqkv_status aqkv_quantize_values(const aqkv_config *cfg, const aqkv_kv_view *v, 
   job.d = d;
   job.vb = cfg->value_bits;
   job.group = cfg->value_group;
-  job.codes = cache->val_codes;
-  job.scale = cache->val_scale;
-  job.vmin = cache->val_min;
+  const BlockLayout L = layout_of(cfg);
+  job.codes = cache->blocks + L.off[F_VCODES];
+  job.scale = cache->blocks + L.off[F_VSCALE];
+  job.vmin = cache->blocks + L.off[F_VMIN];
+  job.rec = L.rec;
   return hip_status(launch_quantize_values(job, static_cast<hipStream_t>(stream)));
 }
 
@@ -278,17 +294,7 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   if (!aligned(out, 16) || !aligned(q_sketch, 16) || (q_rot && !aligned(q_rot, 16)) ||
       (scores && !aligned(scores, 16)))
     return AQKV_ERR_ALIGN;
-  if (context_len > 0) {
-    if ((st = check_plane(cache->key_signs)) != AQKV_OK) return st;
-    if ((st = check_plane(cache->key_norm)) != AQKV_OK) return st;
-    if (w > 0) {
-      if ((st = check_plane(cache->key_codes)) != AQKV_OK) return st;
-      if ((st = check_plane(cache->key_rnorm)) != AQKV_OK) return st;
-    }
-    if ((st = check_plane(cache->val_codes)) != AQKV_OK) return st;
-    if ((st = check_plane(cache->val_scale)) != AQKV_OK) return st;
-    if ((st = check_plane(cache->val_min)) != AQKV_OK) return st;
-  }
+  if (context_len > 0 && (st = check_blocks(cache)) != AQKV_OK) return st;
   const DecodePlan plan = decode_plan(d, w, m, cfg->value_bits, cache->n_slots, g, context_len);
   if (!workspace || workspace_bytes < plan.total_bytes) return AQKV_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return AQKV_ERR_ALIGN;
@@ -306,13 +312,16 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   job.n_split = plan.n_split;
   job.split_tokens = plan.split_tokens;
   job.centroids = layer->centroids;
-  job.codes = cache->key_codes;
-  job.signs = cache->key_signs;
-  job.norm = cache->key_norm;
-  job.rnorm = cache->key_rnorm;
-  job.vcodes = cache->val_codes;
-  job.vscale = cache->val_scale;
-  job.vmin = cache->val_min;
+  const BlockLayout L = layout_of(cfg);
+  job.blocks = cache->blocks;
+  job.rec = L.rec;
+  job.codes = cache->blocks + L.off[F_CODES];
+  job.signs = cache->blocks + L.off[F_SIGNS];
+  job.norm = cache->blocks + L.off[F_NORM];
+  job.rnorm = cache->blocks + L.off[F_RNORM];
+  job.vcodes = cache->blocks + L.off[F_VCODES];
+  job.vscale = cache->blocks + L.off[F_VSCALE];
+  job.vmin = cache->blocks + L.off[F_VMIN];
   job.q_rot = q_rot;
   job.q_sketch = q_sketch;
   job.softmax_scale = softmax_scale;
@@ -326,10 +335,8 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   job.qodd = reinterpret_cast<int *>(ws + plan.acc_bytes + plan.ml_bytes + plan.pack_bytes + plan.const_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (plan.mfma) {
-    // the matrix-core decoder addresses a slot's rows of a plane with 32-bit byte offsets
-    const int64_t row_max = std::max<int64_t>({int64_t(w) * d / 8, int64_t(m) / 8, int64_t(d) * cfg->value_bits / 8,
-                                               int64_t(d) / 32 * 4});
-    if (cache->capacity * row_max >= (int64_t(1) << 31)) return AQKV_ERR_UNSUPPORTED;
+    // the matrix-core decoder addresses a slot's records with 32-bit byte offsets
+    if (cache->capacity / kBlockRows * L.rec >= (int64_t(1) << 31)) return AQKV_ERR_UNSUPPORTED;
     return hip_status(launch_decode_mfma(job, s));
   }
   return hip_status(launch_decode(job, s));

@@ -76,10 +76,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
     // blocks: a block's words hold codes of all its tokens); past the end -> 0
     const bool block_valid = c0 + (tid & ~31) < t_end;
     for (int i = 0; i < vwords; ++i)
-      vcw[tid * vwords + i] = block_valid ? reinterpret_cast<const uint32_t *>(job.vcodes + row * (D * vb / 8))[i] : 0u;
+      vcw[tid * vwords + i] = block_valid ? reinterpret_cast<const uint32_t *>(job.vcodes + rec_row(row, D * vb / 8, job.rec))[i] : 0u;
     for (int i = 0; i < kGroups; ++i) {
-      vsc[tid * kGroups + i] = valid ? job.vscale[row * kGroups + i] : 0.0f;
-      vmn[tid * kGroups + i] = valid ? job.vmin[row * kGroups + i] : 0.0f;
+      vsc[tid * kGroups + i] = valid ? reinterpret_cast<const float *>(job.vscale + rec_row(row, 4 * kGroups, job.rec))[i] : 0.0f;
+      vmn[tid * kGroups + i] = valid ? reinterpret_cast<const float *>(job.vmin + rec_row(row, 4 * kGroups, job.rec))[i] : 0.0f;
     }
 
     // A. scores
@@ -87,13 +87,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
 #pragma unroll
     for (int g = 0; g < G; ++g) s_acc[g] = 0.0f;
     if (valid) {
-      const float n = job.norm[row];
-      const float gamma = W > 0 ? job.rnorm[row] : n;
+      const float n = *reinterpret_cast<const float *>(job.norm + rec_row(row, 4, job.rec));
+      const float gamma = W > 0 ? *reinterpret_cast<const float *>(job.rnorm + rec_row(row, 4, job.rec)) : n;
       float mse[G], qjl[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) { mse[g] = 0.0f; qjl[g] = 0.0f; }
       if constexpr (W > 0) {
-        const uint32_t *cw = reinterpret_cast<const uint32_t *>(job.codes + row * code_bytes);
+        const uint32_t *cw = reinterpret_cast<const uint32_t *>(job.codes + rec_row(row, code_bytes, job.rec));
         for (int wi = 0; wi < D / 32; ++wi) {
           uint32_t pl[W];
 #pragma unroll
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
           }
         }
       }
-      const uint32_t *sw = reinterpret_cast<const uint32_t *>(job.signs + row * sign_bytes);
+      const uint32_t *sw = reinterpret_cast<const uint32_t *>(job.signs + rec_row(row, sign_bytes, job.rec));
       for (int wi = 0; wi < m / 32; ++wi) {
         const uint32_t bits = sw[wi];
 #pragma unroll

@@ -29,9 +29,10 @@
 // Work: block (slot, split) of 4 waves; each wave walks 32-token tiles of the
 // block's range (interleaved across waves) with its own online-softmax state.
 // Every shape parameter is a template constant, so a tile is straight-line
-// code.  Every plane of a tile goes HBM -> LDS with buffer_load_dwordx4 ... lds
-// (per-slot buffer resources, wave-uniform tile offsets) into a per-wave ring
-// of three tile buffers, so two tiles stream in while one is computed.  The
+// code.  A tile is one 32-token block record of the cache (all seven fields
+// contiguous); it goes HBM -> LDS with buffer_load_dwordx4 ... lds (per-slot
+// buffer resource, wave-uniform record offset) into a per-wave ring of three
+// tile buffers, so two tiles stream in while one is computed.  The
 // waves merge in LDS; combine_kernel merges the splits.
 #pragma once
 
@@ -110,9 +111,9 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// Buffer resource over the rows of one cache plane of one slot (raw, untyped
-// loads; records = bytes, reads past them return 0).  Offsets are 32-bit, so a
-// slot's rows of a plane must span fewer than 2^31 bytes (the host checks this).
+// Buffer resource over the block records of one slot (raw, untyped loads;
+// num_records = bytes, reads past them return 0).  Offsets are 32-bit, so a
+// slot's records must span fewer than 2^31 bytes (the host checks this).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
@@ -189,9 +190,7 @@ struct Geo {
   static_assert(tile_bytes == tile_bytes_of(D, W, MC, VB), "tile geometry");
   static constexpr int wave_lds = wave_lds_of(D, W, MC, G, VB);
   // load instructions per tile (each wave waits on whole tiles)
-  static constexpr int loads_per_tile = (W > 0 ? loads_of<kTT * CB>() + loads_of<kTT * 4>() : 0) +
-                                        loads_of<kTT * SB>() + loads_of<kTT * 4>() + loads_of<kTT * VBY>() +
-                                        2 * loads_of<kTT * kGroups * 4>();
+  static constexpr int loads_per_tile = loads_of<tile_bytes>();
   static constexpr int nc_all = chunks_max(D, W, 64 * MC);
   static constexpr bool reg_a_all = RB * nc_all * 4 <= kRegAVgprs;
   static constexpr int qa_lds_bytes = reg_a_all ? 0 : RB * nc_all * 1024;
@@ -264,27 +263,15 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
 #pragma unroll
   for (int i = 0; i < kPairs; ++i) corr[i] = 0.0f;
 
-  // ---- per-slot plane resources (byte offsets relative to row slot * capacity)
+  // ---- the slot's block records: one contiguous record per 32-token tile
   const int64_t n_tiles = (t_end > t_begin) ? (t_end - t_begin + kTT - 1) / kTT : 0;
-  const int64_t r0 = slot * job.capacity;
-  const uint32_t cap = static_cast<uint32_t>(job.capacity);
-  const __amdgpu_buffer_rsrc_t rs_codes = plane_rsrc(W > 0 ? job.codes + r0 * CB : job.signs, cap * (W > 0 ? CB : 1));
-  const __amdgpu_buffer_rsrc_t rs_signs = plane_rsrc(job.signs + r0 * SB, cap * SB);
-  const __amdgpu_buffer_rsrc_t rs_norm = plane_rsrc(job.norm + r0, cap * 4);
-  const __amdgpu_buffer_rsrc_t rs_rnorm = plane_rsrc(W > 0 ? job.rnorm + r0 : job.norm + r0, cap * 4);
-  const __amdgpu_buffer_rsrc_t rs_vcodes = plane_rsrc(job.vcodes + r0 * VBY, cap * VBY);
-  const __amdgpu_buffer_rsrc_t rs_vscale = plane_rsrc(job.vscale + r0 * kGroups, cap * kGroups * 4);
-  const __amdgpu_buffer_rsrc_t rs_vmin = plane_rsrc(job.vmin + r0 * kGroups, cap * kGroups * 4);
+  const int64_t recs = job.capacity / kTT;
+  const __amdgpu_buffer_rsrc_t rs_blocks =
+      plane_rsrc(job.blocks + slot * recs * Gm::tile_bytes, static_cast<uint32_t>(recs * Gm::tile_bytes));
   auto issue = [&](int64_t tile) {
-    const uint32_t t = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t_begin + tile * kTT));
+    const uint32_t rec = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t_begin / kTT + tile));
     uint8_t *b = wbase + static_cast<int>((tile / kWaves) % kRing) * Gm::tile_bytes;
-    if constexpr (W > 0) copy_region<kTT * CB>(rs_codes, t * CB, b, lane);
-    copy_region<kTT * SB>(rs_signs, t * SB, b + Gm::o_signs, lane);
-    copy_region<kTT * 4>(rs_norm, t * 4, b + Gm::o_norm, lane);
-    if constexpr (W > 0) copy_region<kTT * 4>(rs_rnorm, t * 4, b + Gm::o_rnorm, lane);
-    copy_region<kTT * VBY>(rs_vcodes, t * VBY, b + Gm::o_vcodes, lane);
-    copy_region<kTT * kGroups * 4>(rs_vscale, t * kGroups * 4, b + Gm::o_vscale, lane);
-    copy_region<kTT * kGroups * 4>(rs_vmin, t * kGroups * 4, b + Gm::o_vmin, lane);
+    copy_region<Gm::tile_bytes>(rs_blocks, rec * Gm::tile_bytes, b, lane);
   };
 
   // weight tokens: K-slot 8 q' + i of the value product is token 4 i + q'; lane

@@ -11,6 +11,39 @@ namespace aqkv {
 
 constexpr int kMaxSketch = 1024;
 constexpr int kMaxQPerKv = 16;
+constexpr int kBlockRows = 32;   // token rows per cache block record
+
+// Block-record geometry (include/aqkv.h): fields in record order, bytes per
+// row and offsets; rec = bytes of one 32-row record.
+enum Field { F_CODES = 0, F_SIGNS, F_NORM, F_RNORM, F_VCODES, F_VSCALE, F_VMIN, F_COUNT };
+struct BlockLayout {
+  int64_t row[F_COUNT];
+  int64_t off[F_COUNT];
+  int64_t rec;
+};
+inline BlockLayout block_layout(int d, int w, int m, int vb) {
+  BlockLayout L{};
+  L.row[F_CODES] = static_cast<int64_t>(w) * d / 8;
+  L.row[F_SIGNS] = m / 8;
+  L.row[F_NORM] = 4;
+  L.row[F_RNORM] = w > 0 ? 4 : 0;
+  L.row[F_VCODES] = static_cast<int64_t>(d) * vb / 8;
+  L.row[F_VSCALE] = 4 * (d / 32);
+  L.row[F_VMIN] = 4 * (d / 32);
+  int64_t o = 0;
+  for (int f = 0; f < F_COUNT; ++f) {
+    L.off[f] = o;
+    o += kBlockRows * L.row[f];
+  }
+  L.rec = o;
+  return L;
+}
+
+// Byte offset, from a field's place in record 0, of cache row `row` (= slot *
+// capacity + t, capacity a multiple of 32) of a field with rb bytes per row.
+__host__ __device__ inline int64_t rec_row(int64_t row, int64_t rb, int64_t rec) {
+  return (row >> 5) * rec + (row & 31) * rb;
+}
 
 // Everything a key-quantise launch needs, already validated.
 struct KeyJob {
@@ -22,8 +55,9 @@ struct KeyJob {
   int d, w, m;
   const uint8_t *ops;     // matrix-core operands of Pi and S Pi^T (or S), see quant_keys_mfma.hip
   const float *centroids, *boundaries;
-  uint8_t *codes, *signs;
-  float *norm, *rnorm;
+  // cache fields, each at its place in record 0; row r at + rec_row(r, row bytes, rec)
+  uint8_t *codes, *signs, *norm, *rnorm;
+  int64_t rec;
 };
 
 struct ValueJob {
@@ -33,8 +67,9 @@ struct ValueJob {
   int64_t batch_stride, head_stride, token_stride;
   int64_t n_slots, n_tokens, token_offset, capacity;
   int d, vb, group;
-  uint8_t *codes;
-  float *scale, *vmin;
+  // cache fields, each at its place in record 0; row r at + rec_row(r, row bytes, rec)
+  uint8_t *codes, *scale, *vmin;
+  int64_t rec;
 };
 
 struct QueryJob {
@@ -53,10 +88,10 @@ struct DecodeJob {
   int n_split;
   int64_t split_tokens;  // tokens per split (multiple of the chunk)
   const float *centroids;
-  const uint8_t *codes, *signs;
-  const float *norm, *rnorm;
-  const uint8_t *vcodes;
-  const float *vscale, *vmin;
+  // cache: the slots' records (blocks) and each field at its place in record 0
+  const uint8_t *blocks;
+  int64_t rec;
+  const uint8_t *codes, *signs, *norm, *rnorm, *vcodes, *vscale, *vmin;
   const float *q_rot, *q_sketch;
   float softmax_scale;
   float *scores;         // nullable [n_slots*g][context]

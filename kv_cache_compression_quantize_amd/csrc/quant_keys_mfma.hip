@@ -481,7 +481,7 @@ __device__ __forceinline__ void sketch_slab(const KeyJob &job, const SlabOps<D> 
   if (full && sub == 7) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      if (L.valid[nt]) reinterpret_cast<uint32_t *>(job.signs + L.row[nt] * srow_bytes)[4 * (tz >> 3) + g] = sw[nt];
+      if (L.valid[nt]) reinterpret_cast<uint32_t *>(job.signs + rec_row(L.row[nt], srow_bytes, job.rec))[4 * (tz >> 3) + g] = sw[nt];
       sw[nt] = 0u;
     }
   } else if (!full && sub == 3) {
@@ -490,7 +490,7 @@ __device__ __forceinline__ void sketch_slab(const KeyJob &job, const SlabOps<D> 
       uint32_t v = sw[nt] << (16 * (g & 1));
       v |= __shfl_xor(v, 16);
       if (L.valid[nt] && (g & 1) == 0)
-        reinterpret_cast<uint32_t *>(job.signs + L.row[nt] * srow_bytes)[4 * FM + (g >> 1)] = v;
+        reinterpret_cast<uint32_t *>(job.signs + rec_row(L.row[nt], srow_bytes, job.rec))[4 * FM + (g >> 1)] = v;
       sw[nt] = 0u;
     }
   }
@@ -504,7 +504,7 @@ __device__ __forceinline__ void store_codes_norms(const KeyJob &job, const TileL
   for (int nt = 0; nt < Geo<D>::NT; ++nt) {
     if (!L.valid[nt]) continue;
     if constexpr (W > 0) {
-      uint8_t *crow = job.codes + L.row[nt] * (W * D / 8);
+      uint8_t *crow = job.codes + rec_row(L.row[nt], W * D / 8, job.rec);
 #pragma unroll
       for (int p = 0; p < W; ++p) {
         uint32_t *plane = reinterpret_cast<uint32_t *>(crow + p * (D / 8));
@@ -515,8 +515,8 @@ __device__ __forceinline__ void store_codes_norms(const KeyJob &job, const TileL
       }
     }
     if (g == 0) {
-      job.norm[L.row[nt]] = nrm[nt];
-      if constexpr (W > 0) job.rnorm[L.row[nt]] = gam[nt];
+      *reinterpret_cast<float *>(job.norm + rec_row(L.row[nt], 4, job.rec)) = nrm[nt];
+      if constexpr (W > 0) *reinterpret_cast<float *>(job.rnorm + rec_row(L.row[nt], 4, job.rec)) = gam[nt];
     }
   }
 }
@@ -583,7 +583,7 @@ __device__ __forceinline__ void store_signs(const KeyJob &job, const v4f (&z)[TM
         v |= __shfl_xor(v, 16);
       }
       if (L.valid[nt] && (cnt == 8 || (g & 1) == 0))
-        reinterpret_cast<uint32_t *>(job.signs + L.row[nt] * srow_bytes)[cnt == 8 ? 4 * wl + g : 4 * FM + (g >> 1)] = v;
+        reinterpret_cast<uint32_t *>(job.signs + rec_row(L.row[nt], srow_bytes, job.rec))[cnt == 8 ? 4 * wl + g : 4 * FM + (g >> 1)] = v;
     }
   }
 }

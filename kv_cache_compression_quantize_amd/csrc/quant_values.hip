@@ -3,9 +3,9 @@
 // "Value 分组量化 2 bit/维, min-max", and §七, kv_cache.py "value group
 // quantisation and bit packing").
 //
-// Codes are stored in blocks of 32 tokens so that a decoder reads, for one
-// channel, the codes of 8 tokens of the block from one 32-bit word (the
-// layout is described in include/aqkv.h).  One block of 256 threads owns one
+// Codes are stored in blocks of 32 tokens (the val_codes field of a cache
+// block record) so that a decoder reads, for one channel, the codes of 8
+// tokens of the block from one 32-bit word (layout in include/aqkv.h).  One block of 256 threads owns one
 // 32-token cache block of one slot:
 //   1. one thread per (token, group): 32 elements loaded with 16-byte loads,
 //      min / max, scale = (max - min) / (2^vb - 1) and the codes in IEEE fp32
@@ -85,14 +85,15 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueJob job, int6
       cds[tt][g * kGroup + i] = static_cast<uint8_t>(code);
     }
     const int64_t row = s * job.capacity + ct;
-    job.scale[row * kGroups + g] = scale;
-    job.vmin[row * kGroups + g] = mn;
+    reinterpret_cast<float *>(job.scale + rec_row(row, kGroups * 4, job.rec))[g] = scale;
+    reinterpret_cast<float *>(job.vmin + rec_row(row, kGroups * 4, job.rec))[g] = mn;
   }
   __syncthreads();
 
   // 2. block words
   constexpr int kWords = kBlockTokens * D * VB / 32;
-  uint32_t *dst = reinterpret_cast<uint32_t *>(job.codes + (s * job.capacity + ct0) * (D * VB / 8));
+  // the code block of these 32 tokens: the val_codes field of one record
+  uint32_t *dst = reinterpret_cast<uint32_t *>(job.codes + rec_row(s * job.capacity + ct0, D * VB / 8, job.rec));
   const bool full = lo == ct0 && hi == ct0 + kBlockTokens;
   for (int wi = tid; wi < kWords; wi += 256) {
     // word -> (group g, column n, token residue r) and the channel half(s) it holds

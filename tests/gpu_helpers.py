@@ -76,14 +76,14 @@ def cfg_of(hl: HostLayer, vb: int = 2):
 
 
 def read_planes(cache: aqkv.Cache, slot: int, t0: int, t1: int) -> dict:
-    """Host copies of rows [t0, t1) of one slot."""
+    """Host copies of rows [t0, t1) of one slot, field by field."""
     r0, r1 = slot * cache.capacity + t0, slot * cache.capacity + t1
-    g = lambda t: None if t is None else t[r0:r1].cpu().numpy()
+    g = lambda name: None if cache.field(name) is None else cache.rows(name, r0, r1 - r0).cpu().numpy()
     # value codes live in 32-token blocks: whole blocks covering [t0, t1) (only when t0 % 32 == 0)
     b1 = slot * cache.capacity + (t1 + 31) // 32 * 32
-    vcodes = cache.val_codes[r0:b1].cpu().numpy() if t0 % 32 == 0 else None
-    return dict(codes=g(cache.key_codes), signs=g(cache.key_signs), norm=g(cache.key_norm),
-                rnorm=g(cache.key_rnorm), vcodes=vcodes, vscale=g(cache.val_scale), vmin=g(cache.val_min))
+    vcodes = cache.rows("val_codes", r0, b1 - r0).cpu().numpy() if t0 % 32 == 0 else None
+    return dict(codes=g("key_codes"), signs=g("key_signs"), norm=g("key_norm"), rnorm=g("key_rnorm"),
+                vcodes=vcodes, vscale=g("val_scale"), vmin=g("val_min"))
 
 
 def oracle_rows(hl: HostLayer, k: np.ndarray, v: np.ndarray, vb: int = 2):

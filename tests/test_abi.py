@@ -37,13 +37,22 @@ def test_status_strings():
 
 
 def test_cache_layout_and_bad_configs():
-    rb = aqkv.cache_layout(aqkv.config(128, 2, 128))
+    lo = aqkv.cache_layout(aqkv.config(128, 2, 128))
+    rb = lo["row"]
     assert rb == dict(key_codes=32, key_signs=16, key_norm=4, key_rnorm=4, val_codes=32, val_scale=16, val_min=16)
-    assert sum(rb.values()) == 120
-    rb = aqkv.cache_layout(aqkv.config(256, 3, 256))
-    assert sum(rb.values()) == 96 + 32 + 8 + 64 + 64 == 264
-    rb = aqkv.cache_layout(aqkv.config(128, 0, 192))
+    assert sum(rb.values()) == 120 and lo["block_bytes"] == 32 * 120
+    # a record holds the seven fields one after the other, 32 rows each
+    off = 0
+    for name in aqkv.FIELDS:
+        assert lo["offset"][name] == off
+        off += 32 * rb[name]
+    assert off == lo["block_bytes"]
+    lo = aqkv.cache_layout(aqkv.config(256, 3, 256))
+    assert sum(lo["row"].values()) == 96 + 32 + 8 + 64 + 64 == 264
+    lo = aqkv.cache_layout(aqkv.config(128, 0, 192))
+    rb = lo["row"]
     assert rb["key_codes"] == 0 and rb["key_rnorm"] == 0 and rb["key_signs"] == 24
+    assert lo["block_bytes"] % 16 == 0
     for bad in [(96, 2, 128), (128, 4, 128), (128, 2, 100), (128, 2, 2048), (128, -1, 128)]:
         with pytest.raises(aqkv.AqkvError) as e:
             aqkv.cache_layout(aqkv.config(*bad))
@@ -68,9 +77,8 @@ def test_workspace_sizes():
 FAKE = 0x10000  # never dereferenced: every call below fails validation first
 
 
-def _cache(n_slots=2, cap=64, misalign=0):
-    p = FAKE + misalign
-    return aqkv.CacheDesc(p, p, p, p, p, p, p, n_slots, cap)
+def _cache(n_slots=2, cap=64, misalign=0, blocks=FAKE):
+    return aqkv.CacheDesc(None if blocks is None else blocks + misalign, n_slots, cap)
 
 
 def _view(tokens=8, dtype=aqkv.BF16, data=FAKE, stride=128):
@@ -100,6 +108,8 @@ def test_quantize_keys_validation_codes():
     assert call(off=60) == -4
     assert call(off=-1) == -2
     assert call(cache=_cache(misalign=8)) == -3
+    assert call(cache=_cache(blocks=None)) == -1
+    assert call(cache=_cache(cap=48)) == -2          # capacity must be whole 32-token records
     assert call(wsb=16) == -5
     assert call(wsp=None) == -5
     assert call(layer=aqkv.LayerParams(FAKE, None, FAKE, FAKE)) == -1

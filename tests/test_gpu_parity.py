@@ -131,8 +131,7 @@ def test_chunked_append_matches_one_call():
     kd, vd = to_device_kv(k, "bf16"), to_device_kv(v, "bf16")
     def zeroed(cache):
         # rows past T (capacity is rounded up to 32) must compare equal too
-        for name in ("key_codes", "key_signs", "key_norm", "key_rnorm", "val_codes", "val_scale", "val_min"):
-            getattr(cache, name).zero_()
+        cache.blocks.zero_()
         return cache
 
     one = zeroed(aqkv.Cache.allocate(cfg, B * H, T))
@@ -143,8 +142,10 @@ def test_chunked_append_matches_one_call():
         aqkv.quantize_keys(cfg, layer, kd[:, :, a:e], parts, token_offset=a)
         aqkv.quantize_values(cfg, vd[:, :, a:e], parts, token_offset=a)
     torch.cuda.synchronize()
-    for name in ("key_codes", "key_signs", "key_norm", "key_rnorm", "val_codes", "val_scale", "val_min"):
-        assert torch.equal(getattr(one, name), getattr(parts, name)), name
+    for name in aqkv.FIELDS:
+        a, b = one.field(name), parts.field(name)
+        assert (a is None and b is None) or torch.equal(a, b), name
+    assert torch.equal(one.blocks, parts.blocks)
 
 
 @pytest.mark.parametrize("d,w,m,qdtype", [(128, 2, 128, "fp32"), (128, 0, 512, "bf16"), (256, 3, 256, "fp32")])
@@ -172,10 +173,7 @@ def _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity):
     torch, dev = torch_dev()
     n_slots = len(ks)
     cache = aqkv.Cache.allocate(cfg, n_slots, capacity)
-    for name in ("key_codes", "key_signs", "key_norm", "key_rnorm", "val_codes", "val_scale", "val_min"):
-        t = getattr(cache, name)
-        if t is not None:
-            t.zero_()
+    cache.blocks.zero_()
     refs = []
     for s in range(n_slots):
         qk, kr, vt, vpacked = oracle_rows(hl, ks[s], vs[s], vb)
@@ -183,13 +181,13 @@ def _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity):
         r0 = s * cache.capacity          # allocate() rounds the capacity up to 32
         codes, signs, norm, rnorm = kr
         if hl.w > 0:
-            cache.key_codes[r0:r0 + T] = torch.from_numpy(codes).to(dev)
-            cache.key_rnorm[r0:r0 + T] = torch.from_numpy(rnorm).to(dev)
-        cache.key_signs[r0:r0 + T] = torch.from_numpy(signs).to(dev)
-        cache.key_norm[r0:r0 + T] = torch.from_numpy(norm).to(dev)
-        cache.val_codes[r0:r0 + vpacked.shape[0]] = torch.from_numpy(vpacked).to(dev)
-        cache.val_scale[r0:r0 + T] = torch.from_numpy(vt[1]).to(dev)
-        cache.val_min[r0:r0 + T] = torch.from_numpy(vt[2]).to(dev)
+            cache.set_rows("key_codes", r0, torch.from_numpy(codes).to(dev))
+            cache.set_rows("key_rnorm", r0, torch.from_numpy(rnorm).to(dev))
+        cache.set_rows("key_signs", r0, torch.from_numpy(signs).to(dev))
+        cache.set_rows("key_norm", r0, torch.from_numpy(norm).to(dev))
+        cache.set_rows("val_codes", r0, torch.from_numpy(vpacked).to(dev))
+        cache.set_rows("val_scale", r0, torch.from_numpy(vt[1]).to(dev))
+        cache.set_rows("val_min", r0, torch.from_numpy(vt[2]).to(dev))
         # the oracle consumes exactly what was stored (fp32 norms)
         refs.append(((qk.idx, qk.bits, norm.astype(np.float64), rnorm.astype(np.float64)), vt))
     return cache, refs
