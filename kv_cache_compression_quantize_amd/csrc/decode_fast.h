@@ -19,12 +19,14 @@
 // accumulation; a key bit becomes an int8 {0,1} operand byte with one shift
 // and one mask per 4 bits (bit rows are byte-transposed for this).
 //
-// Values: out[g] = sum_t p_t (code_t scale_t + min_t).  The f16 operand
-// 1 + code/4 (2-bit codes; 1 + code/16 for 4-bit) is exact and is built with
-// one shift and one and-or from the 32-token block word that holds 8 tokens'
-// codes of one channel; the token weights a_t = p_t scale_t are split into f16
-// hi + lo rows and v_mfma_f32_16x16x32_f16 accumulates sum_t a_t (1 + code_t/4)
-// over 32 tokens; sum_t p_t (min_t - 4 scale_t) is added at the end.
+// Values: out[g] = sum_t p_t (code_t scale_t + min_t).  The f16 operand is the
+// code itself in the low mantissa bits with a zero exponent, i.e. the exact
+// denormal code * 2^-24 (the matrix cores keep f16 denormals), cut from the
+// 32-token block word that holds 8 tokens' codes of one channel with one shift
+// and one mask per two codes; the token weights a_t = p_t scale_t are split
+// into f16 hi + lo rows and v_mfma_f32_16x16x32_f16 accumulates
+// sum_t a_t code_t 2^-24 over 32 tokens; the result is scaled by 2^24 and
+// sum_t p_t min_t is added at the end.
 //
 // Work: block (slot, split) of 4 waves; each wave walks 32-token tiles of the
 // block's range (interleaved across waves) with its own online-softmax state.
@@ -149,16 +151,18 @@ struct HeadConst {
 __host__ __device__ constexpr int pairs_of(int g, int d) { return (g * (d / 32) + 3) / 4; }
 
 // Tile staging: every cache plane of 32 tokens, copied whole into a per-wave
-// ring of kRing buffers (tiles t+1 .. t+kRing-1 stream in while t is computed).
-constexpr int kRing = 3;
+// ring of kRing buffers (tiles t+1 .. t+kRing-1 stream in while t is computed;
+// two buffers and more resident waves beat deeper prefetch with fewer waves).
+constexpr int kRing = 2;
 __host__ __device__ constexpr int tile_bytes_of(int d, int w, int mc, int vb) {
   return kTT * (w * d / 8 + mc * 8 + 4 + (w > 0 ? 4 : 0) + d * vb / 8 + 8 * (d / 32));
 }
 // LDS bytes per block of decode_fast_kernel<D, W, m / 64, G, VB> (host and device):
-// per wave the tile ring, the softmax weights P [32 tokens][G] and the value-weight
-// operand [groups][4][2G rows][16 B]; at the end the 4-wave merge
+// per wave the tile ring and the value-weight operand [groups][4][2G rows][16 B],
+// whose first bytes also hold the softmax weights P [32 tokens][G] until they are
+// read; at the end the 4-wave merge
 __host__ __device__ constexpr int wave_lds_of(int d, int w, int mc, int g, int vb) {
-  return kRing * tile_bytes_of(d, w, mc, vb) + kTT * g * 4 + (d / 32) * 4 * 2 * g * 16;
+  return kRing * tile_bytes_of(d, w, mc, vb) + (d / 32) * 4 * 2 * g * 16;
 }
 __host__ __device__ constexpr int smem_of(int d, int w, int mc, int g, int vb) {
   const int waves = kWaves * wave_lds_of(d, w, mc, g, vb);
@@ -206,8 +210,6 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   constexpr int NC = NP * HC + MC;
   constexpr int NCmax = Gm::NCmax;
   constexpr bool kRegA = RB * NC * 4 <= kRegAVgprs;
-  constexpr float kMag = VB == 2 ? 4.0f : 16.0f;
-  constexpr uint32_t one16 = 0x3c003c00u;   // f16 pair {1, 1}
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform in an SGPR: tile offsets and LDS bases derive from it
@@ -249,8 +251,8 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   const float kappa_qjl = 1.2533141373155003f / static_cast<float>(64 * MC);   // sqrt(pi/2) / m
   const float lscale = job.softmax_scale * kLog2e;
 
-  float *P = reinterpret_cast<float *>(wbase + kRing * Gm::tile_bytes);             // [kTT][G]
-  uint8_t *aval = wbase + kRing * Gm::tile_bytes + kTT * G * 4;                     // [grp][q][2G][16 B]
+  uint8_t *aval = wbase + kRing * Gm::tile_bytes;                                   // [grp][q][2G][16 B]
+  float *P = reinterpret_cast<float *>(aval);   // [kTT][G], read out before aval is written
 
   // ---- per-wave state
   float m_ref[RB], l_part[RB];
@@ -283,10 +285,14 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   for (int k = 0; k < kRing - 1; ++k)
     if (tile + k * kWaves < n_tiles) issue(tile + k * kWaves);
   for (; tile < n_tiles; tile += kWaves) {
-    // wait for this tile: the later tiles already issued may stay in flight
-    static_assert(kRing == 3, "wait ladder below assumes two tiles in flight");
-    if (tile + kWaves < n_tiles) wait_vm<Gm::loads_per_tile>();
-    else wait_vm<0>();
+    // wait for this tile: the (up to kRing - 2) later tiles already issued may stay in flight
+    static_assert(kRing >= 2 && kRing <= 4, "wait ladder");
+    {
+      const int64_t after = (n_tiles - 1 - tile) / kWaves;
+      if (kRing >= 4 && after >= 2) wait_vm<(kRing >= 4 ? 2 : 0) * Gm::loads_per_tile>();
+      else if (kRing >= 3 && after >= 1) wait_vm<(kRing >= 3 ? 1 : 0) * Gm::loads_per_tile>();
+      else wait_vm<0>();
+    }
     compiler_fence();
     if (tile + (kRing - 1) * kWaves < n_tiles) issue(tile + (kRing - 1) * kWaves);
     const uint8_t *tb = wbase + static_cast<int>((tile / kWaves) % kRing) * Gm::tile_bytes;
@@ -453,7 +459,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
     }
     compiler_fence();
 
-    // ---------------- value weights a = p * scale (f16 hi + lo), correction sums
+    // ---------------- value weights a = p * scale (f16 hi + lo), correction sums p * min
     {
       const int qd = n16 & 3, i0 = 2 * (n16 >> 2);
       const float *vs = reinterpret_cast<const float *>(tb + Gm::o_vscale);
@@ -464,6 +470,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
         pa[g] = P[ta * G + g];
         pb[g] = P[tb4 * G + g];
       }
+      compiler_fence();   // P shares its bytes with the operand written below
 #pragma unroll
       for (int k = 0; k < kPairs; ++k) {
         const int pair = q + 4 * k;
@@ -475,18 +482,15 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
           // whatever their cache rows hold
           float aa = fmul_legacy(pa[g], sa);
           float ab = fmul_legacy(pb[g], sb);
-          // pin the fp32 weights so both uses of the f16 high part round the same value
+          // pin the fp32 weights so both uses of the f16 high part see the same value
           asm volatile("" : "+v"(aa), "+v"(ab));
-          corr[k] += fmul_legacy(pa[g], fmaf(-kMag, sa, ma));
-          corr[k] += fmul_legacy(pb[g], fmaf(-kMag, sb, mb));
-          const _Float16 ha = static_cast<_Float16>(aa), hb = static_cast<_Float16>(ab);
-          const _Float16 la = static_cast<_Float16>(aa - static_cast<float>(ha));
-          const _Float16 lb = static_cast<_Float16>(ab - static_cast<float>(hb));
+          corr[k] += fmul_legacy(pa[g], ma) + fmul_legacy(pb[g], mb);
+          // hi = the weights rounded toward zero to f16, lo = f16 of the exact fp32 remainders
+          const auto hi = __builtin_amdgcn_cvt_pkrtz(aa, ab);
+          const auto lo = __builtin_amdgcn_cvt_pkrtz(aa - static_cast<float>(hi[0]), ab - static_cast<float>(hi[1]));
           uint8_t *dst = aval + ((grp * 4 + qd) * (2 * G) + 2 * g) * 16 + 2 * i0;
-          *reinterpret_cast<uint32_t *>(dst) =
-              static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ha)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hb)) << 16);
-          *reinterpret_cast<uint32_t *>(dst + 16) =
-              static_cast<uint32_t>(__builtin_bit_cast(uint16_t, la)) | (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lb)) << 16);
+          *reinterpret_cast<uint32_t *>(dst) = __builtin_bit_cast(uint32_t, hi);
+          *reinterpret_cast<uint32_t *>(dst + 16) = __builtin_bit_cast(uint32_t, lo);
         }
       }
     }
@@ -497,11 +501,12 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
       const uint8_t *vc = tb + Gm::o_vcodes;
 #pragma unroll
       for (int grp = 0; grp < kGroups; ++grp) {
-        // rows >= 2G of the weight operand are zero
-        v8h aop = v8h{0, 0, 0, 0, 0, 0, 0, 0};
-        if (G == 8 || n16 < 2 * G) aop = *reinterpret_cast<const v8h *>(aval + ((grp * 4 + q) * (2 * G) + n16) * 16);
+        // rows >= 2G of the weight operand repeat rows < 2G; their outputs are never read
+        const v8h aop = *reinterpret_cast<const v8h *>(aval + ((grp * 4 + q) * (2 * G) + (n16 & (2 * G - 1))) * 16);
         // block word(s) of column n16: tokens 4 i + q of channels 32 grp + 16 h + n16;
-        // operand dword k = K-slots (8q + 2k, 8q + 2k + 1) = i (2k, 2k + 1)
+        // operand dword k = K-slots (8q + 2k, 8q + 2k + 1) = i (2k, 2k + 1).  The
+        // code itself, masked into the low mantissa bits of an f16 with a zero
+        // exponent, is the exact denormal code * 2^-24.
         uint32_t wv[2];
         if constexpr (VB == 2) {
           wv[0] = reinterpret_cast<const uint32_t *>(vc)[(16 * grp + n16) * 4 + q];
@@ -514,19 +519,13 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
         for (int h = 0; h < 2; ++h) {
           v4i bw;
           if constexpr (VB == 2) {
-            // h = 0: code of i = 2k at bits 2k, of 2k+1 at 16 + 2k; h = 1: 8 bits higher
+            // code of i = 2k at bits 8h + 2k, of 2k+1 at 16 + 8h + 2k
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t sh = h == 0 ? (wv[0] << (8 - 2 * k)) : (wv[0] >> (2 * k));
-              bw[k] = static_cast<int>((sh & 0x03000300u) | one16);
-            }
+            for (int k = 0; k < 4; ++k) bw[k] = static_cast<int>((wv[0] >> (8 * h + 2 * k)) & 0x00030003u);
           } else {
-            // code of i = 2k at bits 4k, of 2k+1 at 16 + 4k -> mantissa bits 6..9
+            // code of i = 2k at bits 4k, of 2k+1 at 16 + 4k
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const uint32_t sh = k < 2 ? (wv[h] << (6 - 4 * k)) : (wv[h] >> (4 * k - 6));
-              bw[k] = static_cast<int>((sh & 0x03c003c0u) | one16);
-            }
+            for (int k = 0; k < 4; ++k) bw[k] = static_cast<int>((wv[h] >> (4 * k)) & 0x000f000fu);
           }
           const v8h bop = __builtin_bit_cast(v8h, bw);
           cval[2 * grp + h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, cval[2 * grp + h], 0, 0, 0);
@@ -569,7 +568,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
         for (int h = 0; h < 2; ++h) {
           const int ch = 32 * grp + 16 * h + n16;
           const v4f c = cval[2 * grp + h];
-          mrg[(wave * G + g) * D + ch] = kMag * (c[2 * e] + c[2 * e + 1]) + cg;
+          mrg[(wave * G + g) * D + ch] = 16777216.0f * (c[2 * e] + c[2 * e + 1]) + cg;   // 2^24 undoes the denormal scale
         }
       }
     }
@@ -600,8 +599,8 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   }
 }
 
-// waves per SIMD the register allocation aims for (12 or 8 per CU)
-__host__ __device__ constexpr int waves_per_simd(int d, int g) { return (g >= 8 || d >= 256) ? 2 : 3; }
+// waves per SIMD the register allocation aims for (16 or 8 per CU)
+__host__ __device__ constexpr int waves_per_simd(int d, int g) { return (g >= 8 || d >= 256) ? 2 : 4; }
 
 template <int D, int W, int MC, int G, int VB>
 __global__ __launch_bounds__(kThreads, waves_per_simd(D, G)) void decode_fast_kernel(DecodeJob job) {
