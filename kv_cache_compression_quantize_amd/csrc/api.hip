@@ -89,10 +89,7 @@ DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int6
   const size_t heads = static_cast<size_t>(n_slots) * g;
   p.acc_bytes = round_up(heads * p.n_split * d * sizeof(float), 256);
   p.ml_bytes = round_up(heads * p.n_split * 2 * sizeof(float), 256);
-  p.pack_bytes = p.mfma ? round_up(decode_mfma_pack_bytes(d, w, g, m, n_slots), 256) : 0;
-  p.const_bytes = p.mfma ? round_up(heads * 4 * sizeof(float), 256) : 0;
-  p.odd_bytes = p.mfma ? round_up(static_cast<size_t>(n_slots) * sizeof(int), 256) : 0;
-  p.total_bytes = p.acc_bytes + p.ml_bytes + p.pack_bytes + p.const_bytes + p.odd_bytes;
+  p.total_bytes = p.acc_bytes + p.ml_bytes;
   return p;
 }
 
@@ -330,9 +327,6 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   job.part_acc = static_cast<float *>(workspace);
   char *ws = static_cast<char *>(workspace);
   job.part_ml = reinterpret_cast<float *>(ws + plan.acc_bytes);
-  job.qpack = reinterpret_cast<uint8_t *>(ws + plan.acc_bytes + plan.ml_bytes);
-  job.qconst = reinterpret_cast<float *>(ws + plan.acc_bytes + plan.ml_bytes + plan.pack_bytes);
-  job.qodd = reinterpret_cast<int *>(ws + plan.acc_bytes + plan.ml_bytes + plan.pack_bytes + plan.const_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (plan.mfma) {
     // the matrix-core decoder addresses a slot's records with 32-bit byte offsets

@@ -225,45 +225,54 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
 
 // Merge the split partials of one query head: M = max_i m_i, weights
 // w_i = 2^(m_i - M) (0 for empty splits), out = sum_i w_i acc_i / sum_i w_i l_i.
-// The weights are computed once per split into LDS (splits <= 1024 in one pass,
-// more in a loop), then each thread sums its channels over the splits.
+// The weights go to LDS (1024 splits per pass); 256 / d threads share a channel,
+// each summing every (256 / d)-th split with independent loads in flight.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeJob job) {
   __shared__ float wts[1024];
   __shared__ float red[256];
   const int64_t head = blockIdx.x;
   const int d = job.d, ns = job.n_split, tid = threadIdx.x;
   const float *ml = job.part_ml + head * ns * 2;
+  const float *acc = job.part_acc + head * ns * d;
+  // M over the non-empty splits
   float mx = -INFINITY;
   for (int i = tid; i < ns; i += 256)
     if (ml[2 * i + 1] > 0.0f) mx = fmaxf(mx, ml[2 * i]);
-  red[tid] = mx;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) red[tid] = fmaxf(red[tid], red[tid + s]);
-    __syncthreads();
-  }
-  mx = red[0];
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
-  float o[2] = {0.0f, 0.0f};
-  float lsum = 0.0f;
+  const int P = 256 / d;                  // threads per channel
+  const int j = tid % d, p = tid / d;
+  float o = 0.0f, lsum = 0.0f;
   for (int c0 = 0; c0 < ns; c0 += 1024) {
     const int cn = min(1024, ns - c0);
     for (int i = tid; i < cn; i += 256) {
       const float l = ml[2 * (c0 + i) + 1];
-      wts[i] = l > 0.0f ? exp2f(ml[2 * (c0 + i)] - mx) : 0.0f;
+      const float w = l > 0.0f ? exp2f(ml[2 * (c0 + i)] - mx) : 0.0f;
+      wts[i] = w;
+      lsum = fmaf(l, w, lsum);
     }
     __syncthreads();
-    for (int i = 0; i < cn; ++i) lsum = fmaf(ml[2 * (c0 + i) + 1], wts[i], lsum);
-    for (int r = 0; r < 2; ++r) {
-      const int j = tid + 256 * r;
-      if (j < d)
-        for (int i = 0; i < cn; ++i) o[r] = fmaf(job.part_acc[(head * ns + c0 + i) * d + j], wts[i], o[r]);
-    }
+#pragma unroll 8
+    for (int i = p; i < cn; i += P) o = fmaf(acc[static_cast<int64_t>(c0 + i) * d + j], wts[i], o);
     __syncthreads();
   }
-  for (int r = 0; r < 2; ++r) {
-    const int j = tid + 256 * r;
-    if (j < d) job.out[head * d + j] = lsum > 0.0f ? o[r] / lsum : 0.0f;
+  // sum of the l weights over the block, partial outputs over the P threads of a channel
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
+  red[tid] = o;
+  __syncthreads();
+  __shared__ float lred[4];
+  if ((tid & 63) == 0) lred[tid >> 6] = lsum;
+  __syncthreads();
+  if (p == 0) {
+    float t = 0.0f;
+    for (int k = 0; k < P; ++k) t += red[k * d + j];
+    const float L = lred[0] + lred[1] + lred[2] + lred[3];
+    job.out[head * d + j] = L > 0.0f ? t / L : 0.0f;
   }
 }
 

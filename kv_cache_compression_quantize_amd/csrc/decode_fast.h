@@ -11,9 +11,9 @@
 //   <q_rot, c[idx_t]>    = c[0] sum(q_rot) + sum_A kappa_A <q_rot, par_A(t)>
 //   <q_sk, 2 bits_t - 1> = 2 <q_sk, bits_t> - sum(q_sk)
 // and every score is a fixed combination of dot products between query rows
-// and {0,1} bit-planes of the cached keys.  decode_pack_kernel quantises the
-// query side (kappa_A q_rot, 2 q_sk) once per call to 15-bit integers split
-// into int8 hi / lo parts, laid out as ready-made matrix-core A operands.
+// and {0,1} bit-planes of the cached keys.  Each block first quantises the
+// query side of its heads (kappa_A q_rot, 2 q_sk) to 15-bit integers split into
+// int8 hi / lo parts, laid out as ready-made matrix-core A operands.
 // v_mfma_i32_16x16x64_i8 then contracts 64 coordinates of 16 tokens for 16
 // rows = 4 heads x {mse hi, mse lo, qjl hi, qjl lo} with exact integer
 // accumulation; a key bit becomes an int8 {0,1} operand byte with one shift
@@ -201,8 +201,96 @@ struct Geo {
   static constexpr int smem = smem_of(D, W, MC, G, VB);
 };
 
+// Query side of the slot's G heads, built by the whole block once (the
+// TurboQuant article's "rotate and sketch the query once" step, here also
+// integerised): per head the scales sig = max |value| / 16383 and the constant
+// terms c[0] sum(q_rot), -sum(q_sk) go to hc; every A-operand value v = round
+// (value / sig) (kappa_A q_rot for the code planes in PL, 2 q_sk for the sign
+// chunks) is split into int8 parts hi = v >> 7, lo = v & 127 and written to
+// `ops`, lane-major: byte i of lane (row, q) of chunk c in row block r sits at
+// ((r * NC + c) * 64 + lane) * 16 + i and is K-slot 16 q + i; row = 4 (g % 4) + t
+// with t = mse hi, mse lo, qjl hi, qjl lo and g = 4 r + row / 4.  K-slot 16 q + i of
+// chunk h of a plane is coordinate (D/4) q + 16 h + i; of sign chunk h, sketch row
+// 16 MC q + 16 h + i.
+template <int D, int W, int MC, int G, int PL>
+__device__ __forceinline__ void pack_query(const DecodeJob &job, int64_t head0, const float *kappa, uint8_t *ops,
+                                           HeadConst *hc) {
+  constexpr int RB = heads_rb(G), HC = D / 64, NP = popc(PL), NC = NP * HC + MC, m = 64 * MC;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float km = 0.0f;
+#pragma unroll
+  for (int a = 1; a < (1 << W); ++a)
+    if ((PL >> a) & 1) km = fmaxf(km, fabsf(kappa[a - 1]));
+  for (int g = wave; g < G; g += kWaves) {
+    float mx = 0.0f, sr = 0.0f, mq = 0.0f, sq = 0.0f;
+    if constexpr (W > 0)
+      for (int j = lane; j < D; j += 64) {
+        const float v = job.q_rot[(head0 + g) * D + j];
+        sr += v;
+        mx = fmaxf(mx, km * fabsf(v));
+      }
+    for (int i = lane; i < m; i += 64) {
+      const float v = job.q_sketch[(head0 + g) * m + i];
+      sq += v;
+      mq = fmaxf(mq, fabsf(2.0f * v));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+      mq = fmaxf(mq, __shfl_xor(mq, off));
+      sr += __shfl_xor(sr, off);
+      sq += __shfl_xor(sq, off);
+    }
+    if (lane == 0)
+      hc[g] = HeadConst{mx > 0.0f ? mx / 16383.0f : 1.0f, mq > 0.0f ? mq / 16383.0f : 1.0f,
+                        W > 0 ? job.centroids[0] * sr : 0.0f, -sq};
+  }
+  __syncthreads();
+  for (int e4 = tid; e4 < RB * NC * 256; e4 += kThreads) {
+    const int rc = e4 / 256, rem = e4 % 256;
+    const int r = rc / NC, c = rc % NC;
+    const int l = rem / 4, i0 = (rem % 4) * 4;
+    const int row = l % 16, q = l / 16;
+    const int g = 4 * r + row / 4, t = row % 4;
+    uint32_t word = 0;
+    if (g < G) {
+      const float *src = nullptr;
+      float scl = 0.0f;
+      if (c < NP * HC) {
+        if (t < 2) {
+          // the (c / HC)-th plane of PL, coordinates (D/4) q + 16 h .. + 15
+          int a = 1, n = 0;
+#pragma unroll
+          for (int b = 1; b < (1 << W); ++b)
+            if ((PL >> b) & 1) {
+              if (n == c / HC) a = b;
+              ++n;
+            }
+          src = job.q_rot + (head0 + g) * D + (D / 4) * q + 16 * (c % HC) + i0;
+          scl = kappa[a - 1] / hc[g].sig_mse;
+        }
+      } else if (t >= 2) {
+        src = job.q_sketch + (head0 + g) * m + 16 * MC * q + 16 * (c - NP * HC) + i0;
+        scl = 2.0f / hc[g].sig_qjl;
+      }
+      if (src) {
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          int v = static_cast<int>(rintf(src[bb] * scl));
+          v = max(-16383, min(16383, v));
+          const int part = (t & 1) ? (v & 127) : (v >> 7);
+          word |= (static_cast<uint32_t>(part) & 0xffu) << (8 * bb);
+        }
+      }
+    }
+    reinterpret_cast<uint32_t *>(ops)[e4] = word;
+  }
+  __syncthreads();
+}
+
 template <int D, int W, int MC, int G, int VB, int PL>
-__device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, int split, uint8_t *smem) {
+__device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, int split, uint8_t *smem,
+                                            const float *kappa) {
   using Gm = Geo<D, W, MC, G, VB>;
   constexpr int RB = Gm::RB, HC = Gm::HC, kGroups = Gm::kGroups, CB = Gm::CB, SB = Gm::SB, VBY = Gm::VBY;
   constexpr int kWpl = Gm::kWpl, kSw = Gm::kSw, kPairs = Gm::kPairs;
@@ -219,23 +307,20 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   const int64_t t_end = min<int64_t>(job.context, t_begin + job.split_tokens);
   const int64_t head0 = slot * G;
 
-  // ---- query operands and per-head constants from the pack kernel
-  const uint8_t *qp = job.qpack + slot * static_cast<int64_t>(RB * NCmax * 1024);
+  // ---- query operands and per-head constants, built by this block
+  __shared__ HeadConst s_hc[G];
   uint8_t *qa_lds = smem;
   uint8_t *wbase = smem + Gm::qa_lds_bytes + wave * Gm::wave_lds;
+  // register-resident operands are staged in the (not yet used) tile rings
+  uint8_t *ops = kRegA ? smem + Gm::qa_lds_bytes : qa_lds;
+  static_assert(!kRegA || RB * NC * 1024 <= kWaves * Gm::wave_lds, "operand staging space");
+  pack_query<D, W, MC, G, PL>(job, head0, kappa, ops, s_hc);
   v4i aq[kRegA ? RB : 1][kRegA ? NC : 1];
   if constexpr (kRegA) {
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) aq[r][c] = *reinterpret_cast<const v4i *>(qp + ((r * NCmax + c) * 64 + lane) * 16);
-  } else {
-    for (int i = tid; i < RB * NC * 64; i += kThreads) {
-      const int rc = i / 64, l = i % 64;
-      const int r = rc / NC, c = rc % NC;
-      reinterpret_cast<v4i *>(qa_lds)[i] = *reinterpret_cast<const v4i *>(qp + ((r * NCmax + c) * 64 + l) * 16);
-    }
-    __syncthreads();
+      for (int c = 0; c < NC; ++c) aq[r][c] = *reinterpret_cast<const v4i *>(ops + ((r * NC + c) * 64 + lane) * 16);
   }
   auto A = [&](int r, int c) -> v4i {
     if constexpr (kRegA) return aq[r][c];
@@ -245,9 +330,9 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const int g = 4 * r + q;
-    if (g < G) hc[r] = reinterpret_cast<const HeadConst *>(job.qconst)[head0 + g];
-    else hc[r] = HeadConst{0.0f, 0.0f, 0.0f, 0.0f};
+    hc[r] = g < G ? s_hc[g] : HeadConst{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  __syncthreads();   // staging space is free again before the first tile lands in it
   const float kappa_qjl = 1.2533141373155003f / static_cast<float>(64 * MC);   // sqrt(pi/2) / m
   const float lscale = job.softmax_scale * kLog2e;
 
@@ -597,6 +682,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
       job.part_ml[ph * 2 + 1] = L;
     }
   }
+
 }
 
 // waves per SIMD the register allocation aims for (16 or 8 per CU)
@@ -605,14 +691,42 @@ __host__ __device__ constexpr int waves_per_simd(int d, int g) { return (g >= 8 
 template <int D, int W, int MC, int G, int VB>
 __global__ __launch_bounds__(kThreads, waves_per_simd(D, G)) void decode_fast_kernel(DecodeJob job) {
   extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float s_cen[8], s_kappa[8];
   const int64_t slot = blockIdx.x / job.n_split;
   const int split = static_cast<int>(blockIdx.x % job.n_split);
+  const int tid = threadIdx.x;
+  constexpr int L = 1 << W;
+  if constexpr (W > 0) {
+    // kappa_A (thread A) = -2 (-1)^|A| 2^-w sum_idx c[idx] prod_{k in A} (2 bit_k(idx) - 1),
+    // summed over complementary index pairs so odd-symmetric codebooks give exact zeros
+    if (tid < L) s_cen[tid] = job.centroids[tid];
+    __syncthreads();
+    if (tid >= 1 && tid < L) {
+      double acc = 0.0;
+      for (int i = 0; i < L / 2; ++i) {
+        const int j = L - 1 - i;
+        double si = 1.0, sj = 1.0;
+        for (int k = 0; k < W; ++k)
+          if ((tid >> k) & 1) {
+            si *= ((i >> k) & 1) ? 1.0 : -1.0;
+            sj *= ((j >> k) & 1) ? 1.0 : -1.0;
+          }
+        acc += static_cast<double>(s_cen[i]) * si + static_cast<double>(s_cen[j]) * sj;
+      }
+      s_kappa[tid - 1] = static_cast<float>(-2.0 * ((__popc(tid) & 1) ? -1.0 : 1.0) * acc / L);
+    }
+    __syncthreads();
+  }
   if constexpr (W >= 2) {
-    // the pack kernel laid out the odd planes only when the codebook is odd-symmetric
-    if (job.qodd[slot]) decode_body<D, W, MC, G, VB, odd_planes(W)>(job, slot, split, smem);
-    else decode_body<D, W, MC, G, VB, all_planes(W)>(job, slot, split, smem);
+    // only the odd-size planes when every even-size coefficient vanishes (odd-symmetric codebook)
+    bool odd = true;
+#pragma unroll
+    for (int a = 1; a < L; ++a)
+      if (!(popc(a) & 1) && s_kappa[a - 1] != 0.0f) odd = false;
+    if (odd) decode_body<D, W, MC, G, VB, odd_planes(W)>(job, slot, split, smem, s_kappa);
+    else decode_body<D, W, MC, G, VB, all_planes(W)>(job, slot, split, smem, s_kappa);
   } else {
-    decode_body<D, W, MC, G, VB, all_planes(W)>(job, slot, split, smem);
+    decode_body<D, W, MC, G, VB, all_planes(W)>(job, slot, split, smem, s_kappa);
   }
 }
 

@@ -98,10 +98,6 @@ struct DecodeJob {
   float *out;            // [n_slots*g][d]
   float *part_acc;       // [n_slots*g][n_split][d]
   float *part_ml;        // [n_slots*g][n_split][2]
-  // matrix-core decoder only: packed query operands written by decode_pack_kernel
-  uint8_t *qpack;        // [n_slots][row blocks][chunks][64 lanes][16 B]
-  float *qconst;         // [n_slots*g][4]: integer scales and constant terms per head
-  int *qodd;             // [n_slots]: 1 when only the odd-size code planes are laid out
 };
 
 // Decode split-K plan shared by the workspace query and the launch.
@@ -109,7 +105,7 @@ struct DecodePlan {
   bool mfma;             // matrix-core kernel (else the scalar fallback)
   int n_split;
   int64_t split_tokens;
-  size_t acc_bytes, ml_bytes, pack_bytes, const_bytes, odd_bytes, total_bytes;
+  size_t acc_bytes, ml_bytes, total_bytes;
 };
 DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int64_t context);
 
@@ -124,10 +120,9 @@ hipError_t launch_prepare_query(const QueryJob &job, hipStream_t stream);
 hipError_t launch_decode(const DecodeJob &job, hipStream_t stream);
 hipError_t launch_combine(const DecodeJob &job, hipStream_t stream);
 bool decode_supported(int d, int w, int g, int m, int vb);
-// matrix-core decode (query pack + decode + combine), shapes with a compiled kernel
+// matrix-core decode (decode + split combine), shapes with a compiled kernel
 bool decode_mfma_supported(int d, int w, int g, int m, int vb);
 int decode_mfma_blocks_per_cu(int d, int w, int g, int m, int vb);
-size_t decode_mfma_pack_bytes(int d, int w, int g, int m, int64_t n_slots);
 hipError_t launch_decode_mfma(const DecodeJob &job, hipStream_t stream);
 // per head_dim kernel launchers (decode_fast_d*.hip)
 hipError_t launch_decode_fast_d64(const DecodeJob &job, hipStream_t stream);
