@@ -77,8 +77,9 @@ DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int6
   constexpr int64_t kCUs = 256;        // MI355X compute units
   DecodePlan p{};
   p.mfma = decode_mfma_supported(d, w, g, m, vb);
-  // two rounds of resident blocks for the matrix-core kernel, ~4 per CU otherwise
-  const int64_t target = p.mfma ? 2 * kCUs * decode_mfma_blocks_per_cu(d, w, g, m, vb) : 4 * kCUs;
+  // one round of resident blocks for the matrix-core kernel (each block pays its
+  // query-side prologue once), ~4 per CU otherwise
+  const int64_t target = p.mfma ? kCUs * decode_mfma_blocks_per_cu(d, w, g, m, vb) : 4 * kCUs;
   const int64_t grains = (context + kGrain - 1) / kGrain;
   int64_t split = n_slots > 0 ? (target + n_slots - 1) / n_slots : 1;
   if (split > grains) split = grains;

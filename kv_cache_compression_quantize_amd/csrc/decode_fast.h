@@ -193,6 +193,7 @@ struct Geo {
   static constexpr int tile_bytes = o_vmin + kTT * kGroups * 4;
   static_assert(tile_bytes == tile_bytes_of(D, W, MC, VB), "tile geometry");
   static constexpr int wave_lds = wave_lds_of(D, W, MC, G, VB);
+  static constexpr int aval_bytes = kGroups * 4 * 2 * G * 16;
   // load instructions per tile (each wave waits on whole tiles)
   static constexpr int loads_per_tile = loads_of<tile_bytes>();
   static constexpr int nc_all = chunks_max(D, W, 64 * MC);
@@ -307,13 +308,41 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   const int64_t t_end = min<int64_t>(job.context, t_begin + job.split_tokens);
   const int64_t head0 = slot * G;
 
+  // ---- LDS: ring slot k of wave w at ring + (k * kWaves + w) * tile_bytes, then
+  // the waves' value-weight operands
+  uint8_t *qa_lds = smem;
+  uint8_t *ring = smem + Gm::qa_lds_bytes;
+  uint8_t *aval = ring + kRing * kWaves * Gm::tile_bytes + wave * Gm::aval_bytes;   // [grp][q][2G][16 B]
+  float *P = reinterpret_cast<float *>(aval);   // [kTT][G], read out before aval is written
+  auto slot_buf = [&](int64_t tile) -> uint8_t * {
+    return ring + (static_cast<int>((tile / kWaves) % kRing) * kWaves + wave) * Gm::tile_bytes;
+  };
+
+  // ---- the slot's block records: one contiguous record per 32-token tile
+  const int64_t n_tiles = (t_end > t_begin) ? (t_end - t_begin + kTT - 1) / kTT : 0;
+  const int64_t recs = job.capacity / kTT;
+  const __amdgpu_buffer_rsrc_t rs_blocks =
+      plane_rsrc(job.blocks + slot * recs * Gm::tile_bytes, static_cast<uint32_t>(recs * Gm::tile_bytes));
+  auto issue = [&](int64_t tile) {
+    const uint32_t rec = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t_begin / kTT + tile));
+    copy_region<Gm::tile_bytes>(rs_blocks, rec * Gm::tile_bytes, slot_buf(tile), lane);
+  };
+  // register-resident operands are staged in the last ring slots, which load
+  // last, so the first tiles stream in while the query side is built (when the
+  // operands need more room they take the whole ring and the tiles wait)
+  constexpr bool kStageLast = RB * NC * 1024 <= kWaves * Gm::tile_bytes;
+  static_assert(!kRegA || RB * NC * 1024 <= kRing * kWaves * Gm::tile_bytes, "operand staging space");
+  uint8_t *ops = !kRegA ? qa_lds : kStageLast ? ring + (kRing - 1) * kWaves * Gm::tile_bytes : ring;
+  int64_t tile = wave;
+  auto issue_first = [&]() {
+#pragma unroll
+    for (int k = 0; k < kRing - 1; ++k)
+      if (tile + k * kWaves < n_tiles) issue(tile + k * kWaves);
+  };
+  if constexpr (!kRegA || kStageLast) issue_first();
+
   // ---- query operands and per-head constants, built by this block
   __shared__ HeadConst s_hc[G];
-  uint8_t *qa_lds = smem;
-  uint8_t *wbase = smem + Gm::qa_lds_bytes + wave * Gm::wave_lds;
-  // register-resident operands are staged in the (not yet used) tile rings
-  uint8_t *ops = kRegA ? smem + Gm::qa_lds_bytes : qa_lds;
-  static_assert(!kRegA || RB * NC * 1024 <= kWaves * Gm::wave_lds, "operand staging space");
   pack_query<D, W, MC, G, PL>(job, head0, kappa, ops, s_hc);
   v4i aq[kRegA ? RB : 1][kRegA ? NC : 1];
   if constexpr (kRegA) {
@@ -332,12 +361,10 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
     const int g = 4 * r + q;
     hc[r] = g < G ? s_hc[g] : HeadConst{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  __syncthreads();   // staging space is free again before the first tile lands in it
+  __syncthreads();   // staging space is free again before tiles land in it
+  if constexpr (kRegA && !kStageLast) issue_first();
   const float kappa_qjl = 1.2533141373155003f / static_cast<float>(64 * MC);   // sqrt(pi/2) / m
   const float lscale = job.softmax_scale * kLog2e;
-
-  uint8_t *aval = wbase + kRing * Gm::tile_bytes;                                   // [grp][q][2G][16 B]
-  float *P = reinterpret_cast<float *>(aval);   // [kTT][G], read out before aval is written
 
   // ---- per-wave state
   float m_ref[RB], l_part[RB];
@@ -350,25 +377,10 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
 #pragma unroll
   for (int i = 0; i < kPairs; ++i) corr[i] = 0.0f;
 
-  // ---- the slot's block records: one contiguous record per 32-token tile
-  const int64_t n_tiles = (t_end > t_begin) ? (t_end - t_begin + kTT - 1) / kTT : 0;
-  const int64_t recs = job.capacity / kTT;
-  const __amdgpu_buffer_rsrc_t rs_blocks =
-      plane_rsrc(job.blocks + slot * recs * Gm::tile_bytes, static_cast<uint32_t>(recs * Gm::tile_bytes));
-  auto issue = [&](int64_t tile) {
-    const uint32_t rec = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t_begin / kTT + tile));
-    uint8_t *b = wbase + static_cast<int>((tile / kWaves) % kRing) * Gm::tile_bytes;
-    copy_region<Gm::tile_bytes>(rs_blocks, rec * Gm::tile_bytes, b, lane);
-  };
-
   // weight tokens: K-slot 8 q' + i of the value product is token 4 i + q'; lane
   // (tp, pq) handles tokens ta = 8 (tp / 4) + tp % 4 and ta + 4
   const int ta = 8 * (n16 >> 2) + (n16 & 3), tb4 = ta + 4;
 
-  int64_t tile = wave;
-#pragma unroll
-  for (int k = 0; k < kRing - 1; ++k)
-    if (tile + k * kWaves < n_tiles) issue(tile + k * kWaves);
   for (; tile < n_tiles; tile += kWaves) {
     // wait for this tile: the (up to kRing - 2) later tiles already issued may stay in flight
     static_assert(kRing >= 2 && kRing <= 4, "wait ladder");
@@ -380,7 +392,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
     }
     compiler_fence();
     if (tile + (kRing - 1) * kWaves < n_tiles) issue(tile + (kRing - 1) * kWaves);
-    const uint8_t *tb = wbase + static_cast<int>((tile / kWaves) % kRing) * Gm::tile_bytes;
+    const uint8_t *tb = slot_buf(tile);
     const int64_t t0 = t_begin + tile * kTT;
     const int nt = static_cast<int>(min<int64_t>(kTT, t_end - t0));
 
