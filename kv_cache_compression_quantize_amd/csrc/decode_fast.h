@@ -158,11 +158,12 @@ __host__ __device__ constexpr int tile_bytes_of(int d, int w, int mc, int vb) {
   return kTT * (w * d / 8 + mc * 8 + 4 + (w > 0 ? 4 : 0) + d * vb / 8 + 8 * (d / 32));
 }
 // LDS bytes per block of decode_fast_kernel<D, W, m / 64, G, VB> (host and device):
-// per wave the tile ring and the value-weight operand [groups][4][2G rows][16 B],
+// per wave the tile ring and the value-weight operand [groups][4][2G + 1 rows][16 B],
 // whose first bytes also hold the softmax weights P [32 tokens][G] until they are
 // read; at the end the 4-wave merge
+__host__ __device__ constexpr int aval_rows_of(int g) { return 2 * g + 1; }   // + 1 row: writes spread over all banks
 __host__ __device__ constexpr int wave_lds_of(int d, int w, int mc, int g, int vb) {
-  return kRing * tile_bytes_of(d, w, mc, vb) + (d / 32) * 4 * 2 * g * 16;
+  return kRing * tile_bytes_of(d, w, mc, vb) + (d / 32) * 4 * aval_rows_of(g) * 16;
 }
 __host__ __device__ constexpr int smem_of(int d, int w, int mc, int g, int vb) {
   const int waves = kWaves * wave_lds_of(d, w, mc, g, vb);
@@ -193,7 +194,8 @@ struct Geo {
   static constexpr int tile_bytes = o_vmin + kTT * kGroups * 4;
   static_assert(tile_bytes == tile_bytes_of(D, W, MC, VB), "tile geometry");
   static constexpr int wave_lds = wave_lds_of(D, W, MC, G, VB);
-  static constexpr int aval_bytes = kGroups * 4 * 2 * G * 16;
+  static constexpr int AR = aval_rows_of(G);        // 16-byte rows per (group, lane group) block
+  static constexpr int aval_bytes = kGroups * 4 * AR * 16;
   // load instructions per tile (each wave waits on whole tiles)
   static constexpr int loads_per_tile = loads_of<tile_bytes>();
   static constexpr int nc_all = chunks_max(D, W, 64 * MC);
@@ -312,7 +314,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   // the waves' value-weight operands
   uint8_t *qa_lds = smem;
   uint8_t *ring = smem + Gm::qa_lds_bytes;
-  uint8_t *aval = ring + kRing * kWaves * Gm::tile_bytes + wave * Gm::aval_bytes;   // [grp][q][2G][16 B]
+  uint8_t *aval = ring + kRing * kWaves * Gm::tile_bytes + wave * Gm::aval_bytes;   // [grp][q][AR][16 B]
   float *P = reinterpret_cast<float *>(aval);   // [kTT][G], read out before aval is written
   auto slot_buf = [&](int64_t tile) -> uint8_t * {
     return ring + (static_cast<int>((tile / kWaves) % kRing) * kWaves + wave) * Gm::tile_bytes;
@@ -585,7 +587,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
           // hi = the weights rounded toward zero to f16, lo = f16 of the exact fp32 remainders
           const auto hi = __builtin_amdgcn_cvt_pkrtz(aa, ab);
           const auto lo = __builtin_amdgcn_cvt_pkrtz(aa - static_cast<float>(hi[0]), ab - static_cast<float>(hi[1]));
-          uint8_t *dst = aval + ((grp * 4 + qd) * (2 * G) + 2 * g) * 16 + 2 * i0;
+          uint8_t *dst = aval + ((grp * 4 + qd) * Gm::AR + 2 * g) * 16 + 2 * i0;
           *reinterpret_cast<uint32_t *>(dst) = __builtin_bit_cast(uint32_t, hi);
           *reinterpret_cast<uint32_t *>(dst + 16) = __builtin_bit_cast(uint32_t, lo);
         }
@@ -599,7 +601,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
 #pragma unroll
       for (int grp = 0; grp < kGroups; ++grp) {
         // rows >= 2G of the weight operand repeat rows < 2G; their outputs are never read
-        const v8h aop = *reinterpret_cast<const v8h *>(aval + ((grp * 4 + q) * (2 * G) + (n16 & (2 * G - 1))) * 16);
+        const v8h aop = *reinterpret_cast<const v8h *>(aval + ((grp * 4 + q) * Gm::AR + (n16 & (2 * G - 1))) * 16);
         // block word(s) of column n16: tokens 4 i + q of channels 32 grp + 16 h + n16;
         // operand dword k = K-slots (8q + 2k, 8q + 2k + 1) = i (2k, 2k + 1).  The
         // code itself, masked into the low mantissa bits of an f16 with a zero
