@@ -42,7 +42,7 @@
  * block c of slot s is one contiguous record at byte
  * (s * capacity / 32 + c) * block_bytes of the cache buffer, so a decoder
  * streams each 32-token block with a few large contiguous reads.  A record
- * holds seven fields one after the other, each 32 token rows of its own row
+ * holds six fields one after the other, each 32 token rows of its own row
  * format (offsets and sizes from aqkv_cache_layout):
  *   bit rows   32-bit little-endian words of 32 consecutive elements; element
  *              j = 4 i + k of a word (i in 0..7, k in 0..3) is bit 8 k + i.
@@ -57,8 +57,12 @@
  *              h, column n) of token 4 i + r (r in 0..3, i in 0..7) is at
  *                value_bits 2: word (16 g + n) * 4 + r, bits 8 h + 16 (i & 1) + 2 (i >> 1);
  *                value_bits 4: word ((16 g + n) * 4 + r) * 2 + h, bits 16 (i & 1) + 4 (i >> 1).
- *   val_scale  fp32 [d / value_group] per row.
- *   val_min    fp32 [d / value_group] per row.
+ *   val_side   fp32 scale and min of every value group, 8 * d / value_group
+ *              bytes per row, stored group-major in the record so that one
+ *              16-byte read returns what a decoder lane needs: the scale (j =
+ *              0) and min (j = 1) of group g for token t = 8 a + 4 h + b (b in
+ *              0..3, h in 0..1) is float ((g * 16 + 4 a + b) * 2 + h) * 2 + j of
+ *              the field.
  * The cache buffer must be 16-byte aligned (every block_bytes is a multiple
  * of 16).
  */
@@ -124,7 +128,7 @@ typedef struct {
 
 /* One 64-bit number per cache field. */
 typedef struct {
-  int64_t key_codes, key_signs, key_norm, key_rnorm, val_codes, val_scale, val_min;
+  int64_t key_codes, key_signs, key_norm, key_rnorm, val_codes, val_side;
 } aqkv_fields;
 
 /* Block-record geometry for a configuration. */
@@ -187,7 +191,7 @@ aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer,
  * value_group contiguous channels: min, scale = (max - min) / (2^vb - 1),
  * code = clamp(rint((v - min) / scale), 0, 2^vb - 1), all in IEEE fp32; code 0
  * when scale == 0.  Same view / offset rules as aqkv_quantize_keys; writes
- * val_codes, val_scale, val_min. */
+ * val_codes and val_side. */
 aqkv_status aqkv_quantize_values(const aqkv_config *cfg, const aqkv_kv_view *v, int64_t token_offset,
                                  const aqkv_cache *cache, void *stream);
 

@@ -51,8 +51,18 @@ class KvView(C.Structure):
                 ("token_stride", C.c_int64)]
 
 
-FIELDS = ("key_codes", "key_signs", "key_norm", "key_rnorm", "val_codes", "val_scale", "val_min")
-FLOAT_FIELDS = ("key_norm", "key_rnorm", "val_scale", "val_min")
+FIELDS = ("key_codes", "key_signs", "key_norm", "key_rnorm", "val_codes", "val_side")
+FLOAT_FIELDS = ("key_norm", "key_rnorm", "val_side")
+
+
+def side_index(groups: int) -> np.ndarray:
+    """[32 tokens, groups, 2] -> float index inside a record's val_side field
+    (j = 0 scale, 1 min; include/aqkv.h): ((g * 16 + 4 a + b) * 2 + h) * 2 + j for
+    token t = 8 a + 4 h + b."""
+    t = np.arange(32)[:, None, None]
+    g = np.arange(groups)[None, :, None]
+    j = np.arange(2)[None, None, :]
+    return ((g * 16 + 4 * (t >> 3) + (t & 3)) * 2 + ((t >> 2) & 1)) * 2 + j
 
 
 class Fields(C.Structure):
@@ -237,6 +247,27 @@ class Cache:
             k = min(32 - i, row0 + n - r)
             f[rec, i:i + k] = values[r - row0:r - row0 + k].reshape(k, -1)
             r += k
+
+    def value_side(self, row0: int, n: int):
+        """(scale, min) of cache rows row0 .. row0 + n - 1, each [n, groups] float32, in token order."""
+        import torch
+        groups = self.cfg.head_dim // self.cfg.value_group
+        f = self.field("val_side").flatten(1)                       # [records, 32 * groups * 2]
+        idx = torch.from_numpy(side_index(groups).reshape(-1)).to(f.device)
+        tok = f[:, idx].reshape(-1, 32, groups, 2).flatten(0, 1)   # rows in token order
+        sel = tok[row0:row0 + n]
+        return sel[..., 0].clone(), sel[..., 1].clone()
+
+    def set_value_side(self, row0: int, scale, vmin):
+        """Write scale / min [n, groups] into cache rows row0 .. row0 + n - 1."""
+        import torch
+        groups = self.cfg.head_dim // self.cfg.value_group
+        f = self.field("val_side").flatten(1)
+        idx = torch.from_numpy(side_index(groups)).to(f.device)
+        both = torch.stack([scale, vmin], dim=-1).to(f.dtype)
+        for i in range(scale.shape[0]):
+            rec, t = divmod(row0 + i, 32)
+            f[rec, idx[t].reshape(-1)] = both[i].reshape(-1)
 
     def desc(self) -> CacheDesc:
         return CacheDesc(_ptr(self.blocks), self.n_slots, self.capacity)

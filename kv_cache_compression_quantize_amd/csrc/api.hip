@@ -124,15 +124,13 @@ aqkv_status aqkv_cache_layout(const aqkv_config *cfg, aqkv_layout *out) {
     rb->key_norm = L.row[F_NORM];
     rb->key_rnorm = L.row[F_RNORM];
     rb->val_codes = L.row[F_VCODES];
-    rb->val_scale = L.row[F_VSCALE];
-    rb->val_min = L.row[F_VMIN];
+    rb->val_side = L.row[F_VSIDE];
     of->key_codes = L.off[F_CODES];
     of->key_signs = L.off[F_SIGNS];
     of->key_norm = L.off[F_NORM];
     of->key_rnorm = L.off[F_RNORM];
     of->val_codes = L.off[F_VCODES];
-    of->val_scale = L.off[F_VSCALE];
-    of->val_min = L.off[F_VMIN];
+    of->val_side = L.off[F_VSIDE];
     out->block_bytes = L.rec;
   }
   return AQKV_OK;
@@ -234,8 +232,7 @@ aqkv_status aqkv_quantize_values(const aqkv_config *cfg, const aqkv_kv_view *v, 
   job.group = cfg->value_group;
   const BlockLayout L = layout_of(cfg);
   job.codes = cache->blocks + L.off[F_VCODES];
-  job.scale = cache->blocks + L.off[F_VSCALE];
-  job.vmin = cache->blocks + L.off[F_VMIN];
+  job.side = cache->blocks + L.off[F_VSIDE];
   job.rec = L.rec;
   return hip_status(launch_quantize_values(job, static_cast<hipStream_t>(stream)));
 }
@@ -318,8 +315,7 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   job.norm = cache->blocks + L.off[F_NORM];
   job.rnorm = cache->blocks + L.off[F_RNORM];
   job.vcodes = cache->blocks + L.off[F_VCODES];
-  job.vscale = cache->blocks + L.off[F_VSCALE];
-  job.vmin = cache->blocks + L.off[F_VMIN];
+  job.vside = cache->blocks + L.off[F_VSIDE];
   job.q_rot = q_rot;
   job.q_sketch = q_sketch;
   job.softmax_scale = softmax_scale;

@@ -78,8 +78,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
     for (int i = 0; i < vwords; ++i)
       vcw[tid * vwords + i] = block_valid ? reinterpret_cast<const uint32_t *>(job.vcodes + rec_row(row, D * vb / 8, job.rec))[i] : 0u;
     for (int i = 0; i < kGroups; ++i) {
-      vsc[tid * kGroups + i] = valid ? reinterpret_cast<const float *>(job.vscale + rec_row(row, 4 * kGroups, job.rec))[i] : 0.0f;
-      vmn[tid * kGroups + i] = valid ? reinterpret_cast<const float *>(job.vmin + rec_row(row, 4 * kGroups, job.rec))[i] : 0.0f;
+      const float *side = reinterpret_cast<const float *>(job.vside + rec_row(row & ~int64_t(31), 0, job.rec));
+      vsc[tid * kGroups + i] = valid ? side[side_index(i, static_cast<int>(row & 31), 0)] : 0.0f;
+      vmn[tid * kGroups + i] = valid ? side[side_index(i, static_cast<int>(row & 31), 1)] : 0.0f;
     }
 
     // A. scores

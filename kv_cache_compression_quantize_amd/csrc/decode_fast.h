@@ -155,7 +155,7 @@ __host__ __device__ constexpr int pairs_of(int g, int d) { return (g * (d / 32) 
 // two buffers and more resident waves beat deeper prefetch with fewer waves).
 constexpr int kRing = 2;
 __host__ __device__ constexpr int tile_bytes_of(int d, int w, int mc, int vb) {
-  return kTT * (w * d / 8 + mc * 8 + 4 + (w > 0 ? 4 : 0) + d * vb / 8 + 8 * (d / 32));
+  return kTT * (w * d / 8 + mc * 8 + 4 + (w > 0 ? 4 : 0) + d * vb / 8 + 8 * (d / 32));   // = record bytes
 }
 // LDS bytes per block of decode_fast_kernel<D, W, m / 64, G, VB> (host and device):
 // per wave the tile ring and the value-weight operand [groups][4][2G + 1 rows][16 B],
@@ -185,13 +185,13 @@ struct Geo {
   static constexpr int kWpl = D >= 128 ? D / 128 : 1;    // plane words per lane per token
   static constexpr int kSw = (MC + 1) / 2;               // sign words per lane per token
   static constexpr int kPairs = pairs_of(G, D);
+  static constexpr int kLG = kGroups >= 4 ? kGroups / 4 : 1;   // value groups one lane reads per tile
   static constexpr int o_signs = kTT * CB;
   static constexpr int o_norm = o_signs + kTT * SB;
   static constexpr int o_rnorm = o_norm + kTT * 4;
   static constexpr int o_vcodes = o_rnorm + (W > 0 ? kTT * 4 : 0);
-  static constexpr int o_vscale = o_vcodes + kTT * VBY;
-  static constexpr int o_vmin = o_vscale + kTT * kGroups * 4;
-  static constexpr int tile_bytes = o_vmin + kTT * kGroups * 4;
+  static constexpr int o_vside = o_vcodes + kTT * VBY;
+  static constexpr int tile_bytes = o_vside + kTT * kGroups * 8;
   static_assert(tile_bytes == tile_bytes_of(D, W, MC, VB), "tile geometry");
   static constexpr int wave_lds = wave_lds_of(D, W, MC, G, VB);
   static constexpr int AR = aval_rows_of(G);        // 16-byte rows per (group, lane group) block
@@ -296,7 +296,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
                                             const float *kappa) {
   using Gm = Geo<D, W, MC, G, VB>;
   constexpr int RB = Gm::RB, HC = Gm::HC, kGroups = Gm::kGroups, CB = Gm::CB, SB = Gm::SB, VBY = Gm::VBY;
-  constexpr int kWpl = Gm::kWpl, kSw = Gm::kSw, kPairs = Gm::kPairs;
+  constexpr int kWpl = Gm::kWpl, kSw = Gm::kSw, kPairs = Gm::kPairs, kLG = Gm::kLG;
   constexpr int NP = popc(PL);
   constexpr int NC = NP * HC + MC;
   constexpr int NCmax = Gm::NCmax;
@@ -561,8 +561,12 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
     // ---------------- value weights a = p * scale (f16 hi + lo), correction sums p * min
     {
       const int qd = n16 & 3, i0 = 2 * (n16 >> 2);
-      const float *vs = reinterpret_cast<const float *>(tb + Gm::o_vscale);
-      const float *vm = reinterpret_cast<const float *>(tb + Gm::o_vmin);
+      // {scale, min} of tokens ta and ta + 4 of group (q + 4u) % kGroups: one
+      // contiguous 16-byte read per lane (group-major val_side field)
+      float4 side[kLG];
+#pragma unroll
+      for (int u = 0; u < kLG; ++u)
+        side[u] = reinterpret_cast<const float4 *>(tb + Gm::o_vside)[((q + 4 * u) % kGroups) * 16 + n16];
       float pa[G], pb[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -575,8 +579,8 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
         const int pair = q + 4 * k;
         if (pair < G * kGroups) {
           const int g = pair / kGroups, grp = pair % kGroups;
-          const float sa = vs[ta * kGroups + grp], sb = vs[tb4 * kGroups + grp];
-          const float ma = vm[ta * kGroups + grp], mb = vm[tb4 * kGroups + grp];
+          const float4 sd = side[k % kLG];   // group (q + 4 k) % kGroups
+          const float sa = sd.x, ma = sd.y, sb = sd.z, mb = sd.w;
           // legacy multiply: 0 * x = 0 for any x, so masked tokens (p = 0) ignore
           // whatever their cache rows hold
           float aa = fmul_legacy(pa[g], sa);

@@ -15,7 +15,7 @@ constexpr int kBlockRows = 32;   // token rows per cache block record
 
 // Block-record geometry (include/aqkv.h): fields in record order, bytes per
 // row and offsets; rec = bytes of one 32-row record.
-enum Field { F_CODES = 0, F_SIGNS, F_NORM, F_RNORM, F_VCODES, F_VSCALE, F_VMIN, F_COUNT };
+enum Field { F_CODES = 0, F_SIGNS, F_NORM, F_RNORM, F_VCODES, F_VSIDE, F_COUNT };
 struct BlockLayout {
   int64_t row[F_COUNT];
   int64_t off[F_COUNT];
@@ -28,8 +28,7 @@ inline BlockLayout block_layout(int d, int w, int m, int vb) {
   L.row[F_NORM] = 4;
   L.row[F_RNORM] = w > 0 ? 4 : 0;
   L.row[F_VCODES] = static_cast<int64_t>(d) * vb / 8;
-  L.row[F_VSCALE] = 4 * (d / 32);
-  L.row[F_VMIN] = 4 * (d / 32);
+  L.row[F_VSIDE] = 8 * (d / 32);
   int64_t o = 0;
   for (int f = 0; f < F_COUNT; ++f) {
     L.off[f] = o;
@@ -37,6 +36,13 @@ inline BlockLayout block_layout(int d, int w, int m, int vb) {
   }
   L.rec = o;
   return L;
+}
+
+// Float index, within a record's val_side field, of the scale (j = 0) or min
+// (j = 1) of value group g of the record's token t (0..31): group-major, tokens
+// t and t + 4 of a group side by side (include/aqkv.h).
+__host__ __device__ inline int side_index(int g, int t, int j) {
+  return ((g * 16 + 4 * (t >> 3) + (t & 3)) * 2 + ((t >> 2) & 1)) * 2 + j;
 }
 
 // Byte offset, from a field's place in record 0, of cache row `row` (= slot *
@@ -68,7 +74,7 @@ struct ValueJob {
   int64_t n_slots, n_tokens, token_offset, capacity;
   int d, vb, group;
   // cache fields, each at its place in record 0; row r at + rec_row(r, row bytes, rec)
-  uint8_t *codes, *scale, *vmin;
+  uint8_t *codes, *side;
   int64_t rec;
 };
 
@@ -91,7 +97,7 @@ struct DecodeJob {
   // cache: the slots' records (blocks) and each field at its place in record 0
   const uint8_t *blocks;
   int64_t rec;
-  const uint8_t *codes, *signs, *norm, *rnorm, *vcodes, *vscale, *vmin;
+  const uint8_t *codes, *signs, *norm, *rnorm, *vcodes, *vside;
   const float *q_rot, *q_sketch;
   float softmax_scale;
   float *scores;         // nullable [n_slots*g][context]

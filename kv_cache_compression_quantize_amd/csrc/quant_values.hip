@@ -9,8 +9,8 @@
 // 32-token cache block of one slot:
 //   1. one thread per (token, group): 32 elements loaded with 16-byte loads,
 //      min / max, scale = (max - min) / (2^vb - 1) and the codes in IEEE fp32
-//      (subtract, correctly rounded divide, round-half-even); scale and min are
-//      written to their rows, the codes to LDS;
+//      (subtract, correctly rounded divide, round-half-even); scale and min go
+//      to the record's val_side field, the codes to LDS;
 //   2. one thread per output word gathers its 16 (vb = 2) or 8 (vb = 4) codes;
 //      words of a block only partly covered by this call keep the bits of the
 //      other tokens (read-modify-write), so appends of any length work.
@@ -84,9 +84,10 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueJob job, int6
       }
       cds[tt][g * kGroup + i] = static_cast<uint8_t>(code);
     }
-    const int64_t row = s * job.capacity + ct;
-    reinterpret_cast<float *>(job.scale + rec_row(row, kGroups * 4, job.rec))[g] = scale;
-    reinterpret_cast<float *>(job.vmin + rec_row(row, kGroups * 4, job.rec))[g] = mn;
+    // scale and min into the record's val_side field (group-major, include/aqkv.h)
+    float *side = reinterpret_cast<float *>(job.side + rec_row(s * job.capacity + ct0, 0, job.rec));
+    side[side_index(g, tt, 0)] = scale;
+    side[side_index(g, tt, 1)] = mn;
   }
   __syncthreads();
 

@@ -82,8 +82,9 @@ def read_planes(cache: aqkv.Cache, slot: int, t0: int, t1: int) -> dict:
     # value codes live in 32-token blocks: whole blocks covering [t0, t1) (only when t0 % 32 == 0)
     b1 = slot * cache.capacity + (t1 + 31) // 32 * 32
     vcodes = cache.rows("val_codes", r0, b1 - r0).cpu().numpy() if t0 % 32 == 0 else None
+    vscale, vmin = cache.value_side(r0, r1 - r0)
     return dict(codes=g("key_codes"), signs=g("key_signs"), norm=g("key_norm"), rnorm=g("key_rnorm"),
-                vcodes=vcodes, vscale=g("val_scale"), vmin=g("val_min"))
+                vcodes=vcodes, vscale=vscale.cpu().numpy(), vmin=vmin.cpu().numpy())
 
 
 def oracle_rows(hl: HostLayer, k: np.ndarray, v: np.ndarray, vb: int = 2):

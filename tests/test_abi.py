@@ -39,9 +39,9 @@ def test_status_strings():
 def test_cache_layout_and_bad_configs():
     lo = aqkv.cache_layout(aqkv.config(128, 2, 128))
     rb = lo["row"]
-    assert rb == dict(key_codes=32, key_signs=16, key_norm=4, key_rnorm=4, val_codes=32, val_scale=16, val_min=16)
+    assert rb == dict(key_codes=32, key_signs=16, key_norm=4, key_rnorm=4, val_codes=32, val_side=32)
     assert sum(rb.values()) == 120 and lo["block_bytes"] == 32 * 120
-    # a record holds the seven fields one after the other, 32 rows each
+    # a record holds the six fields one after the other, 32 rows each
     off = 0
     for name in aqkv.FIELDS:
         assert lo["offset"][name] == off
@@ -168,3 +168,14 @@ def test_library_rotation_matches_oracle(d, layer):
     ref = orot.rotation_from_gaussian(g)
     assert np.max(np.abs(pi.astype(np.float64) - ref)) < 2e-7
     assert np.max(np.abs(pi.astype(np.float64).T @ pi.astype(np.float64) - np.eye(d))) < 1e-6
+
+
+def test_value_side_index_is_a_permutation():
+    # the scale / min of every (token, group) of a record has its own float of the field,
+    # and tokens t, t + 4 of a group share one 16-byte quad
+    for groups in (2, 4, 8):
+        idx = aqkv.side_index(groups)
+        assert sorted(idx.reshape(-1).tolist()) == list(range(32 * groups * 2))
+        for t in range(32):
+            if (t >> 2) & 1 == 0:
+                np.testing.assert_array_equal(idx[t + 4] // 4, idx[t] // 4)

@@ -186,8 +186,7 @@ def _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity):
         cache.set_rows("key_signs", r0, torch.from_numpy(signs).to(dev))
         cache.set_rows("key_norm", r0, torch.from_numpy(norm).to(dev))
         cache.set_rows("val_codes", r0, torch.from_numpy(vpacked).to(dev))
-        cache.set_rows("val_scale", r0, torch.from_numpy(vt[1]).to(dev))
-        cache.set_rows("val_min", r0, torch.from_numpy(vt[2]).to(dev))
+        cache.set_value_side(r0, torch.from_numpy(vt[1]).to(dev), torch.from_numpy(vt[2]).to(dev))
         # the oracle consumes exactly what was stored (fp32 norms)
         refs.append(((qk.idx, qk.bits, norm.astype(np.float64), rnorm.astype(np.float64)), vt))
     return cache, refs
