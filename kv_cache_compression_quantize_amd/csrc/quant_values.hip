@@ -3,18 +3,42 @@
 // "Value 分组量化 2 bit/维, min-max", and §七, kv_cache.py "value group
 // quantisation and bit packing").
 //
-// Codes are stored in blocks of 32 tokens (the val_codes field of a cache
-// block record) so that a decoder reads, for one channel, the codes of 8
-// tokens of the block from one 32-bit word (layout in include/aqkv.h).  One block of 256 threads owns one
-// 32-token cache block of one slot:
-//   1. one thread per (token, group): 32 elements loaded with 16-byte loads,
-//      min / max, scale = (max - min) / (2^vb - 1) and the codes in IEEE fp32
-//      (subtract, correctly rounded divide, round-half-even); scale and min go
-//      to the record's val_side field, the codes to LDS;
-//   2. one thread per output word gathers its 16 (vb = 2) or 8 (vb = 4) codes;
-//      words of a block only partly covered by this call keep the bits of the
-//      other tokens (read-modify-write), so appends of any length work.
-// The pass is a streaming one, bound by HBM bandwidth.
+// code = clamp(rint((v - min) / scale), 0, 2^vb - 1) with scale = (max - min) /
+// (2^vb - 1), every step in IEEE fp32 (subtract, correctly rounded divide,
+// round-half-even); code 0 when scale == 0.
+//
+// Lane layout.  The code block of a record stores, per (group g, column n,
+// token residue r), the codes of channel 32 g + 16 half + n for the tokens
+// 8 a + 4 b + r (a = 0..3, b = 0..1) of the record, a = the position inside a
+// byte (vb = 2) or half-word (vb = 4), (half, b) = which one (include/aqkv.h).
+// So one thread of a record takes the tokens c + 8 a (c = 4 b + r, a = 0..3)
+// of one 8-channel chunk: the four codes of each of its channels make one
+// finished byte / half-word of the output.  Threads c * (d / 8) + chunk, so the
+// 4 threads that share a (token, group) are neighbouring lanes (min / max by
+// DPP lane swaps) and each load instruction of a wave reads whole tokens.
+//
+// Scale.  fl(x / L) for x = max - min in [1e-28, 1e28] is q0 = x * fl(1/L),
+// r = fma(-q0, L, x) (exact), fl(x / L) = fma(r, fl(1/L), q0): for L = 3 and
+// 15 this equals the IEEE quotient for every fp32 significand (exhaustive
+// check in the tests), and the exponent range keeps every step normal; other
+// x take the IEEE divide.
+//
+// Codes.  With rr = rcp(scale) (1 ulp) and c0 = 0.5 - min * rr (one fma),
+// fma(v, rr, c0) lies within (5 L + 1 + 2 |c0|) 2^-24 of
+// X = fl(fl(v - min) / scale) + 0.5 (L = 2^vb - 1, quotients <= L), well inside
+// eps = (|c0| + L + 2) 2^-21.  So t = fma(v, rr, c0 - eps) has X in
+// (t, t + 2 eps): when fract(t) < 1 - 2 eps that interval holds no integer,
+// floor(t) = floor(X) and X is no tie, so floor(t) is the round-half-even
+// code.  A piece (8 values of one token) with a value that fails the test, or
+// with a scale outside [1e-30, 1e30], is redone with IEEE subtract, divide and
+// rint.
+//
+// Each record's bytes / half-words are assembled in LDS (rows of 64 words
+// padded by 8 so the byte writes of a wave spread over the banks) and leave as
+// 16-byte stores; words of a record only partly covered by the call keep the
+// bits of the other tokens (read-modify-write), so appends of any length work.
+// The pass is a streaming one: HBM bandwidth with a thin VALU margin
+// (about 9 vector instructions per value).
 #include "internal.h"
 
 namespace aqkv {
@@ -23,103 +47,169 @@ namespace {
 constexpr int kGroup = 32;
 constexpr int kBlockTokens = 32;
 
-template <int D, int VB, bool BF16>
-__global__ __launch_bounds__(256) void quantize_values_kernel(ValueJob job, int64_t blocks_per_slot) {
-  constexpr int kGroups = D / kGroup;
-  constexpr int kLevels = (1 << VB) - 1;
-  __shared__ uint8_t cds[kBlockTokens][D];
-  const int tid = threadIdx.x;
-  const int64_t s = blockIdx.x / blocks_per_slot;
-  const int64_t cblk = job.token_offset / kBlockTokens + blockIdx.x % blocks_per_slot;   // cache block
-  const int64_t ct0 = cblk * kBlockTokens;                                              // its first cache token
-  const int64_t lo = max<int64_t>(ct0, job.token_offset);
-  const int64_t hi = min<int64_t>(ct0 + kBlockTokens, job.token_offset + job.n_tokens);
-  const int64_t b = s / job.heads, h = s % job.heads;
+// min and max over the 4 consecutive (aligned) lanes that share a group
+// (quad permutations read only lanes that exist, so bound_ctrl changes nothing
+// and lets the swap fold into the min / max as one DPP instruction)
+__device__ __forceinline__ float quad_min(float x) {
+  x = fminf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));   // lane ^ 1
+  return fminf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));   // lane ^ 2
+}
+__device__ __forceinline__ float quad_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));
+}
 
-  // 1. codes of (token, group)
-  for (int item = tid; item < kBlockTokens * kGroups; item += 256) {
-    const int tt = item / kGroups, g = item % kGroups;
-    const int64_t ct = ct0 + tt;
-    if (ct < lo || ct >= hi) continue;
-    const int64_t t = ct - job.token_offset;      // input token
-    const int64_t src = b * job.batch_stride + h * job.head_stride + t * job.token_stride + g * kGroup;
-    float v[kGroup];
-    if (BF16) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(job.v) + src);
+// padded LDS word index of code word wi
+__device__ __forceinline__ int lds_word(int wi) { return wi + 8 * (wi >> 6); }
+
+// fl(x / L), L = 2^vb - 1
+template <int L>
+__device__ __forceinline__ float div_levels(float x) {
+  if (!(x >= 1.0e-28f && x <= 1.0e28f)) return x / static_cast<float>(L);   // IEEE divide
+  constexpr float z = 1.0f / static_cast<float>(L);
+  const float q0 = x * z;
+  const float r = __builtin_fmaf(-q0, static_cast<float>(L), x);
+  return __builtin_fmaf(r, z, q0);
+}
+
+template <int D, int VB, bool BF16>
+__global__ __launch_bounds__(256) void quantize_values_kernel(ValueJob job, int blocks_per_slot, int n_rec) {
+  constexpr int kLevels = (1 << VB) - 1;
+  constexpr int kChunks = D / 8;                  // 8-channel chunks per token
+  constexpr int kRpb = 256 / D;                   // records per block (a record's threads are whole waves)
+  constexpr int kWords = D * VB;                  // code words per record
+  constexpr int kLdsWords = kWords + 8 * (kWords / 64);
+  constexpr int kElt = BF16 ? 2 : 4;
+  constexpr int kLoads = BF16 ? 1 : 2;            // 16-byte loads per (token, chunk)
+  __shared__ uint4 lds_all[kRpb * kLdsWords / 4];
+  const int tid = threadIdx.x;
+  const int sub = __builtin_amdgcn_readfirstlane(tid / D);   // record within the block
+  const int lane = tid % D;
+  const int c = lane / kChunks, chunk = lane % kChunks;
+  const int rid0 = blockIdx.x * kRpb + sub;
+  const bool live = rid0 < n_rec;                  // the last block may hold fewer records (all reach the barrier)
+  const int rid = live ? rid0 : 0;
+  const int64_t s = rid / blocks_per_slot;
+  const int64_t ct0 = (job.token_offset / kBlockTokens + rid % blocks_per_slot) * kBlockTokens;
+  // tokens [t_lo, t_hi) of the record are in this call
+  const int t_lo = live ? static_cast<int>(max<int64_t>(ct0, job.token_offset) - ct0) : 0;
+  const int t_hi = live ? static_cast<int>(min<int64_t>(ct0 + kBlockTokens, job.token_offset + job.n_tokens) - ct0) : 0;
+  const int64_t b = s / job.heads, h = s % job.heads;
+  const int64_t stride_bytes = job.token_stride * kElt;
+  const char *rbase = static_cast<const char *>(job.v) +
+                      (b * job.batch_stride + h * job.head_stride) * kElt + (ct0 - job.token_offset) * stride_bytes;
+  const char *lbase = rbase + c * stride_bytes + 8 * chunk * kElt;
+
+  // 1. every load in flight first: tokens c + 8 a, channels 8 chunk .. + 7
+  uint4 raw[4][kLoads];
 #pragma unroll
-      for (int i = 0; i < kGroup / 8; ++i) {
-        const uint4 qv = p[i];
-        const uint32_t wv[4] = {qv.x, qv.y, qv.z, qv.w};
+  for (int a = 0; a < 4; ++a) {
+    const int tt = c + 8 * a;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[8 * i + 2 * j] = bf16_to_f32(wv[j] & 0xffffu);
-          v[8 * i + 2 * j + 1] = bf16_to_f32(wv[j] >> 16);
+    for (int l = 0; l < kLoads; ++l) raw[a][l] = make_uint4(0, 0, 0, 0);
+    if (tt >= t_lo && tt < t_hi) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(lbase + 8 * a * stride_bytes);
+#pragma unroll
+      for (int l = 0; l < kLoads; ++l) raw[a][l] = src[l];
+    }
+  }
+
+  const int g = chunk / 4, q = chunk % 4;         // group, lane within the group
+  // val_side float of (g, token c + 8 a, q): side_lane + 16 a
+  float *side_lane = reinterpret_cast<float *>(job.side + rec_row(s * job.capacity + ct0, 0, job.rec)) +
+                     side_index(g, c, q);
+  uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};     // per channel: its 4 codes, VB bits apart
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    float v[8];
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const uint32_t wv[4] = {raw[a][l].x, raw[a][l].y, raw[a][l].z, raw[a][l].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (BF16) {
+          v[2 * j] = __uint_as_float(wv[j] << 16);
+          v[2 * j + 1] = __uint_as_float(wv[j] & 0xffff0000u);
+        } else {
+          v[4 * l + j] = __uint_as_float(wv[j]);
         }
       }
+    }
+    float mn = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])), fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
+    float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    mn = quad_min(mn);
+    mx = quad_max(mx);
+    const float scale = div_levels<kLevels>(mx - mn);
+    const float rr = __builtin_amdgcn_rcpf(scale);
+    const float c0 = fmaf(-mn, rr, 0.5f);
+    const float eps = (fabsf(c0) + static_cast<float>(kLevels + 2)) * 4.76837158203125e-7f;
+    const float c1 = c0 - eps;                     // t - eps: no integer in (t - eps, t + eps] <=> fract < 1 - 2 eps
+    const float th = 1.0f - 2.0f * eps;
+    uint32_t codes[8];
+    bool near = !(scale >= 1.0e-30f && scale <= 1.0e30f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float t = fmaf(v[j], rr, c1);
+      codes[j] = static_cast<uint32_t>(t);                          // floor: t > 0
+      near |= __builtin_amdgcn_fractf(t) >= th;
+    }
+    if (near) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float cf = scale > 0.0f ? rintf((v[j] - mn) / scale) : 0.0f;
+        codes[j] = static_cast<uint32_t>(fminf(fmaxf(cf, 0.0f), static_cast<float>(kLevels)));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] |= codes[j] << (VB * a);
+    const int tt = c + 8 * a;
+    if (q < 2 && tt >= t_lo && tt < t_hi) side_lane[16 * a] = q == 0 ? scale : mn;
+  }
+
+  // 2. bytes (vb = 2) / half-words (vb = 4) into the record's LDS words
+  uint32_t *lw = reinterpret_cast<uint32_t *>(lds_all) + sub * kLdsWords;
+  const int half = q / 2, bb = c / 4, r = c % 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int n = 8 * (chunk % 2) + j;
+    if constexpr (VB == 2) {
+      const int wi = g * 64 + n * 4 + r;
+      reinterpret_cast<uint8_t *>(lw)[4 * lds_word(wi) + half + 2 * bb] = static_cast<uint8_t>(acc[j]);
     } else {
-      const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(job.v) + src);
-#pragma unroll
-      for (int i = 0; i < kGroup / 4; ++i) {
-        const float4 qv = p[i];
-        v[4 * i] = qv.x;
-        v[4 * i + 1] = qv.y;
-        v[4 * i + 2] = qv.z;
-        v[4 * i + 3] = qv.w;
-      }
+      const int wi = g * 128 + n * 8 + r * 2 + half;
+      reinterpret_cast<uint16_t *>(lw)[2 * lds_word(wi) + bb] = static_cast<uint16_t>(acc[j]);
     }
-    float mn = v[0], mx = v[0];
-#pragma unroll
-    for (int i = 1; i < kGroup; ++i) {
-      mn = fminf(mn, v[i]);
-      mx = fmaxf(mx, v[i]);
-    }
-    const float scale = (mx - mn) / static_cast<float>(kLevels);   // IEEE divide
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      uint32_t code = 0;
-      if (scale > 0.0f) {
-        float c = rintf((v[i] - mn) / scale);                     // IEEE subtract, divide, RNE
-        c = fminf(fmaxf(c, 0.0f), static_cast<float>(kLevels));
-        code = static_cast<uint32_t>(c);
-      }
-      cds[tt][g * kGroup + i] = static_cast<uint8_t>(code);
-    }
-    // scale and min into the record's val_side field (group-major, include/aqkv.h)
-    float *side = reinterpret_cast<float *>(job.side + rec_row(s * job.capacity + ct0, 0, job.rec));
-    side[side_index(g, tt, 0)] = scale;
-    side[side_index(g, tt, 1)] = mn;
   }
   __syncthreads();
 
-  // 2. block words
-  constexpr int kWords = kBlockTokens * D * VB / 32;
-  // the code block of these 32 tokens: the val_codes field of one record
-  uint32_t *dst = reinterpret_cast<uint32_t *>(job.codes + rec_row(s * job.capacity + ct0, D * VB / 8, job.rec));
-  const bool full = lo == ct0 && hi == ct0 + kBlockTokens;
-  for (int wi = tid; wi < kWords; wi += 256) {
-    // word -> (group g, column n, token residue r) and the channel half(s) it holds
-    const int g = VB == 2 ? wi / 64 : wi / 128;
-    const int n = VB == 2 ? (wi / 4) % 16 : (wi / 8) % 16;
-    const int r = VB == 2 ? wi % 4 : (wi / 2) % 4;
-    constexpr int kHalves = VB == 2 ? 2 : 1;
-    uint32_t word = 0, cover = 0;
+  // 3. the record's code words, 16 bytes a thread
+  if (live && lane < kWords / 4) {
+    uint4 w = *reinterpret_cast<const uint4 *>(lw + lds_word(4 * lane));
+    uint4 *dst = reinterpret_cast<uint4 *>(job.codes + rec_row(s * job.capacity + ct0, D * VB / 8, job.rec)) + lane;
+    if (t_lo != 0 || t_hi != kBlockTokens) {
+      // bits of the tokens of this call: word (.., r, ..) holds tokens 4 i + r
+      uint32_t cover[4];
 #pragma unroll
-    for (int e = 0; e < kHalves; ++e) {
-      const int half = VB == 2 ? e : wi % 2;
-      const int ch = 32 * g + 16 * half + n;
+      for (int k = 0; k < 4; ++k) {
+        const int wi = 4 * lane + k;
+        const int rw = VB == 2 ? wi % 4 : (wi / 2) % 4;
+        uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tt = 4 * i + r;
-        const int bit = VB == 2 ? 8 * half + 16 * (i & 1) + 2 * (i >> 1) : 16 * (i & 1) + 4 * (i >> 1);
-        const int64_t ct = ct0 + tt;
-        if (ct >= lo && ct < hi) {
-          word |= static_cast<uint32_t>(cds[tt][ch]) << bit;
-          cover |= static_cast<uint32_t>(kLevels) << bit;
+        for (int i = 0; i < 8; ++i) {
+          const int tt = 4 * i + rw;
+          const int bit = VB == 2 ? 16 * (i & 1) + 2 * (i >> 1) : 16 * (i & 1) + 4 * (i >> 1);
+          const uint32_t one = VB == 2 ? (3u << bit) | (3u << (bit + 8)) : 15u << bit;
+          if (tt >= t_lo && tt < t_hi) m |= one;
         }
+        cover[k] = m;
       }
+      const uint4 old = *dst;
+      w.x = (old.x & ~cover[0]) | (w.x & cover[0]);
+      w.y = (old.y & ~cover[1]) | (w.y & cover[1]);
+      w.z = (old.z & ~cover[2]) | (w.z & cover[2]);
+      w.w = (old.w & ~cover[3]) | (w.w & cover[3]);
     }
-    if (!full) word = (dst[wi] & ~cover) | word;
-    dst[wi] = word;
+    *dst = w;
   }
 }
 
@@ -128,14 +218,18 @@ hipError_t launch_d(const ValueJob &job, hipStream_t stream) {
   const int64_t first = job.token_offset / kBlockTokens;
   const int64_t last = (job.token_offset + job.n_tokens - 1) / kBlockTokens;
   const int64_t per_slot = last - first + 1;
-  const dim3 grid(static_cast<unsigned>(per_slot * job.n_slots));
+  const int64_t n_rec = per_slot * job.n_slots;
+  if (n_rec >= (int64_t{1} << 31)) return hipErrorInvalidValue;
+  constexpr int kRpb = 256 / D;
+  const dim3 grid(static_cast<unsigned>((n_rec + kRpb - 1) / kRpb));
+  const int bps = static_cast<int>(per_slot), nr = static_cast<int>(n_rec);
   const bool bf16 = job.dtype == AQKV_BF16;
   if (job.vb == 2) {
-    if (bf16) quantize_values_kernel<D, 2, true><<<grid, 256, 0, stream>>>(job, per_slot);
-    else quantize_values_kernel<D, 2, false><<<grid, 256, 0, stream>>>(job, per_slot);
+    if (bf16) quantize_values_kernel<D, 2, true><<<grid, 256, 0, stream>>>(job, bps, nr);
+    else quantize_values_kernel<D, 2, false><<<grid, 256, 0, stream>>>(job, bps, nr);
   } else {
-    if (bf16) quantize_values_kernel<D, 4, true><<<grid, 256, 0, stream>>>(job, per_slot);
-    else quantize_values_kernel<D, 4, false><<<grid, 256, 0, stream>>>(job, per_slot);
+    if (bf16) quantize_values_kernel<D, 4, true><<<grid, 256, 0, stream>>>(job, bps, nr);
+    else quantize_values_kernel<D, 4, false><<<grid, 256, 0, stream>>>(job, bps, nr);
   }
   return hipGetLastError();
 }

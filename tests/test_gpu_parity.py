@@ -104,6 +104,13 @@ def test_quantize_values_bit_exact(d, vb, dtype):
     v = _as_dtype(_kv(B, H, T, d, seed=7 + d + vb, scale=3.0), dtype)
     v[0, 0, 3, :32] = 1.25                # constant group
     v[1, 2, 9, 32:64] = -0.0
+    # groups spanning exactly 2^vb - 1 in steps of 1/2: scale 1 and every other
+    # quotient an exact tie (round half to even)
+    levels = (1 << vb) - 1
+    ties = (np.arange(32) % (2 * levels + 1)) * 0.5
+    v[0, 1, 5, :32] = ties
+    v[1, 0, 6, d - 32:] = ties - 1.0
+    v[1, 1, 30, :32] = ties[::-1] * 0.25 + 3.0     # the same ties at scale 1/4, away from zero
     hl = host_layer(d, 2, d)
     cfg = cfg_of(hl, vb)
     cache = aqkv.Cache.allocate(cfg, B * H, T)
