@@ -324,10 +324,33 @@ __device__ __forceinline__ void fetch_slab(SlabOps<D> &A, const uint8_t *slab) {
 template <int D, int W>
 struct IndexState {
   static constexpr int NB = (1 << W) - 1;
+  static constexpr int NU = W > 0 ? (1 << (W - 1)) - 1 : 0;   // boundaries above the middle one
   float bnd[NB], cen[NB + 1];                // scaled by 2^8
   uint32_t wv[W][Geo<D>::NT];                // words being built, most significant bit first
   float esq[Geo<D>::NT];                     // ||2^8 e||^2 (this lane's part)
+  float bts[NU > 0 ? NU : 1][Geo<D>::NT];    // symmetric codebook: upper boundaries / yscale, per key
 };
+
+// An odd-symmetric codebook (c[K-1-i] = -c[i], b[K-2-i] = -b[i], middle
+// boundary 0, K = 2^W), as Lloyd-Max gives for the symmetric coordinate law,
+// is indexed from the sign and |y| alone: for s = (y > 0) and m = the number
+// of upper boundaries below |y|, idx = s ? K/2 + m : K/2 - 1 - m, i.e. the top
+// bit is s and the lower bits are those of m, inverted when s = 0; the
+// centroid is sign(y) c[K/2 + m].
+template <int W>
+__device__ __forceinline__ bool codebook_symmetric(const KeyJob &job) {
+  if constexpr (W == 0) {
+    return false;
+  } else {
+    constexpr int K = 1 << W;
+    bool sym = job.boundaries[K / 2 - 1] == 0.0f;
+#pragma unroll
+    for (int i = 0; i < K / 2; ++i) sym = sym && job.centroids[K - 1 - i] == -job.centroids[i];
+#pragma unroll
+    for (int i = 0; i < K / 2 - 1; ++i) sym = sym && job.boundaries[K - 2 - i] == -job.boundaries[i];
+    return sym;
+  }
+}
 
 template <int D, int W>
 __device__ __forceinline__ void index_codebook(const KeyJob &job, IndexState<D, W> &S) {
@@ -343,19 +366,47 @@ __device__ __forceinline__ void index_begin(IndexState<D, W> &S) {
   for (int nt = 0; nt < Geo<D>::NT; ++nt) S.esq[nt] = 0.0f;
 }
 
+// Symmetric codebook: |y'| > b' <=> |acc| > b' / yscale (yscale > 0; a zero
+// key's infinite threshold leaves m = 0)
+template <int D, int W>
+__device__ __forceinline__ void index_thresholds(IndexState<D, W> &S, const float (&yscale)[Geo<D>::NT]) {
+  constexpr int K = 1 << W;
+#pragma unroll
+  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
+    const float inv = 1.0f / yscale[nt];
+#pragma unroll
+    for (int j = 0; j < IndexState<D, W>::NU; ++j) S.bts[j][nt] = S.bnd[K / 2 + j] * inv;
+  }
+}
+
+// The words of a finished group: in the symmetric form the top plane collected
+// sign bits (1 = negative) and the lower planes the bits of m; idx's top bit is
+// the inverted sign and its lower bits are m's xor the sign.  `valid` masks the
+// bits a (half) word holds.
+template <int D, int W, bool SYM>
+__device__ __forceinline__ void finish_words(IndexState<D, W> &S, uint32_t valid) {
+  if constexpr (SYM) {
+#pragma unroll
+    for (int nt = 0; nt < Geo<D>::NT; ++nt) {
+      const uint32_t neg = S.wv[W - 1][nt];
+#pragma unroll
+      for (int p = 0; p < W - 1; ++p) S.wv[p][nt] ^= neg;
+      S.wv[W - 1][nt] = ~neg & valid;
+    }
+  }
+}
+
 // Rotated tile t of the key tile: acc = (2^8 Pi rows of tile t) x (key
 // operand); y' = acc * yscale = 2^8 y.  Indices go into the words, e' = y' - c'
 // (2^8 e: exact scaling) into the sketch's B operand (slots 4 (t % 2) + i of
 // k-step t / 2), e'^2 into esq.  The index is the thermometer count of the
 // comparisons; bit p of it is the xor of the comparisons q with
 // (q + 1) % 2^p == 0.
-template <int D, int W, bool BF16>
-__device__ __forceinline__ void index_tile(int t, const SlabOps<D> &A, const Ops<D> &uh, const Ops<D> &ul,
-                                           const float (&yscale)[Geo<D>::NT], IndexState<D, W> &S, Ops<D> &bh,
-                                           Ops<D> &bl) {
+// The rotation product of one 16-row tile (matrix cores only)
+template <int D, bool BF16>
+__device__ __forceinline__ void rot_tile(const SlabOps<D> &A, const Ops<D> &uh, const Ops<D> &ul,
+                                         v4f (&acc)[Geo<D>::NT]) {
   constexpr int NT = Geo<D>::NT;
-  constexpr int NB = IndexState<D, W>::NB;
-  v4f acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -369,9 +420,47 @@ __device__ __forceinline__ void index_tile(int t, const SlabOps<D> &A, const Ops
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_v8h(uh[nt][k]), acc[nt], 0, 0, 0);
     }
   }
+}
+
+// Indices, residual operand and ||e||^2 of rotated tile t (vector ALU only)
+template <int D, int W, bool SYM>
+__device__ __forceinline__ void index_vals(int t, const v4f (&acc)[Geo<D>::NT], const float (&yscale)[Geo<D>::NT],
+                                           IndexState<D, W> &S, Ops<D> &bh, Ops<D> &bl) {
+  constexpr int NT = Geo<D>::NT;
+  constexpr int NB = IndexState<D, W>::NB;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float e[4];
+    if constexpr (SYM) {
+      constexpr int K = 1 << W;
+      constexpr int NU = IndexState<D, W>::NU;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        const float av = acc[nt][i];
+        const float aa = fabsf(av);
+        bool a[NU > 0 ? NU : 1];
+        float cm = S.cen[K / 2];
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+          a[j] = aa > S.bts[j][nt];
+          cm = a[j] ? S.cen[K / 2 + 1 + j] : cm;
+        }
+        // top plane: the sign bit of y (inverted when the group's words finish)
+        S.wv[W - 1][nt] = __builtin_amdgcn_alignbit(S.wv[W - 1][nt], __float_as_uint(av), 31);
+#pragma unroll
+        for (int p = 0; p < W - 1; ++p) {
+          bool bit = false;
+#pragma unroll
+          for (int j = 0; j < NU; ++j)
+            if (((j + 1) & ((1 << p) - 1)) == 0) bit ^= a[j];
+          S.wv[p][nt] = push_bit(S.wv[p][nt], bit);
+        }
+        // e' = sign(y) (|y'| - c'_m)
+        const float em = fmaf(aa, yscale[nt], -cm);
+        e[i] = __uint_as_float(__float_as_uint(em) ^ (__float_as_uint(av) & 0x80000000u));
+        S.esq[nt] = fmaf(em, em, S.esq[nt]);
+      }
+    } else {
 #pragma unroll
     for (int i = 3; i >= 0; --i) {
       const float y = acc[nt][i] * yscale[nt];
@@ -393,15 +482,25 @@ __device__ __forceinline__ void index_tile(int t, const SlabOps<D> &A, const Ops
       e[i] = y - cv;
       S.esq[nt] = fmaf(e[i], e[i], S.esq[nt]);
     }
+    }
     split_pair(e[0], e[1], bh[nt][t >> 1].w[2 * (t & 1)], bl[nt][t >> 1].w[2 * (t & 1)]);
     split_pair(e[2], e[3], bh[nt][t >> 1].w[2 * (t & 1) + 1], bl[nt][t >> 1].w[2 * (t & 1) + 1]);
   }
 }
 
+template <int D, int W, bool BF16, bool SYM>
+__device__ __forceinline__ void index_tile(int t, const SlabOps<D> &A, const Ops<D> &uh, const Ops<D> &ul,
+                                           const float (&yscale)[Geo<D>::NT], IndexState<D, W> &S, Ops<D> &bh,
+                                           Ops<D> &bl) {
+  v4f acc[Geo<D>::NT];
+  rot_tile<D, BF16>(A, uh, ul, acc);
+  index_vals<D, W, SYM>(t, acc, yscale, S, bh, bl);
+}
+
 // Word group wl of the coordinates: its tiles (8, or 4 for a trailing group)
 // from the last down, so the bits arrive most significant first.  `group`
 // points at this lane's bytes of the group's first slab.
-template <int D, int W, bool BF16>
+template <int D, int W, bool BF16, bool SYM>
 __device__ __forceinline__ void index_group(int wl, const uint8_t *group, int g, const Ops<D> &uh, const Ops<D> &ul,
                                             const float (&yscale)[Geo<D>::NT], IndexState<D, W> &S,
                                             uint32_t (&cw)[W][Geo<D>::NT][Geo<D>::WPL], Ops<D> &bh, Ops<D> &bl) {
@@ -416,8 +515,9 @@ __device__ __forceinline__ void index_group(int wl, const uint8_t *group, int g,
 #pragma unroll
   for (int j = cnt - 1; j >= 0; --j) {
     if (j > 0) fetch_slab<D>(A[(j - 1) & 1], group + (j - 1) * Geo<D>::SLAB);
-    index_tile<D, W, BF16>(8 * wl + j, A[j & 1], uh, ul, yscale, S, bh, bl);
+    index_tile<D, W, BF16, SYM>(8 * wl + j, A[j & 1], uh, ul, yscale, S, bh, bl);
   }
+  finish_words<D, W, SYM>(S, cnt == 8 ? 0xffffffffu : 0xffffu);
 #pragma unroll
   for (int p = 0; p < W; ++p)
 #pragma unroll
@@ -595,21 +695,16 @@ __device__ __forceinline__ void store_signs(const KeyJob &job, const v4f (&z)[TM
 // after the two coordinate tiles of that k-step are rotated and indexed, so
 // matrix products and vector work interleave; only one k-step of the
 // residual operand is ever live.
-template <int D, int W, bool BF16, int TMS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quantize_keys_resident_kernel(
-    KeyJob job, int64_t n_tiles) {
+template <int D, int W, bool BF16, int TMS, bool SYM>
+__device__ __forceinline__ void resident_body(const KeyJob &job, int64_t n_tiles, uint8_t *smem) {
   using Gm = Geo<D>;
   constexpr int NT = Gm::NT;
   constexpr int KS = Gm::KS;
   constexpr bool THREE = W > 0 || !BF16;   // the sketch's B operand has a low part
-  extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   constexpr int pi_slabs = W > 0 ? Gm::TD : 0;
-  copy_to_lds(job.ops, smem, (pi_slabs + TMS) * Gm::SLAB, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   const uint8_t *pi_lds = smem + 16 * lane;
   const uint8_t *sk_lds = smem + pi_slabs * Gm::SLAB + 16 * lane;
 
@@ -618,30 +713,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   if (tile >= n_tiles) return;
   IndexState<D, W> S;
   if constexpr (W > 0) index_codebook<D, W>(job, S);
-  TileLoc<D> L = locate<D>(job, tile * Gm::KT, n);
   RawKeys<D, BF16> R;
-  load_keys<D, BF16>(job, L, g, R);
+  load_keys<D, BF16>(job, locate<D>(job, tile * Gm::KT, n), g, R);
   for (; tile < n_tiles; tile += stride) {
     float nrm[NT], yscale[NT];
     Op uh[NT][KS], ul[NT][KS];
     prepare_keys<D, BF16>(R, nrm, yscale, uh, ul);
-    // prefetch the next tile
-    const TileLoc<D> Lc = L;
-    if (tile + stride < n_tiles) {
-      L = locate<D>(job, (tile + stride) * Gm::KT, n);
-      load_keys<D, BF16>(job, L, g, R);
-    }
-    v4f z[TMS][NT];
-#pragma unroll
-    for (int tz = 0; tz < TMS; ++tz)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) z[tz][nt] = v4f{0.f, 0.f, 0.f, 0.f};
     uint32_t cw[W > 0 ? W : 1][NT][Gm::WPL];
     float gam[NT];
+    Ops<D> bh, bl;   // the sketch's B operand, every k-step
     if constexpr (W > 0) {
+      // 1. rotation and indices.  k-steps from the last down: tiles 2k+1, 2k
+      // keep the word bits most significant first.  Each tile's rotation is
+      // issued one tile ahead of its index work, so the matrix products of the
+      // next tile and the vector work of the current one are independent.
       index_begin<D, W>(S);
-      // k-steps from the last down: tiles 2k+1, 2k keep the word bits most
-      // significant first
+      if constexpr (SYM) index_thresholds<D, W>(S, yscale);
+      // The operands of each rotation tile are fetched from LDS one tile ahead.
+      SlabOps<D> A[2];
+      v4f acc_hi[NT], acc_lo[NT];
+      fetch_slab<D>(A[1], pi_lds + (2 * KS - 1) * Gm::SLAB);
+      fetch_slab<D>(A[0], pi_lds + (2 * KS - 2) * Gm::SLAB);
+      rot_tile<D, BF16>(A[1], uh, ul, acc_hi);
 #pragma unroll
       for (int k = KS - 1; k >= 0; --k) {
         const int t_hi = 2 * k + 1;
@@ -653,14 +746,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) S.wv[p][nt] = 0u;
         }
-        Ops<D> bh, bl;   // only k-step k is filled and used
-        SlabOps<D> A;
-        fetch_slab<D>(A, pi_lds + t_hi * Gm::SLAB);
-        index_tile<D, W, BF16>(t_hi, A, uh, ul, yscale, S, bh, bl);
-        fetch_slab<D>(A, pi_lds + (t_hi - 1) * Gm::SLAB);
-        index_tile<D, W, BF16>(t_hi - 1, A, uh, ul, yscale, S, bh, bl);
+        rot_tile<D, BF16>(A[0], uh, ul, acc_lo);                      // tile t_hi - 1
+        if (k > 0) fetch_slab<D>(A[1], pi_lds + (t_hi - 2) * Gm::SLAB);
+        index_vals<D, W, SYM>(t_hi, acc_hi, yscale, S, bh, bl);
+        if (k > 0) {
+          rot_tile<D, BF16>(A[1], uh, ul, acc_hi);                    // tile t_hi - 2
+          fetch_slab<D>(A[0], pi_lds + (t_hi - 3) * Gm::SLAB);
+        }
+        index_vals<D, W, SYM>(t_hi - 1, acc_lo, yscale, S, bh, bl);
         if (((t_hi - 1) & 7) == 0) {
           // bottom tile of word group wl: the words are complete
+          finish_words<D, W, SYM>(S, wl == Gm::FD ? 0xffffu : 0xffffffffu);
 #pragma unroll
           for (int p = 0; p < W; ++p)
 #pragma unroll
@@ -677,49 +773,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
               cw[p][nt][wl] = v;
             }
         }
-        Op kh[NT], kl[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          kh[nt] = bh[nt][k];
-          kl[nt] = bl[nt][k];
-        }
-#pragma unroll
-        for (int tz = 0; tz < TMS; ++tz) sketch_kstep<D, THREE>(z[tz], sk_lds + tz * Gm::SLAB, k, kh, kl);
       }
       index_end<D, W>(S, nrm, gam);
     } else {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) gam[nt] = 0.0f;
-#pragma unroll
-      for (int k = KS - 1; k >= 0; --k) {
-        Op kh[NT], kl[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          kh[nt] = uh[nt][k];
-          kl[nt] = ul[nt][k];
-        }
-#pragma unroll
-        for (int tz = 0; tz < TMS; ++tz) sketch_kstep<D, THREE>(z[tz], sk_lds + tz * Gm::SLAB, k, kh, kl);
-      }
+      key_operand_as_sketch_input<D>(uh, ul, bh, bl, gam);
     }
-    store_signs<D, TMS>(job, z, g, nrm, Lc);
+    // 2. the sketch, slab by slab (sign words stored as their groups complete),
+    // while the next tile's keys stream in
+    if (tile + stride < n_tiles) load_keys<D, BF16>(job, locate<D>(job, (tile + stride) * Gm::KT, n), g, R);
+    const TileLoc<D> Lc = locate<D>(job, tile * Gm::KT, n);
+    uint32_t sw[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) sw[nt] = 0u;
+    SlabOps<D> As[2];
+    fetch_slab<D>(As[0], sk_lds);
+#pragma unroll
+    for (int tz = 0; tz < TMS; ++tz) {
+      if (tz + 1 < TMS) fetch_slab<D>(As[(tz + 1) & 1], sk_lds + (tz + 1) * Gm::SLAB);
+      sketch_slab<D, THREE>(job, As[tz & 1], tz, TMS / 8, g, bh, bl, nrm, Lc, sw);
+    }
     store_codes_norms<D, W>(job, Lc, g, cw, nrm, gam);
   }
+}
+
+template <int D, int W, bool BF16, int TMS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quantize_keys_resident_kernel(
+    KeyJob job, int64_t n_tiles) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int pi_slabs = W > 0 ? Geo<D>::TD : 0;
+  copy_to_lds(job.ops, smem, (pi_slabs + TMS) * Geo<D>::SLAB, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (codebook_symmetric<W>(job)) resident_body<D, W, BF16, TMS, W != 0>(job, n_tiles, smem);
+  else resident_body<D, W, BF16, TMS, false>(job, n_tiles, smem);
 }
 
 // ---- streamed operands (sets larger than LDS): a block quantises one tile
 // of 8 x 32 (d = 256: 8 x 16) keys.  The rotation slabs come through LDS one
 // word group (8 slabs, at most 128 KiB) at a time, the sketch slabs in
 // double-buffered chunks of 2 or 4 slabs.
-template <int D, int W, bool BF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quantize_keys_stream_kernel(
-    KeyJob job) {
+template <int D, int W, bool BF16, bool SYM>
+__device__ __forceinline__ void stream_body(const KeyJob &job, uint8_t *smem) {
   using Gm = Geo<D>;
   constexpr int NT = Gm::NT;
   constexpr bool THREE = W > 0 || !BF16;
   constexpr int CH = chunk_slabs(D);
   constexpr int CHUNK = CH * Gm::SLAB;
-  extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -742,6 +843,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     IndexState<D, W> S;
     index_codebook<D, W>(job, S);
     index_begin<D, W>(S);
+    if constexpr (SYM) index_thresholds<D, W>(S, yscale);
 #pragma unroll
     for (int wl = 0; wl < Gm::WPL; ++wl) {
       if (wl > 0) {
@@ -751,7 +853,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      index_group<D, W, BF16>(wl, smem + 16 * lane, g, uh, ul, yscale, S, cw, bh, bl);
+      index_group<D, W, BF16, SYM>(wl, smem + 16 * lane, g, uh, ul, yscale, S, cw, bh, bl);
     }
     index_end<D, W>(S, nrm, gam);
     __syncthreads();   // every wave is done with the rotation slabs
@@ -781,6 +883,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
   store_codes_norms<D, W>(job, L, g, cw, nrm, gam);
+}
+
+template <int D, int W, bool BF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quantize_keys_stream_kernel(
+    KeyJob job) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  if (codebook_symmetric<W>(job)) stream_body<D, W, BF16, W != 0>(job, smem);
+  else stream_body<D, W, BF16, false>(job, smem);
 }
 
 constexpr size_t kLdsMax = 160 * 1024;
