@@ -33,8 +33,9 @@ DEFAULT_WORKLOAD = "llama2_7b_layer_mha32_t32k"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "i8": 5000.0, "fp32": 157.3}
 KERNEL_SOURCES = {
-    "decode": ["decode_mfma.hip", "decode.hip"],
-    "quantize_keys": ["quant_keys_mfma.hip", "query.hip"],
+    "decode": ["decode_fast.h", "decode_launch.hip", "decode_fast_d64.hip", "decode_fast_d128.hip",
+               "decode_fast_d256.hip", "decode.hip"],
+    "quantize_keys": ["quant_keys_mfma.hip"],
     "quantize_values": ["quant_values.hip"],
     "prepare_query": ["query.hip"],
 }
@@ -104,7 +105,9 @@ class Path:
         self.x = make_inputs(w, layer)
         dev = torch.device("cuda:0")
         self.cache = aqkv.Cache.allocate(self.cfg, w.n_slots, w.context)
-        self.kws = torch.empty(max(aqkv.quantize_keys_workspace_bytes(self.cfg), 256), dtype=torch.uint8, device=dev)
+        # the layer's key operands (Pi and S Pi^T as matrix-core operands) are built once per layer,
+        # as a serving loop would; every step quantises against them
+        self.kws = aqkv.prepare_key_operands(self.cfg, self.layer, device=dev)
         self.dws = torch.empty(aqkv.decode_workspace_bytes(self.cfg, w.batch, w.n_q_heads, w.n_kv_heads, w.context),
                                dtype=torch.uint8, device=dev)
         self.q_rot = (torch.empty((w.batch, w.n_q_heads, w.head_dim), device=dev) if w.mse_bits > 0 else None)
@@ -113,7 +116,10 @@ class Path:
         self.scores = (torch.empty((w.batch, w.n_q_heads, w.context), device=dev) if w.scores else None)
 
     def quantize_keys(self):
-        self.aqkv.quantize_keys(self.cfg, self.layer, self.x["k"], self.cache, 0, self.kws)
+        self.aqkv.quantize_keys_prepared(self.cfg, self.layer, self.x["k"], self.cache, self.kws)
+
+    def prepare_key_operands(self):
+        self.aqkv.prepare_key_operands(self.cfg, self.layer, self.kws)
 
     def quantize_values(self):
         self.aqkv.quantize_values(self.cfg, self.x["v"], self.cache, 0)
@@ -153,7 +159,7 @@ def time_calls(path, reps: int) -> dict:
     """Average duration of each call, HIP events on the launch stream."""
     import torch
     stream = torch.cuda.current_stream()
-    names = ["quantize_keys", "quantize_values", "prepare_query", "decode"]
+    names = ["quantize_keys", "quantize_values", "prepare_query", "decode", "prepare_key_operands"]
     ev = {n: [] for n in names}
     for _ in range(reps):
         for n in names:
@@ -242,6 +248,57 @@ def cpu_baseline(w, layer: int, budget_s: float = 20.0) -> dict:
                       f"numpy BLAS threads = {threads}, elementwise numpy single-threaded"}
 
 
+# kernels of each call, as rocprofv3 names them (substring match)
+KERNEL_NAMES = {
+    "decode": ["decode_fast_kernel", "combine_kernel", "decode_kernel"],
+    "quantize_keys": ["quantize_keys_resident_kernel", "quantize_keys_stream_kernel"],
+    "quantize_values": ["quantize_values_kernel"],
+}
+
+
+def write_counters(fetch_csv: str, write_csv: str, out: str) -> dict:
+    """profiles/counters.json from two rocprofv3 --pmc passes (FETCH_SIZE, then
+    WRITE_SIZE, both in KiB per dispatch) over `bench.py --calibrate-copy`: each
+    counter is scaled by what it reads for the plain 1 GiB device copy (1 GiB
+    fetched and 1 GiB written), and each call's HBM bytes per launch are the sum
+    over its kernels of the mean per dispatch."""
+    import collections
+    import csv
+
+    def means(path, counter):
+        acc = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return acc
+
+    fetch, write = means(fetch_csv, "FETCH_SIZE"), means(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    copy_f = [v for k, vs in fetch.items() if "copyBuffer" in k for v in vs if v > 0.5 * gib_kib]
+    copy_w = [v for k, vs in write.items() if "copyBuffer" in k for v in vs if v > 0.5 * gib_kib]
+    if not copy_f or not copy_w:
+        raise SystemExit("no 1 GiB copy dispatch in the counter files (run bench.py with --calibrate-copy)")
+    f_fetch = gib_kib / float(np.mean(copy_f))
+    f_write = gib_kib / float(np.mean(copy_w))
+    rec = {"calibration": {"copy_bytes": 1 << 30, "fetch_kib_read": float(np.mean(copy_f)),
+                           "write_kib_read": float(np.mean(copy_w)), "fetch_factor": f_fetch,
+                           "write_factor": f_write},
+           "kernels": {}}
+    for call, subs in KERNEL_NAMES.items():
+        kb_f = sum(float(np.mean(v)) for k, v in fetch.items() if any(x in k for x in subs))
+        kb_w = sum(float(np.mean(v)) for k, v in write.items() if any(x in k for x in subs))
+        if kb_f == 0 and kb_w == 0:
+            continue
+        rec["kernels"][call] = {"source_hash": source_hash(call),
+                                "fetch_bytes_per_launch": kb_f * 1024 * f_fetch,
+                                "write_bytes_per_launch": kb_w * 1024 * f_write,
+                                "hbm_bytes_per_launch": kb_f * 1024 * f_fetch + kb_w * 1024 * f_write}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,7 +310,14 @@ def main():
     ap.add_argument("--no-detail", action="store_true", help="skip per-call timing (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: write profiles/counters.json from two rocprofv3 counter_collection.csv "
+                         "files (FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy run")
     args = ap.parse_args()
+    if args.write_counters:
+        print(json.dumps(write_counters(*args.write_counters, os.path.join(ROOT, "profiles", "counters.json")),
+                         indent=1))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -322,6 +386,7 @@ def main():
             "keys_GBps": qk_bytes / (per["quantize_keys"] / 1e3) / 1e9,
             "values_GBps": qv_bytes / (per["quantize_values"] / 1e3) / 1e9}
         rec["prepare_query_ms"] = per["prepare_query"]
+        rec["prepare_key_operands_ms_once_per_layer"] = per["prepare_key_operands"]
         dominant = max(["decode", "quantize_keys", "quantize_values"], key=lambda n: per[n])
         if dominant == "decode":
             ach = dec_bytes / (per["decode"] / 1e3) / 1e9

@@ -186,6 +186,25 @@ aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer,
                                const aqkv_cache *cache, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/* The per-layer half of aqkv_quantize_keys, for callers that quantise many
+ * chunks with one layer (a decode loop appending one token per step): writes
+ * into workspace (dev, 256-byte aligned, aqkv_quantize_keys_workspace_bytes
+ * bytes) the matrix-core operands built from layer->rotation and
+ * layer->sketch (the product S Pi^T included).  The workspace then stays valid
+ * for aqkv_quantize_keys_prepared with the same cfg for as long as the caller
+ * leaves it and the layer's rotation and sketch unchanged. */
+aqkv_status aqkv_prepare_key_operands(const aqkv_config *cfg, const aqkv_layer *layer, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
+/* aqkv_quantize_keys on a workspace prepared by aqkv_prepare_key_operands (same
+ * cfg and layer): the same results, without the operand pass.  layer supplies
+ * the codebook (centroids, boundaries); its rotation and sketch are not read.
+ * The workspace is only read. */
+aqkv_status aqkv_quantize_keys_prepared(const aqkv_config *cfg, const aqkv_layer *layer,
+                                        const aqkv_kv_view *k, int64_t token_offset,
+                                        const aqkv_cache *cache, const void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
 /* Value quantisation (TurboQuant component table and §七: conventional
  * min-max grouped quantisation with bit packing).  Per token, per group of
  * value_group contiguous channels: min, scale = (max - min) / (2^vb - 1),

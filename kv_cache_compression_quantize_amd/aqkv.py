@@ -83,6 +83,9 @@ _SIGS = {
     "aqkv_decode_workspace_bytes": (C.c_size_t, [_P(Config), C.c_int32, C.c_int32, C.c_int32, C.c_int64]),
     "aqkv_quantize_keys": (C.c_int, [_P(Config), _P(LayerParams), _P(KvView), C.c_int64, _P(CacheDesc),
                                      C.c_void_p, C.c_size_t, C.c_void_p]),
+    "aqkv_prepare_key_operands": (C.c_int, [_P(Config), _P(LayerParams), C.c_void_p, C.c_size_t, C.c_void_p]),
+    "aqkv_quantize_keys_prepared": (C.c_int, [_P(Config), _P(LayerParams), _P(KvView), C.c_int64, _P(CacheDesc),
+                                              C.c_void_p, C.c_size_t, C.c_void_p]),
     "aqkv_quantize_values": (C.c_int, [_P(Config), _P(KvView), C.c_int64, _P(CacheDesc), C.c_void_p]),
     "aqkv_prepare_query": (C.c_int, [_P(Config), _P(LayerParams), C.c_void_p, C.c_int, C.c_int64,
                                      C.c_void_p, C.c_void_p, C.c_void_p]),
@@ -292,6 +295,28 @@ def quantize_keys(cfg: Config, layer: Layer, k, cache: Cache, token_offset: int 
                                   C.byref(cache.desc()), _ptr(workspace),
                                   workspace.numel() if workspace is not None else 0, _stream(stream))
     _check(st, "aqkv_quantize_keys")
+
+
+def prepare_key_operands(cfg: Config, layer: Layer, workspace=None, device=None, stream=None):
+    """The layer's key-quantisation operands into `workspace` (allocated when None); pass it to
+    quantize_keys_prepared."""
+    ws_bytes = quantize_keys_workspace_bytes(cfg)
+    if workspace is None:
+        import torch
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device or "cuda")
+    st = lib().aqkv_prepare_key_operands(C.byref(cfg), C.byref(layer.desc()), _ptr(workspace), workspace.numel(),
+                                         _stream(stream))
+    _check(st, "aqkv_prepare_key_operands")
+    return workspace
+
+
+def quantize_keys_prepared(cfg: Config, layer: Layer, k, cache: Cache, workspace, token_offset: int = 0,
+                           stream=None):
+    v = kv_view(k)
+    st = lib().aqkv_quantize_keys_prepared(C.byref(cfg), C.byref(layer.desc()), C.byref(v), token_offset,
+                                           C.byref(cache.desc()), _ptr(workspace), workspace.numel(),
+                                           _stream(stream))
+    _check(st, "aqkv_quantize_keys_prepared")
 
 
 def quantize_values(cfg: Config, v, cache: Cache, token_offset: int = 0, stream=None):

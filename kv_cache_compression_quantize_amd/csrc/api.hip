@@ -151,9 +151,32 @@ size_t aqkv_decode_workspace_bytes(const aqkv_config *cfg, int32_t batch, int32_
       .total_bytes;
 }
 
-aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_kv_view *k,
-                               int64_t token_offset, const aqkv_cache *cache, void *workspace,
-                               size_t workspace_bytes, void *stream) {
+// The layer's matrix-core operands into the workspace (checked arguments)
+static aqkv_status key_operands(const aqkv_config *cfg, const aqkv_layer *layer, void *workspace,
+                                size_t workspace_bytes, hipStream_t s) {
+  const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
+  aqkv_status st;
+  if (!layer) return AQKV_ERR_NULL;
+  if ((st = check_plane(layer->sketch)) != AQKV_OK) return st;
+  if (w > 0 && (st = check_plane(layer->rotation)) != AQKV_OK) return st;
+  if (!workspace || workspace_bytes < key_workspace_bytes(d, w, m)) return AQKV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return AQKV_ERR_ALIGN;
+  return launch_key_operands(layer->rotation, layer->sketch, static_cast<uint8_t *>(workspace), d, w, m, s) ==
+                 hipSuccess
+             ? AQKV_OK
+             : AQKV_ERR_HIP;
+}
+
+aqkv_status aqkv_prepare_key_operands(const aqkv_config *cfg, const aqkv_layer *layer, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+  aqkv_status st = check_config(cfg);
+  if (st != AQKV_OK) return st;
+  return key_operands(cfg, layer, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+static aqkv_status quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_kv_view *k,
+                                 int64_t token_offset, const aqkv_cache *cache, void *workspace,
+                                 size_t workspace_bytes, void *stream, bool prepare) {
   aqkv_status st = check_config(cfg);
   if (st != AQKV_OK) return st;
   if (!layer) return AQKV_ERR_NULL;
@@ -163,11 +186,11 @@ aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, 
   if (k->batch * k->heads != cache->n_slots) return AQKV_ERR_SHAPE;
   if (token_offset < 0) return AQKV_ERR_SHAPE;
   if (token_offset + k->tokens > cache->capacity) return AQKV_ERR_CAPACITY;
-  if ((st = check_plane(layer->sketch)) != AQKV_OK) return st;
-  if (w > 0) {
-    if ((st = check_plane(layer->rotation)) != AQKV_OK) return st;
-    if (!layer->centroids || !layer->boundaries) return AQKV_ERR_NULL;
+  if (prepare) {
+    if ((st = check_plane(layer->sketch)) != AQKV_OK) return st;
+    if (w > 0 && (st = check_plane(layer->rotation)) != AQKV_OK) return st;
   }
+  if (w > 0 && (!layer->centroids || !layer->boundaries)) return AQKV_ERR_NULL;
   if ((st = check_blocks(cache)) != AQKV_OK) return st;
   const size_t need = key_workspace_bytes(d, w, m);
   if (!workspace || workspace_bytes < need) return AQKV_ERR_WORKSPACE;
@@ -176,8 +199,7 @@ aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t *ops = static_cast<uint8_t *>(workspace);
-  hipError_t e = launch_key_operands(layer->rotation, layer->sketch, ops, d, w, m, s);
-  if (e != hipSuccess) return AQKV_ERR_HIP;
+  if (prepare && (st = key_operands(cfg, layer, workspace, workspace_bytes, s)) != AQKV_OK) return st;
   KeyJob job{};
   job.k = k->data;
   job.dtype = k->dtype;
@@ -202,6 +224,19 @@ aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, 
   job.rnorm = cache->blocks + L.off[F_RNORM];
   job.rec = L.rec;
   return hip_status(launch_quantize_keys_mfma(job, s));
+}
+
+aqkv_status aqkv_quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_kv_view *k,
+                               int64_t token_offset, const aqkv_cache *cache, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+  return quantize_keys(cfg, layer, k, token_offset, cache, workspace, workspace_bytes, stream, true);
+}
+
+aqkv_status aqkv_quantize_keys_prepared(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_kv_view *k,
+                                        int64_t token_offset, const aqkv_cache *cache, const void *workspace,
+                                        size_t workspace_bytes, void *stream) {
+  return quantize_keys(cfg, layer, k, token_offset, cache, const_cast<void *>(workspace), workspace_bytes, stream,
+                       false);
 }
 
 aqkv_status aqkv_quantize_values(const aqkv_config *cfg, const aqkv_kv_view *v, int64_t token_offset,

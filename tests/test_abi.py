@@ -117,6 +117,29 @@ def test_quantize_keys_validation_codes():
     assert call(view=_view(tokens=0)) == 0
 
 
+def test_prepared_key_entry_points_validation_codes():
+    lib = aqkv.lib()
+    cfg = aqkv.config(128, 2, 128)
+    layer = aqkv.LayerParams(FAKE, FAKE, FAKE, FAKE)
+    ws = aqkv.quantize_keys_workspace_bytes(cfg)
+    assert lib.aqkv_prepare_key_operands(None, C.byref(layer), FAKE, ws, None) == -1
+    assert lib.aqkv_prepare_key_operands(C.byref(cfg), None, FAKE, ws, None) == -1
+    assert lib.aqkv_prepare_key_operands(C.byref(cfg), C.byref(layer), FAKE, ws - 1, None) == -5
+    assert lib.aqkv_prepare_key_operands(C.byref(cfg), C.byref(layer), FAKE + 16, ws, None) == -3
+    assert lib.aqkv_prepare_key_operands(C.byref(cfg), C.byref(aqkv.LayerParams(FAKE, None, FAKE, FAKE)),
+                                         FAKE, ws, None) == -1
+
+    def call(view=None, cache=None, wsb=ws, layer=layer):
+        return lib.aqkv_quantize_keys_prepared(C.byref(cfg), C.byref(layer), C.byref(view or _view()), 0,
+                                               C.byref(cache or _cache()), FAKE, wsb, None)
+
+    assert call(wsb=16) == -5
+    assert call(cache=_cache(n_slots=3)) == -2
+    assert call(layer=aqkv.LayerParams(FAKE, FAKE, None, FAKE)) == -1   # the codebook is still read
+    # rotation and sketch are not read: NULL passes validation (zero tokens: nothing to launch)
+    assert call(view=_view(tokens=0), layer=aqkv.LayerParams(None, None, FAKE, FAKE)) == 0
+
+
 def test_quantize_values_and_query_validation_codes():
     lib = aqkv.lib()
     cfg = aqkv.config(128, 2, 128)

@@ -125,6 +125,30 @@ def test_quantize_values_bit_exact(d, vb, dtype):
         np.testing.assert_array_equal(gpu["vmin"].view(np.uint32), vm.view(np.uint32))
 
 
+@pytest.mark.parametrize("d,w,m", [(128, 2, 128), (256, 3, 256), (128, 0, 192)])
+def test_prepared_key_operands_match_one_call(d, w, m):
+    # one operand pass, then appends of 1, 2, 37 and the rest of the tokens: the same
+    # cache bytes as one self-contained call
+    torch, dev = torch_dev()
+    say("prepared key operands", d, w, m)
+    B, H, T = 2, 2, 300
+    k = _as_dtype(_kv(B, H, T, d, seed=11 + d + w), "bf16")
+    hl = host_layer(d, w, m)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    kd = to_device_kv(k, "bf16")
+    one = aqkv.Cache.allocate(cfg, B * H, T)
+    one.blocks.zero_()
+    aqkv.quantize_keys(cfg, layer, kd, one)
+    parts = aqkv.Cache.allocate(cfg, B * H, T)
+    parts.blocks.zero_()
+    ws = aqkv.prepare_key_operands(cfg, layer, device=dev)
+    for a, e in ((0, 1), (1, 3), (3, 40), (40, T)):
+        aqkv.quantize_keys_prepared(cfg, layer, kd[:, :, a:e], parts, ws, token_offset=a)
+    torch.cuda.synchronize()
+    assert torch.equal(one.blocks, parts.blocks)
+
+
 def test_chunked_append_matches_one_call():
     torch, dev = torch_dev()
     say("chunked append")
