@@ -114,6 +114,7 @@ class Path:
         self.q_sk = torch.empty((w.batch, w.n_q_heads, self.cfg.sketch_dim), device=dev)
         self.out = torch.empty((w.batch, w.n_q_heads, w.head_dim), device=dev)
         self.scores = (torch.empty((w.batch, w.n_q_heads, w.context), device=dev) if w.scores else None)
+        self.side = torch.cuda.Stream(device=dev)   # default priority
 
     def quantize_keys(self):
         self.aqkv.quantize_keys_prepared(self.cfg, self.layer, self.x["k"], self.cache, self.kws)
@@ -133,9 +134,18 @@ class Path:
                                    w.context, self.q_rot, self.q_sk, None, self.scores, self.out, self.dws)
 
     def step(self):
+        # values and the query do not depend on the keys: they run on a second stream
+        # beside the (compute-bound) key quantiser; decode waits for both
+        import torch
+        cur = torch.cuda.current_stream()
+        self.side.wait_stream(cur)
+        # the key kernel first: its resident blocks (one per compute unit) take their
+        # place before the value blocks fill what is left
         self.quantize_keys()
-        self.quantize_values()
-        self.prepare_query()
+        with torch.cuda.stream(self.side):
+            self.quantize_values()
+            self.prepare_query()
+        cur.wait_stream(self.side)
         self.decode()
 
 
@@ -310,6 +320,9 @@ def main():
     ap.add_argument("--no-detail", action="store_true", help="skip per-call timing (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step captured once as a HIP graph instead of launching each call from Python "
+                         "(measured no faster for these kernel sizes)")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: write profiles/counters.json from two rocprofv3 counter_collection.csv "
                          "files (FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy run")
@@ -335,10 +348,22 @@ def main():
     for _ in range(args.warmup):
         path.step()
     torch.cuda.synchronize()
+    run = path.step
+    if args.graph:
+        # the four calls captured once as a HIP graph: every replay launches the same kernels
+        # on the same buffers, without the per-call host overhead between them
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            path.step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(max(args.warmup, 1)):
+            run()
+        torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        path.step()
+        run()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed / max(args.steps, 1) * 1e3
@@ -359,7 +384,8 @@ def main():
            "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
                       "context": w.context, "head_dim": w.head_dim, "mse_bits": w.mse_bits,
                       "sketch_dim": w.sketch_dim(layer), "value_bits": w.value_bits,
-                      "value_group": w.value_group, "kv_dtype": w.dtype, "recipe": w.recipe}}
+                      "value_group": w.value_group, "kv_dtype": w.dtype, "recipe": w.recipe,
+                      "launch": "hip_graph" if args.graph else "eager"}}
     if not args.no_detail:
         log("per-call timing")
         per = time_calls(path, reps=max(5, args.steps))
