@@ -59,3 +59,34 @@ def decode_slot(q, key_rows, value_rows, rotation, sketch, centroids, w: int,
     s = scores(q, key_rows, rotation, sketch, centroids, w)
     v_hat = dequantize_values(*value_rows, group=group)
     return s, softmax_attention(s, v_hat, softmax_scale)
+
+
+def decode_slot_window(q, key_rows, value_rows, k_win, v_win, rotation, sketch, centroids, w: int,
+                       softmax_scale=None, group: int = 32):
+    """Decode attention over the compressed history and a recent-token window.
+
+    TurboQuant article §六: the most recent tokens are kept at full precision in
+    a ring buffer and the compressed path serves the older history; attention
+    covers both.  The window's scores are the exact <q, k> and its values are
+    the stored ones; the history's are the estimator and the dequantised
+    values; one softmax runs over all of them (the order of tokens does not
+    matter).  key_rows / value_rows may hold 0 tokens (no history yet) and the
+    window may be empty.  Returns (window scores [G, W], out [G, d])."""
+    q = np.asarray(q, dtype=np.float64)
+    G, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / np.sqrt(d)
+    k_win = np.asarray(k_win, dtype=np.float64).reshape(-1, d)
+    v_win = np.asarray(v_win, dtype=np.float64).reshape(-1, d)
+    s_win = q @ k_win.T
+    n_hist = len(key_rows[2])
+    if n_hist > 0:
+        s_hist = scores(q, key_rows, rotation, sketch, centroids, w)
+        v_hist = dequantize_values(*value_rows, group=group)
+    else:
+        s_hist, v_hist = np.zeros((G, 0)), np.zeros((0, d))
+    s = np.concatenate([s_hist, s_win], axis=1)
+    v = np.concatenate([v_hist, v_win], axis=0)
+    if s.shape[1] == 0:
+        return s_win, np.zeros((G, d))
+    return s_win, softmax_attention(s, v, softmax_scale)

@@ -140,3 +140,55 @@ def test_decode_slot_gqa_shapes():
     vr = values.quantize_values(v)
     sc, out = attention.decode_slot(q, (qk.idx, qk.bits, qk.norm, qk.rnorm), vr, pi, s, c, w)
     assert sc.shape == (4, 33) and out.shape == (4, d)
+
+
+def _window_case(seed, n_hist, n_win, G=4, d=128, w=2):
+    pi, s, c, t = _params(d, w, d)
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n_hist, d))
+    v = rng.standard_normal((n_hist, d)).astype(np.float32)
+    kw = rng.standard_normal((n_win, d))
+    vw = rng.standard_normal((n_win, d))
+    q = rng.standard_normal((G, d))
+    qk = keys.quantize_keys(x, pi, s, c, t, w)
+    vr = values.quantize_values(v)
+    return q, (qk.idx, qk.bits, qk.norm, qk.rnorm), vr, kw, vw, (pi, s, c, w)
+
+
+def test_window_only_is_exact_attention():
+    # no compressed history: plain softmax attention over the window (library softmax)
+    q, kr, vr, kw, vw, (pi, s, c, w) = _window_case(7, 0, 21)
+    sw, out = attention.decode_slot_window(q, kr, vr, kw, vw, pi, s, c, w)
+    np.testing.assert_allclose(sw, q @ kw.T, rtol=1e-13)
+    ref = special.softmax(q @ kw.T / np.sqrt(q.shape[1]), axis=1) @ vw
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_window_merges_with_history_by_partition_functions():
+    # history and window attended separately and merged with their partition
+    # functions Z = sum exp(logits) (the split-merge identity) give the one-softmax result
+    q, kr, vr, kw, vw, (pi, s, c, w) = _window_case(8, 77, 19)
+    scale = 1.0 / np.sqrt(q.shape[1])
+    _, out = attention.decode_slot_window(q, kr, vr, kw, vw, pi, s, c, w)
+    s_hist, out_hist = attention.decode_slot(q, kr, vr, pi, s, c, w)
+    z_hist = special.logsumexp(s_hist * scale, axis=1)
+    z_win = special.logsumexp(q @ kw.T * scale, axis=1)
+    out_win = special.softmax(q @ kw.T * scale, axis=1) @ vw
+    a = 1.0 / (1.0 + np.exp(z_win - z_hist))
+    ref = a[:, None] * out_hist + (1.0 - a)[:, None] * out_win
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_window_empty_and_order():
+    q, kr, vr, kw, vw, (pi, s, c, w) = _window_case(9, 40, 12)
+    # an empty window leaves the history-only decode
+    _, out0 = attention.decode_slot_window(q, kr, vr, kw[:0], vw[:0], pi, s, c, w)
+    np.testing.assert_allclose(out0, attention.decode_slot(q, kr, vr, pi, s, c, w)[1], rtol=1e-13)
+    # a ring buffer holds the window in any rotation: the result does not depend on it
+    _, out1 = attention.decode_slot_window(q, kr, vr, kw, vw, pi, s, c, w)
+    _, out2 = attention.decode_slot_window(q, kr, vr, np.roll(kw, 5, 0), np.roll(vw, 5, 0), pi, s, c, w)
+    np.testing.assert_allclose(out1, out2, rtol=1e-12, atol=1e-14)
+    # nothing at all: zeros
+    empty = (kr[0][:0], kr[1][:0], kr[2][:0], kr[3][:0])
+    _, out3 = attention.decode_slot_window(q, empty, tuple(a[:0] for a in vr), kw[:0], vw[:0], pi, s, c, w)
+    assert np.all(out3 == 0)
