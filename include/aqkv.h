@@ -241,6 +241,29 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
                                   const float *q_sketch, float softmax_scale, float *scores,
                                   float *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Decode attention over the compressed history and a recent-token window
+ * (TurboQuant §六: the latest tokens are kept at full precision in a ring
+ * buffer and only the older history goes through the compressed path; one
+ * softmax covers both).  Cache rows [0, context_len) of each slot are scored
+ * and weighted exactly as by aqkv_decode_attention; the n_window tokens of
+ * k_window / v_window ([batch][n_kv_heads][n_window][d] views, fp32 or bf16,
+ * both the same dtype and n_window, n_window <= 1024; the order of the tokens
+ * does not matter, so a ring buffer is passed as it is) get the exact logit
+ * <q, k> * softmax_scale (fp32 accumulation) and their own values.  q is the
+ * unrotated query [batch][n_q_heads][d] (dev fp32, contiguous); q_rot and
+ * q_sketch are its aqkv_prepare_query outputs.  scores, if not NULL, receives
+ * the compressed rows' estimates only ([batch][n_q_heads][context_len]).
+ * context_len == 0 (no history yet) attends the window alone; both empty
+ * writes out = 0.  Same workspace size and other rules as
+ * aqkv_decode_attention. */
+aqkv_status aqkv_decode_attention_window(const aqkv_config *cfg, const aqkv_layer *layer,
+                                         const aqkv_cache *cache, int32_t batch, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int64_t context_len, const float *q,
+                                         const float *q_rot, const float *q_sketch,
+                                         const aqkv_kv_view *k_window, const aqkv_kv_view *v_window,
+                                         float softmax_scale, float *scores, float *out, void *workspace,
+                                         size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

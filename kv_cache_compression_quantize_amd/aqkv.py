@@ -92,6 +92,10 @@ _SIGS = {
     "aqkv_decode_attention": (C.c_int, [_P(Config), _P(LayerParams), _P(CacheDesc), C.c_int32, C.c_int32,
                                         C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_float,
                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "aqkv_decode_attention_window": (C.c_int, [_P(Config), _P(LayerParams), _P(CacheDesc), C.c_int32, C.c_int32,
+                                               C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                               _P(KvView), _P(KvView), C.c_float, C.c_void_p, C.c_void_p,
+                                               C.c_void_p, C.c_size_t, C.c_void_p]),
 }
 
 _lib_handle = None
@@ -357,4 +361,29 @@ def decode_attention(cfg: Config, layer: Layer, cache: Cache, batch: int, n_q_he
                                      C.c_float(softmax_scale), _ptr(scores), _ptr(out), _ptr(workspace),
                                      workspace.numel(), _stream(stream))
     _check(st, "aqkv_decode_attention")
+    return out
+
+
+def decode_attention_window(cfg: Config, layer: Layer, cache: Cache, batch: int, n_q_heads: int, n_kv_heads: int,
+                            context_len: int, q, q_rot, q_sketch, k_window, v_window,
+                            softmax_scale: Optional[float] = None, scores=None, out=None, workspace=None,
+                            stream=None):
+    """Decode over cache rows [0, context_len) plus the recent-token window k_window / v_window
+    ([batch, n_kv_heads, n_window, d] tensors, any token order); q is the unrotated fp32 query."""
+    import torch
+    dev = q_sketch.device
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(np.sqrt(cfg.head_dim))
+    if out is None:
+        out = torch.empty((batch, n_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    ws_bytes = decode_workspace_bytes(cfg, batch, n_q_heads, n_kv_heads, context_len)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    kv, vv = kv_view(k_window), kv_view(v_window)
+    st = lib().aqkv_decode_attention_window(C.byref(cfg), C.byref(layer.desc()), C.byref(cache.desc()), batch,
+                                            n_q_heads, n_kv_heads, context_len, _ptr(q), _ptr(q_rot),
+                                            _ptr(q_sketch), C.byref(kv), C.byref(vv), C.c_float(softmax_scale),
+                                            _ptr(scores), _ptr(out), _ptr(workspace), workspace.numel(),
+                                            _stream(stream))
+    _check(st, "aqkv_decode_attention_window")
     return out

@@ -88,8 +88,9 @@ DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int6
   p.split_tokens = per_split * kGrain;
   p.n_split = static_cast<int>(grains > 0 ? (grains + per_split - 1) / per_split : 1);
   const size_t heads = static_cast<size_t>(n_slots) * g;
-  p.acc_bytes = round_up(heads * p.n_split * d * sizeof(float), 256);
-  p.ml_bytes = round_up(heads * p.n_split * 2 * sizeof(float), 256);
+  // one more partial per head than splits: room for a recent-token window's
+  p.acc_bytes = round_up(heads * (p.n_split + 1) * d * sizeof(float), 256);
+  p.ml_bytes = round_up(heads * (p.n_split + 1) * 2 * sizeof(float), 256);
   p.total_bytes = p.acc_bytes + p.ml_bytes;
   return p;
 }
@@ -299,11 +300,16 @@ aqkv_status aqkv_prepare_query(const aqkv_config *cfg, const aqkv_layer *layer, 
   return hip_status(launch_prepare_query(job, static_cast<hipStream_t>(stream)));
 }
 
-aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache,
-                                  int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t context_len,
-                                  const float *q_rot, const float *q_sketch, float softmax_scale,
-                                  float *scores, float *out, void *workspace, size_t workspace_bytes,
-                                  void *stream) {
+// The recent-token window of a decode call (all pointers already checked)
+struct WindowArgs {
+  const float *q;
+  const aqkv_kv_view *k, *v;
+};
+
+static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache, int32_t batch,
+                          int32_t n_q_heads, int32_t n_kv_heads, int64_t context_len, const float *q_rot,
+                          const float *q_sketch, float softmax_scale, float *scores, float *out, void *workspace,
+                          size_t workspace_bytes, void *stream, const WindowArgs *win) {
   aqkv_status st = check_config(cfg);
   if (st != AQKV_OK) return st;
   if (!layer) return AQKV_ERR_NULL;
@@ -318,11 +324,21 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
   if (!decode_supported(d, w, g, m, cfg->value_bits) && !decode_mfma_supported(d, w, g, m, cfg->value_bits))
     return AQKV_ERR_UNSUPPORTED;
+  if (win) {
+    if (!win->k || !win->v) return AQKV_ERR_NULL;
+    if ((st = check_view(win->k, d)) != AQKV_OK || (st = check_view(win->v, d)) != AQKV_OK) return st;
+    if (win->k->dtype != win->v->dtype) return AQKV_ERR_DTYPE;
+    if (win->k->batch != batch || win->v->batch != batch || win->k->heads != n_kv_heads ||
+        win->v->heads != n_kv_heads || win->k->tokens != win->v->tokens)
+      return AQKV_ERR_SHAPE;
+    if (win->k->tokens > kMaxWindow) return AQKV_ERR_UNSUPPORTED;
+  }
   if (batch == 0) return AQKV_OK;
   if (!out || !q_sketch) return AQKV_ERR_NULL;
   if (w > 0 && (!q_rot || !layer->centroids)) return AQKV_ERR_NULL;
+  if (win && !win->q) return AQKV_ERR_NULL;
   if (!aligned(out, 16) || !aligned(q_sketch, 16) || (q_rot && !aligned(q_rot, 16)) ||
-      (scores && !aligned(scores, 16)))
+      (scores && !aligned(scores, 16)) || (win && !aligned(win->q, 16)))
     return AQKV_ERR_ALIGN;
   if (context_len > 0 && (st = check_blocks(cache)) != AQKV_OK) return st;
   const DecodePlan plan = decode_plan(d, w, m, cfg->value_bits, cache->n_slots, g, context_len);
@@ -360,12 +376,60 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
   char *ws = static_cast<char *>(workspace);
   job.part_ml = reinterpret_cast<float *>(ws + plan.acc_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (plan.mfma) {
-    // the matrix-core decoder addresses a slot's records with 32-bit byte offsets
-    if (cache->capacity / kBlockRows * L.rec >= (int64_t(1) << 31)) return AQKV_ERR_UNSUPPORTED;
-    return hip_status(launch_decode_mfma(job, s));
+  // the matrix-core decoder addresses a slot's records with 32-bit byte offsets
+  if (plan.mfma && cache->capacity / kBlockRows * L.rec >= (int64_t(1) << 31)) return AQKV_ERR_UNSUPPORTED;
+  // with a window and no history yet, the window is the only partial
+  const bool history = !win || context_len > 0;
+  job.part_stride = history ? plan.n_split + (win ? 1 : 0) : 1;
+  if (history) {
+    const hipError_t e = plan.mfma ? launch_decode_mfma(job, s) : launch_decode(job, s);
+    if (e != hipSuccess) return AQKV_ERR_HIP;
   }
-  return hip_status(launch_decode(job, s));
+  if (win) {
+    WindowJob wj{};
+    wj.k = win->k->data;
+    wj.v = win->v->data;
+    wj.dtype = win->k->dtype;
+    wj.heads = n_kv_heads;
+    wj.k_bs = win->k->batch_stride;
+    wj.k_hs = win->k->head_stride;
+    wj.k_ts = win->k->token_stride;
+    wj.v_bs = win->v->batch_stride;
+    wj.v_hs = win->v->head_stride;
+    wj.v_ts = win->v->token_stride;
+    wj.n_window = static_cast<int>(win->k->tokens);
+    wj.q = win->q;
+    wj.d = d;
+    wj.g = g;
+    wj.n_slots = cache->n_slots;
+    wj.softmax_scale = softmax_scale;
+    wj.part_acc = job.part_acc;
+    wj.part_ml = job.part_ml;
+    wj.part_stride = job.part_stride;
+    wj.part_index = job.part_stride - 1;
+    if (launch_window_partial(wj, s) != hipSuccess) return AQKV_ERR_HIP;
+  }
+  return hip_status(launch_combine(job, s));
+}
+
+aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache,
+                                  int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t context_len,
+                                  const float *q_rot, const float *q_sketch, float softmax_scale,
+                                  float *scores, float *out, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+  return decode(cfg, layer, cache, batch, n_q_heads, n_kv_heads, context_len, q_rot, q_sketch, softmax_scale,
+                scores, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+aqkv_status aqkv_decode_attention_window(const aqkv_config *cfg, const aqkv_layer *layer,
+                                         const aqkv_cache *cache, int32_t batch, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int64_t context_len, const float *q,
+                                         const float *q_rot, const float *q_sketch, const aqkv_kv_view *k_window,
+                                         const aqkv_kv_view *v_window, float softmax_scale, float *scores,
+                                         float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  const WindowArgs win{q, k_window, v_window};
+  return decode(cfg, layer, cache, batch, n_q_heads, n_kv_heads, context_len, q_rot, q_sketch, softmax_scale,
+                scores, out, workspace, workspace_bytes, stream, &win);
 }
 
 }  // extern "C"

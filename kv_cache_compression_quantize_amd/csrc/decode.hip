@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
   }
 
   // partials
-  const int64_t pbase = static_cast<int64_t>(job.n_split);
+  const int64_t pbase = static_cast<int64_t>(job.part_stride);
 #pragma unroll
   for (int i = 0; i < kPairs; ++i) {
     const int pi = tid + i * kThreads;
@@ -224,15 +224,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
   }
 }
 
-// Merge the split partials of one query head: M = max_i m_i, weights
-// w_i = 2^(m_i - M) (0 for empty splits), out = sum_i w_i acc_i / sum_i w_i l_i.
+// Merge the part_stride partials of one query head (the splits, then the
+// recent-token window if there is one): M = max_i m_i, weights
+// w_i = 2^(m_i - M) (0 for empty parts), out = sum_i w_i acc_i / sum_i w_i l_i.
 // The weights go to LDS (1024 splits per pass); 256 / d threads share a channel,
 // each summing every (256 / d)-th split with independent loads in flight.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeJob job) {
   __shared__ float wts[1024];
   __shared__ float red[256];
   const int64_t head = blockIdx.x;
-  const int d = job.d, ns = job.n_split, tid = threadIdx.x;
+  const int d = job.d, ns = job.part_stride, tid = threadIdx.x;
   const float *ml = job.part_ml + head * ns * 2;
   const float *acc = job.part_acc + head * ns * d;
   // M over the non-empty splits
@@ -288,9 +289,7 @@ hipError_t launch_dwg(const DecodeJob &job, hipStream_t stream) {
   if (smem > 64 * 1024) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(job.n_split * job.n_slots));
   decode_kernel<D, W, G><<<grid, kThreads, smem, stream>>>(job);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_combine(job, stream);
+  return hipGetLastError();
 }
 
 template <int D, int W>

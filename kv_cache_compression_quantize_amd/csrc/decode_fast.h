@@ -693,7 +693,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
         O = fmaf(mrg[(wv * G + g) * D + j], f, O);
       }
     }
-    const int64_t ph = (head0 + g) * job.n_split + split;
+    const int64_t ph = (head0 + g) * job.part_stride + split;
     job.part_acc[ph * D + j] = O;
     if (j == 0) {
       job.part_ml[ph * 2 + 0] = M;

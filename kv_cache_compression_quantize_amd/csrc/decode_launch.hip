@@ -1,6 +1,6 @@
 // Matrix-core decode, host side: which shapes have a compiled kernel, how many
-// blocks of it a CU holds, and the launch (decode kernel for the head_dim, then
-// the split combine).
+// blocks of it a CU holds, and the launch of the decode kernel for the head_dim
+// (the caller then launches the split combine).
 #include <math.h>
 
 #include "decode_fast.h"
@@ -38,14 +38,11 @@ int decode_mfma_blocks_per_cu(int d, int w, int g, int m, int vb) {
 }
 
 hipError_t launch_decode_mfma(const DecodeJob &job, hipStream_t stream) {
-  hipError_t e;
   switch (job.d) {
-    case 64: e = launch_decode_fast_d64(job, stream); break;
-    case 128: e = launch_decode_fast_d128(job, stream); break;
-    default: e = launch_decode_fast_d256(job, stream); break;
+    case 64: return launch_decode_fast_d64(job, stream);
+    case 128: return launch_decode_fast_d128(job, stream);
+    default: return launch_decode_fast_d256(job, stream);
   }
-  if (e != hipSuccess) return e;
-  return launch_combine(job, stream);
 }
 
 }  // namespace aqkv

@@ -176,6 +176,34 @@ def test_decode_validation_codes():
     assert call(b=0, cache=_cache(n_slots=0)) == 0
 
 
+def test_decode_window_validation_codes():
+    lib = aqkv.lib()
+    cfg = aqkv.config(128, 2, 128)
+    layer = aqkv.LayerParams(FAKE, FAKE, FAKE, FAKE)
+    need = aqkv.decode_workspace_bytes(cfg, 1, 4, 2, 64)
+
+    def win(tokens=8, dtype=aqkv.BF16, heads=2, batch=1):
+        return aqkv.KvView(FAKE, dtype, batch, heads, tokens, heads * 1024 * 128, 1024 * 128, 128)
+
+    def call(kw=None, vw=None, q=FAKE, T=64):
+        kw = kw or win()
+        vw = vw or win()
+        return lib.aqkv_decode_attention_window(C.byref(cfg), C.byref(layer), C.byref(_cache()), 1, 4, 2, T, q,
+                                                FAKE, FAKE, C.byref(kw), C.byref(vw), C.c_float(0.1), None, FAKE,
+                                                FAKE, need, None)
+
+    assert lib.aqkv_decode_attention_window(C.byref(cfg), C.byref(layer), C.byref(_cache()), 1, 4, 2, 64, FAKE,
+                                            FAKE, FAKE, None, C.byref(win()), C.c_float(0.1), None, FAKE, FAKE,
+                                            need, None) == -1
+    assert call(q=None) == -1
+    assert call(q=FAKE + 4) == -3
+    assert call(vw=win(dtype=aqkv.FP32)) == -6
+    assert call(vw=win(tokens=9)) == -2
+    assert call(kw=win(heads=3), vw=win(heads=3)) == -2
+    assert call(kw=win(tokens=1025), vw=win(tokens=1025)) == -8
+    assert call(kw=win(dtype=7), vw=win(dtype=7)) == -6
+
+
 @pytest.mark.parametrize("d,bits", [(128, 1), (128, 2), (128, 3), (256, 2), (256, 3), (64, 2), (3, 2)])
 def test_library_codebook_equals_oracle(d, bits):
     c, t = aqkv.build_codebook(d, bits)

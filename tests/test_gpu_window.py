@@ -1,0 +1,151 @@
+"""GPU parity of decode over the compressed history plus a full-precision
+recent-token window, through the C ABI, against the oracle on the same
+seeded inputs (history planes quantised by the oracle and uploaded, so only
+the decode is compared).  Bar: outputs within 2e-3 absolute."""
+import numpy as np
+import pytest
+
+from kv_cache_compression_quantize_amd import aqkv, inputs
+from oracle import attention as oatt
+
+from gpu_helpers import OUT_ATOL, cfg_of, device_layer, host_layer, say, score_err, SCORE_RTOL, torch_dev
+from test_gpu_parity import _upload_oracle_cache
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # d, w, m, G, T_hist, n_window, window dtype
+    (128, 2, 128, 4, 300, 37, "bf16"), (128, 2, 128, 1, 1000, 128, "fp32"), (128, 2, 128, 8, 4097, 1024, "bf16"),
+    (256, 3, 256, 2, 130, 16, "bf16"), (128, 0, 192, 4, 513, 64, "bf16"), (64, 1, 64, 8, 77, 5, "fp32"),
+    (128, 2, 128, 4, 0, 15, "bf16"), (128, 2, 128, 2, 250, 1, "bf16"), (128, 2, 128, 2, 250, 0, "bf16"),
+]
+
+
+@pytest.mark.parametrize("d,w,m,G,T,W,wdtype", CASES)
+def test_decode_window_parity(d, w, m, G, T, W, wdtype):
+    torch, dev = torch_dev()
+    say("decode window", d, w, m, G, T, W, wdtype)
+    B, Hkv = 2, 2
+    Hq = Hkv * G
+    hl = host_layer(d, w, m, layer=2)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    rng = np.random.default_rng(d + 3 * T + W)
+    ks = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(B * Hkv)]
+    vs = [(rng.standard_normal((T, d)) * 2).astype(np.float32) for _ in range(B * Hkv)]
+    cache, refs = _upload_oracle_cache(hl, cfg, ks, vs, 2, capacity=max(T, 1) + 5)
+    kw = rng.standard_normal((B, Hkv, W, d)).astype(np.float32) * 1.5
+    vw = rng.standard_normal((B, Hkv, W, d)).astype(np.float32)
+    if wdtype == "bf16":
+        kw, vw = inputs.bf16_bits_to_f32(inputs.to_bf16_bits(kw)), inputs.bf16_bits_to_f32(inputs.to_bf16_bits(vw))
+        tw = lambda x: torch.from_numpy(inputs.to_bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        tw = lambda x: torch.from_numpy(x).to(dev)
+    # a strided window: every other slot of a larger ring buffer
+    ring_k = torch.zeros((B, Hkv, 2 * max(W, 1), d), dtype=torch.bfloat16 if wdtype == "bf16" else torch.float32,
+                         device=dev)
+    ring_v = torch.zeros_like(ring_k)
+    ring_k[:, :, 0:2 * W:2] = tw(kw)
+    ring_v[:, :, 0:2 * W:2] = tw(vw)
+    k_win, v_win = ring_k[:, :, 0:2 * W:2], ring_v[:, :, 0:2 * W:2]
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    q_rot, q_sk = oatt.prepare_query(q.reshape(-1, d), hl.rotation, hl.sketch, w)
+    qd = torch.from_numpy(q).to(dev)
+    qr_d = torch.from_numpy(q_rot.astype(np.float32)).to(dev) if w > 0 else None
+    qs_d = torch.from_numpy(q_sk.astype(np.float32)).to(dev)
+    scores = torch.full((B, Hq, max(T, 1)), float("nan"), device=dev)
+    out = aqkv.decode_attention_window(cfg, layer, cache, B, Hq, Hkv, T, qd, qr_d, qs_d, k_win, v_win,
+                                       scores=scores)
+    torch.cuda.synchronize()
+    out, scores = out.cpu().numpy(), scores.cpu().numpy()
+    worst_o = worst_s = 0.0
+    for s in range(B * Hkv):
+        b, hkv = divmod(s, Hkv)
+        qh = q[b, hkv * G:(hkv + 1) * G]
+        _, o_ref = oatt.decode_slot_window(qh, refs[s][0], refs[s][1], kw[b, hkv], vw[b, hkv], hl.rotation,
+                                           hl.sketch, hl.centroids, w)
+        worst_o = max(worst_o, float(np.max(np.abs(out[b, hkv * G:(hkv + 1) * G] - o_ref))))
+        if T > 0:
+            s_ref = oatt.scores(qh, refs[s][0], hl.rotation, hl.sketch, hl.centroids, w)
+            worst_s = max(worst_s, score_err(scores[b, hkv * G:(hkv + 1) * G, :T], s_ref))
+    say(f"out err {worst_o:.2e}, score err {worst_s:.2e}")
+    assert worst_o <= OUT_ATOL
+    assert worst_s <= SCORE_RTOL
+
+
+def test_decode_window_empty_everything_and_no_window_equals_plain():
+    torch, dev = torch_dev()
+    d, w, m, G, T = 128, 2, 128, 2, 300
+    hl = host_layer(d, w, m)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    rng = np.random.default_rng(4)
+    cache, _ = _upload_oracle_cache(hl, cfg, [rng.standard_normal((T, d)).astype(np.float32)],
+                                    [rng.standard_normal((T, d)).astype(np.float32)], 2, capacity=T)
+    q = torch.from_numpy(rng.standard_normal((1, G, d)).astype(np.float32)).to(dev)
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, q)
+    empty = torch.zeros((1, 1, 0, d), dtype=torch.bfloat16, device=dev)
+    plain = aqkv.decode_attention(cfg, layer, cache, 1, G, 1, T, q_rot, q_sk)
+    with_empty = aqkv.decode_attention_window(cfg, layer, cache, 1, G, 1, T, q, q_rot, q_sk, empty, empty)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, with_empty)
+    none = aqkv.decode_attention_window(cfg, layer, cache, 1, G, 1, 0, q, q_rot, q_sk, empty, empty)
+    assert torch.all(none == 0)
+
+
+def test_streaming_append_with_recent_window():
+    # a decode loop: tokens arrive a few at a time into a full-precision FIFO of
+    # `window` + 32 slots; whenever it is full its oldest 32 tokens (one block
+    # record) are quantised into the compressed cache with the prepared key
+    # operands and the rest move down.  At the end the cache equals a one-call
+    # quantisation of the history, and attention over (history, FIFO) equals the
+    # same call on that cache.
+    torch, dev = torch_dev()
+    say("streaming append with a recent-token window")
+    d, w, m, G = 128, 2, 128, 4
+    B, Hkv, window, total = 2, 2, 48, 333
+    Hq = Hkv * G
+    hl = host_layer(d, w, m, layer=1)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    rng = np.random.default_rng(17)
+    bf = lambda x: torch.from_numpy(inputs.to_bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+    K = bf(rng.standard_normal((B, Hkv, total, d)).astype(np.float32))
+    V = bf(rng.standard_normal((B, Hkv, total, d)).astype(np.float32))
+    q = torch.from_numpy(rng.standard_normal((B, Hq, d)).astype(np.float32)).to(dev)
+
+    cache = aqkv.Cache.allocate(cfg, B * Hkv, total)
+    cache.blocks.zero_()
+    kws = aqkv.prepare_key_operands(cfg, layer, device=dev)
+    fifo_k = torch.zeros((B, Hkv, window + 32, d), dtype=torch.bfloat16, device=dev)
+    fifo_v = torch.zeros_like(fifo_k)
+    n_hist = n_fifo = t = 0
+    while t < total:
+        n = min(int(rng.integers(1, 8)), total - t, window + 32 - n_fifo)
+        fifo_k[:, :, n_fifo:n_fifo + n] = K[:, :, t:t + n]
+        fifo_v[:, :, n_fifo:n_fifo + n] = V[:, :, t:t + n]
+        n_fifo += n
+        t += n
+        if n_fifo == window + 32:
+            aqkv.quantize_keys_prepared(cfg, layer, fifo_k[:, :, :32], cache, kws, token_offset=n_hist)
+            aqkv.quantize_values(cfg, fifo_v[:, :, :32], cache, token_offset=n_hist)
+            n_hist += 32
+            fifo_k[:, :, :window] = fifo_k[:, :, 32:].clone()
+            fifo_v[:, :, :window] = fifo_v[:, :, 32:].clone()
+            n_fifo = window
+    assert n_hist + n_fifo == total and n_hist > 0
+
+    one = aqkv.Cache.allocate(cfg, B * Hkv, total)
+    one.blocks.zero_()
+    aqkv.quantize_keys(cfg, layer, K[:, :, :n_hist], one)
+    aqkv.quantize_values(cfg, V[:, :, :n_hist], one)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.blocks, one.blocks)
+
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, q)
+    out = aqkv.decode_attention_window(cfg, layer, cache, B, Hq, Hkv, n_hist, q, q_rot, q_sk,
+                                       fifo_k[:, :, :n_fifo], fifo_v[:, :, :n_fifo])
+    ref = aqkv.decode_attention_window(cfg, layer, one, B, Hq, Hkv, n_hist, q, q_rot, q_sk,
+                                       K[:, :, n_hist:], V[:, :, n_hist:])
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
