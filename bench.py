@@ -32,6 +32,8 @@ METRIC = "compressed-KV decode attn: keys scored/s + HBM GB/s (%peak); quantize 
 DEFAULT_WORKLOAD = "llama2_7b_layer_mha32_t32k"
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "i8": 5000.0, "fp32": 157.3}
+WINDOW_TOKENS = 128   # recent-token window of the detail timing
+
 KERNEL_SOURCES = {
     "decode": ["decode_fast.h", "decode_launch.hip", "decode_fast_d64.hip", "decode_fast_d128.hip",
                "decode_fast_d256.hip", "decode.hip"],
@@ -115,6 +117,15 @@ class Path:
         self.out = torch.empty((w.batch, w.n_q_heads, w.head_dim), device=dev)
         self.scores = (torch.empty((w.batch, w.n_q_heads, w.context), device=dev) if w.scores else None)
         self.side = torch.cuda.Stream(device=dev)   # default priority
+        # a full-precision recent-token window beside the compressed history (detail timing only)
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        self.n_window = WINDOW_TOKENS
+        self.win_k = torch.randn((w.batch, w.n_kv_heads, self.n_window, w.head_dim), generator=g,
+                                 device=dev).to(torch.bfloat16)
+        self.win_v = torch.randn((w.batch, w.n_kv_heads, self.n_window, w.head_dim), generator=g,
+                                 device=dev).to(torch.bfloat16)
+        self.q_f32 = self.x["q"].float().contiguous()
 
     def quantize_keys(self):
         self.aqkv.quantize_keys_prepared(self.cfg, self.layer, self.x["k"], self.cache, self.kws)
@@ -132,6 +143,12 @@ class Path:
         w = self.w
         self.aqkv.decode_attention(self.cfg, self.layer, self.cache, w.batch, w.n_q_heads, w.n_kv_heads,
                                    w.context, self.q_rot, self.q_sk, None, self.scores, self.out, self.dws)
+
+    def decode_window(self):
+        w = self.w
+        self.aqkv.decode_attention_window(self.cfg, self.layer, self.cache, w.batch, w.n_q_heads, w.n_kv_heads,
+                                          w.context, self.q_f32, self.q_rot, self.q_sk, self.win_k, self.win_v,
+                                          None, None, self.out, self.dws)
 
     def step(self):
         # values and the query do not depend on the keys: they run on a second stream
@@ -169,7 +186,7 @@ def time_calls(path, reps: int) -> dict:
     """Average duration of each call, HIP events on the launch stream."""
     import torch
     stream = torch.cuda.current_stream()
-    names = ["quantize_keys", "quantize_values", "prepare_query", "decode", "prepare_key_operands"]
+    names = ["quantize_keys", "quantize_values", "prepare_query", "decode", "prepare_key_operands", "decode_window"]
     ev = {n: [] for n in names}
     for _ in range(reps):
         for n in names:
@@ -411,6 +428,8 @@ def main():
             "keys_TFLOPs": qk_flops / (per["quantize_keys"] / 1e3) / 1e12,
             "keys_GBps": qk_bytes / (per["quantize_keys"] / 1e3) / 1e9,
             "values_GBps": qv_bytes / (per["quantize_values"] / 1e3) / 1e9}
+        rec["decode_window"] = {"window_tokens": path.n_window, "ms": per["decode_window"],
+                                "extra_ms_over_decode": per["decode_window"] - per["decode"]}
         rec["prepare_query_ms"] = per["prepare_query"]
         rec["prepare_key_operands_ms_once_per_layer"] = per["prepare_key_operands"]
         dominant = max(["decode", "quantize_keys", "quantize_values"], key=lambda n: per[n])

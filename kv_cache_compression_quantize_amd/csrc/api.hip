@@ -88,9 +88,8 @@ DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int6
   p.split_tokens = per_split * kGrain;
   p.n_split = static_cast<int>(grains > 0 ? (grains + per_split - 1) / per_split : 1);
   const size_t heads = static_cast<size_t>(n_slots) * g;
-  // one more partial per head than splits: room for a recent-token window's
-  p.acc_bytes = round_up(heads * (p.n_split + 1) * d * sizeof(float), 256);
-  p.ml_bytes = round_up(heads * (p.n_split + 1) * 2 * sizeof(float), 256);
+  p.acc_bytes = round_up(heads * p.n_split * d * sizeof(float), 256);
+  p.ml_bytes = round_up(heads * p.n_split * 2 * sizeof(float), 256);
   p.total_bytes = p.acc_bytes + p.ml_bytes;
   return p;
 }
@@ -378,14 +377,15 @@ static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the matrix-core decoder addresses a slot's records with 32-bit byte offsets
   if (plan.mfma && cache->capacity / kBlockRows * L.rec >= (int64_t(1) << 31)) return AQKV_ERR_UNSUPPORTED;
-  // with a window and no history yet, the window is the only partial
+  // with a window and no history yet, the window is all there is
   const bool history = !win || context_len > 0;
-  job.part_stride = history ? plan.n_split + (win ? 1 : 0) : 1;
+  job.part_stride = history ? plan.n_split : 0;
   if (history) {
     const hipError_t e = plan.mfma ? launch_decode_mfma(job, s) : launch_decode(job, s);
     if (e != hipSuccess) return AQKV_ERR_HIP;
   }
-  if (win) {
+  if (!win) return hip_status(launch_combine(job, s));
+  {
     WindowJob wj{};
     wj.k = win->k->data;
     wj.v = win->v->data;
@@ -399,17 +399,10 @@ static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const
     wj.v_ts = win->v->token_stride;
     wj.n_window = static_cast<int>(win->k->tokens);
     wj.q = win->q;
-    wj.d = d;
     wj.g = g;
-    wj.n_slots = cache->n_slots;
     wj.softmax_scale = softmax_scale;
-    wj.part_acc = job.part_acc;
-    wj.part_ml = job.part_ml;
-    wj.part_stride = job.part_stride;
-    wj.part_index = job.part_stride - 1;
-    if (launch_window_partial(wj, s) != hipSuccess) return AQKV_ERR_HIP;
+    return hip_status(launch_combine_window(job, wj, s));
   }
-  return hip_status(launch_combine(job, s));
 }
 
 aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache,

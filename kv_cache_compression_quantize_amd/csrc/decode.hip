@@ -224,9 +224,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
   }
 }
 
-// Merge the part_stride partials of one query head (the splits, then the
-// recent-token window if there is one): M = max_i m_i, weights
-// w_i = 2^(m_i - M) (0 for empty parts), out = sum_i w_i acc_i / sum_i w_i l_i.
+// Merge the split partials of one query head: M = max_i m_i, weights
+// w_i = 2^(m_i - M) (0 for empty splits), out = sum_i w_i acc_i / sum_i w_i l_i.
 // The weights go to LDS (1024 splits per pass); 256 / d threads share a channel,
 // each summing every (256 / d)-th split with independent loads in flight.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeJob job) {

@@ -104,10 +104,10 @@ struct DecodeJob {
   float *out;            // [n_slots*g][d]
   float *part_acc;       // [n_slots*g][part_stride][d]
   float *part_ml;        // [n_slots*g][part_stride][2]
-  int part_stride;       // partials per head: n_split, or n_split + 1 with a recent-token window
+  int part_stride;       // partials per head (the decoder's splits; 0 when there is none)
 };
 
-// Exact attention over the recent-token window, written as one more partial
+// The recent-token window of a decode call, merged in by the combine
 constexpr int kMaxWindow = 1024;
 struct WindowJob {
   const void *k, *v;     // [batch][heads][n_window][d] views
@@ -116,11 +116,8 @@ struct WindowJob {
   int64_t k_bs, k_hs, k_ts, v_bs, v_hs, v_ts;   // strides in elements
   int n_window;
   const float *q;        // [n_slots*g][d] fp32
-  int d, g;
-  int64_t n_slots;
+  int g;
   float softmax_scale;
-  float *part_acc, *part_ml;
-  int part_stride, part_index;
 };
 
 // Decode split-K plan shared by the workspace query and the launch.
@@ -142,7 +139,8 @@ hipError_t launch_quantize_values(const ValueJob &job, hipStream_t stream);
 hipError_t launch_prepare_query(const QueryJob &job, hipStream_t stream);
 hipError_t launch_decode(const DecodeJob &job, hipStream_t stream);
 hipError_t launch_combine(const DecodeJob &job, hipStream_t stream);
-hipError_t launch_window_partial(const WindowJob &job, hipStream_t stream);
+// the split combine with a recent-token window merged in (in place of launch_combine)
+hipError_t launch_combine_window(const DecodeJob &job, const WindowJob &wj, hipStream_t stream);
 bool decode_supported(int d, int w, int g, int m, int vb);
 // matrix-core decode kernel (partials only; launch_combine merges them), shapes with a compiled kernel
 bool decode_mfma_supported(int d, int w, int g, int m, int vb);
