@@ -3,6 +3,8 @@ import json
 import os
 
 import numpy as np
+import pytest
+from scipy import linalg as sla
 from scipy import stats
 
 from kv_cache_compression_quantize_amd import inputs
@@ -68,3 +70,40 @@ def test_layer_seeds_differ_and_repeat():
     np.testing.assert_array_equal(s0, s0b)
     assert not np.allclose(g0, g1)
     assert inputs.layer_seed(0) == 42 and inputs.layer_seed(5) == 77
+
+
+# ---------------------------------------------------------------- randomised Hadamard
+
+
+@pytest.mark.parametrize("d", [1, 2, 4, 64, 128, 256])
+def test_sylvester_matches_library(d):
+    np.testing.assert_array_equal(rotation.sylvester_hadamard(d), sla.hadamard(d))
+
+
+def test_sylvester_small_textbook():
+    np.testing.assert_array_equal(rotation.sylvester_hadamard(2), [[1, 1], [1, -1]])
+    with pytest.raises(ValueError):
+        rotation.sylvester_hadamard(96)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_randomized_hadamard_is_orthogonal_and_a_fast_transform(d):
+    g, _ = inputs.layer_gaussians(3, d, d)
+    pi = rotation.randomized_hadamard(g)
+    np.testing.assert_allclose(pi @ pi.T, np.eye(d), atol=1e-13)
+    # Pi x = FWHT(D x) / sqrt(d): the explicit matrix against the butterfly recursion
+    x = np.random.default_rng(d).standard_normal((7, d))
+    s = rotation.hadamard_signs(g)
+    np.testing.assert_allclose(x @ pi.T, rotation.fwht(x * s) / np.sqrt(d), rtol=1e-12, atol=1e-13)
+    # the signs are random: about half of them flip
+    assert 0.3 * d < np.sum(s < 0) < 0.7 * d
+
+
+def test_hadamard_spreads_an_outlier_channel():
+    # NexusQuant stage 4: the energy of a single channel is spread evenly over all d
+    d = 128
+    g, _ = inputs.layer_gaussians(0, d, d)
+    pi = rotation.randomized_hadamard(g)
+    e = np.zeros(d)
+    e[17] = 10.0
+    np.testing.assert_allclose(np.abs(pi @ e), 10.0 / np.sqrt(d), rtol=1e-13)
