@@ -55,7 +55,7 @@ def source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def build_layer(w, layer: int):
+def build_layer(w, layer: int, rotation: str = "qr"):
     """Layer parameters built by the library itself (host builders), then copied to HBM."""
     import torch
 
@@ -65,7 +65,7 @@ def build_layer(w, layer: int):
     dev = torch.device("cuda:0")
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
     if w.mse_bits > 0:
-        pi = aqkv.build_rotation(g)
+        pi = aqkv.build_rotation(g) if rotation == "qr" else aqkv.build_hadamard_rotation(g)
         c, t = aqkv.build_codebook(d, w.mse_bits)
         return aqkv.Layer(rotation=f(pi), sketch=f(s), centroids=f(c), boundaries=f(t))
     return aqkv.Layer(sketch=f(s))
@@ -96,14 +96,14 @@ def make_inputs(w, layer: int):
 class Path:
     """All buffers for one layer of the workload and the four calls of one step."""
 
-    def __init__(self, w, layer: int):
+    def __init__(self, w, layer: int, rotation: str = "qr"):
         import torch
 
         from kv_cache_compression_quantize_amd import aqkv
         self.aqkv = aqkv
         self.w = w
         self.cfg = aqkv.config(w.head_dim, w.mse_bits, w.sketch_dim(layer), w.value_bits, w.value_group)
-        self.layer = build_layer(w, layer)
+        self.layer = build_layer(w, layer, rotation)
         self.x = make_inputs(w, layer)
         dev = torch.device("cuda:0")
         self.cache = aqkv.Cache.allocate(self.cfg, w.n_slots, w.context)
@@ -337,6 +337,8 @@ def main():
     ap.add_argument("--no-detail", action="store_true", help="skip per-call timing (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--rotation", choices=["qr", "hadamard"], default="qr",
+                    help="the keys' rotation: Haar (QR of a Gaussian) or randomised Hadamard")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step captured once as a HIP graph instead of launching each call from Python "
                          "(measured no faster for these kernel sizes)")
@@ -359,7 +361,7 @@ def main():
     w = inputs.WORKLOADS[args.workload]
     layer = args.layer
     log(f"workload {w.name}: setting up inputs")
-    path = Path(w, layer)
+    path = Path(w, layer, args.rotation)
     torch.cuda.synchronize()
     log("warmup")
     for _ in range(args.warmup):
@@ -402,7 +404,7 @@ def main():
                       "context": w.context, "head_dim": w.head_dim, "mse_bits": w.mse_bits,
                       "sketch_dim": w.sketch_dim(layer), "value_bits": w.value_bits,
                       "value_group": w.value_group, "kv_dtype": w.dtype, "recipe": w.recipe,
-                      "launch": "hip_graph" if args.graph else "eager"}}
+                      "launch": "hip_graph" if args.graph else "eager", "rotation": args.rotation}}
     if not args.no_detail:
         log("per-call timing")
         per = time_calls(path, reps=max(5, args.steps))

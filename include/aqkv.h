@@ -163,6 +163,17 @@ aqkv_status aqkv_build_codebook(int32_t head_dim, int32_t bits, float *centroids
  * (host).  d in 1..4096. */
 aqkv_status aqkv_build_rotation(int32_t d, const double *gaussian, float *rotation);
 
+/* Randomised Hadamard rotation (NexusQuant article, stage 4 "Hadamard
+ * rotation": a Hadamard matrix spreads every coordinate's energy over all d,
+ * removing outliers): Pi = H diag(s) / sqrt(d), H Sylvester's Hadamard matrix
+ * (H_ij = (-1)^popcount(i & j)), s_j = +1 where gaussian[j] >= 0 (the first
+ * row of the layer's d x d Gaussian draw, host double), else -1; written
+ * row-major fp32 to rotation (host).  d a power of two up to 4096.  A drop-in
+ * replacement for aqkv_build_rotation's output: the key quantiser notices that
+ * every entry has one magnitude and multiplies by +-1 operands, one matrix
+ * pass instead of two. */
+aqkv_status aqkv_build_hadamard_rotation(int32_t d, const double *gaussian, float *rotation);
+
 /* Workspace bytes aqkv_quantize_keys needs for this configuration. */
 size_t aqkv_quantize_keys_workspace_bytes(const aqkv_config *cfg);
 

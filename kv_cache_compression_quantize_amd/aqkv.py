@@ -80,6 +80,7 @@ _SIGS = {
     "aqkv_build_codebook": (C.c_int, [C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
     "aqkv_build_rotation": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p]),
     "aqkv_quantize_keys_workspace_bytes": (C.c_size_t, [_P(Config)]),
+    "aqkv_build_hadamard_rotation": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p]),
     "aqkv_decode_workspace_bytes": (C.c_size_t, [_P(Config), C.c_int32, C.c_int32, C.c_int32, C.c_int64]),
     "aqkv_quantize_keys": (C.c_int, [_P(Config), _P(LayerParams), _P(KvView), C.c_int64, _P(CacheDesc),
                                      C.c_void_p, C.c_size_t, C.c_void_p]),
@@ -178,6 +179,15 @@ def build_rotation(gaussian: np.ndarray) -> np.ndarray:
     assert g.shape == (d, d)
     out = np.zeros((d, d), dtype=np.float32)
     _check(lib().aqkv_build_rotation(d, g.ctypes.data, out.ctypes.data), "aqkv_build_rotation")
+    return out
+
+
+def build_hadamard_rotation(gaussian: np.ndarray) -> np.ndarray:
+    """Randomised Hadamard rotation H diag(sign(gaussian[0])) / sqrt(d), computed by the library."""
+    g = np.ascontiguousarray(gaussian, dtype=np.float64)
+    d = g.shape[-1]
+    out = np.zeros((d, d), dtype=np.float32)
+    _check(lib().aqkv_build_hadamard_rotation(d, g.ctypes.data, out.ctypes.data), "aqkv_build_hadamard_rotation")
     return out
 
 

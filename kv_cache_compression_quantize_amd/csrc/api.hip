@@ -65,7 +65,7 @@ aqkv_status hip_status(hipError_t e) { return e == hipSuccess ? AQKV_OK : AQKV_E
 
 size_t key_workspace_bytes(int d, int w, int m) {
   // matrix-core operands of Pi and S Pi^T (w > 0) or S (w == 0), f16 hi + lo
-  return round_up(aqkv::key_operand_bytes(d, w, m), 256);
+  return aqkv::key_operand_header(d, w, m) + 256;   // the operands, then the rotation-scale float
 }
 
 }  // namespace
@@ -215,6 +215,7 @@ static aqkv_status quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer
   job.w = w;
   job.m = m;
   job.ops = ops;
+  job.rot_scale = reinterpret_cast<const float *>(ops + key_operand_header(d, w, m));
   job.centroids = layer->centroids;
   job.boundaries = layer->boundaries;
   const BlockLayout L = layout_of(cfg);

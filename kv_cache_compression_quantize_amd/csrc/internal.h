@@ -60,6 +60,7 @@ struct KeyJob {
   int64_t n_slots, n_tokens, token_offset, capacity;
   int d, w, m;
   const uint8_t *ops;     // matrix-core operands of Pi and S Pi^T (or S), see quant_keys_mfma.hip
+  const float *rot_scale; // a > 0 when every |Pi_ij| == a (then the Pi operands are +-1, exact); else 0
   const float *centroids, *boundaries;
   // cache fields, each at its place in record 0; row r at + rec_row(r, row bytes, rec)
   uint8_t *codes, *signs, *norm, *rnorm;
@@ -132,6 +133,8 @@ DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int6
 // Launchers (return a hipError_t from hipGetLastError after the launch).
 // matrix-core key quantisation: operand preparation (workspace) + kernel
 size_t key_operand_bytes(int d, int w, int m);
+// the workspace: the operands, then (at key_operand_header(d, w, m)) one float, the rotation's common |Pi_ij| or 0
+size_t key_operand_header(int d, int w, int m);
 hipError_t launch_key_operands(const float *rotation, const float *sketch, uint8_t *ops, int d, int w, int m,
                                hipStream_t stream);
 hipError_t launch_quantize_keys_mfma(const KeyJob &job, hipStream_t stream);

@@ -132,6 +132,20 @@ aqkv_status aqkv_build_codebook(int32_t head_dim, int32_t bits, float *centroids
   return AQKV_OK;
 }
 
+aqkv_status aqkv_build_hadamard_rotation(int32_t d, const double *gaussian, float *rotation) {
+  if (!gaussian || !rotation) return AQKV_ERR_NULL;
+  if (d < 1 || d > 4096 || (d & (d - 1))) return AQKV_ERR_SHAPE;
+  // Sylvester's H_ij = (-1)^popcount(i & j), columns flipped by the signs of the
+  // first Gaussian row, scaled by 1/sqrt(d)
+  const double a = 1.0 / sqrt(static_cast<double>(d));
+  for (int32_t i = 0; i < d; ++i)
+    for (int32_t j = 0; j < d; ++j) {
+      const double h = (__builtin_popcount(static_cast<unsigned>(i & j)) & 1) ? -a : a;
+      rotation[static_cast<size_t>(i) * d + j] = static_cast<float>(gaussian[j] >= 0.0 ? h : -h);
+    }
+  return AQKV_OK;
+}
+
 aqkv_status aqkv_build_rotation(int32_t d, const double *gaussian, float *rotation) {
   if (!gaussian || !rotation) return AQKV_ERR_NULL;
   if (d < 1 || d > 4096) return AQKV_ERR_SHAPE;

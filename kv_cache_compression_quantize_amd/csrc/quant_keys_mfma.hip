@@ -101,9 +101,21 @@ __device__ __forceinline__ uint32_t push_bit(uint32_t w, bool bit) { return w + 
 
 // One thread per (slab, k-step, lane, slot): writes the high and low f16
 // parts of one A-operand element (scaled by 2^8).
+// Whether every entry of the rotation has one magnitude a (a randomised
+// Hadamard rotation: +-1/sqrt(d)); writes a, or 0, to *scale.  One block.
+__global__ __launch_bounds__(256) void rotation_scale_kernel(const float *__restrict__ rot, int d,
+                                                             float *__restrict__ scale) {
+  const float a = d > 0 ? fabsf(rot[0]) : 0.0f;
+  bool same = a > 0.0f && a < INFINITY;
+  for (int64_t i = threadIdx.x; i < static_cast<int64_t>(d) * d; i += 256) same = same && fabsf(rot[i]) == a;
+  same = __syncthreads_and(same);
+  if (threadIdx.x == 0) *scale = same ? a : 0.0f;
+}
+
 __global__ __launch_bounds__(256) void key_operands_kernel(const float *__restrict__ rot,
                                                            const float *__restrict__ sketch,
-                                                           uint8_t *__restrict__ ops, int d, int w, int m) {
+                                                           uint8_t *__restrict__ ops, int d, int w, int m,
+                                                           const float *__restrict__ rot_scale) {
   const int ks = d / 32, td = d / 16, tm = m / 16;
   const int slabs = (w > 0 ? td : 0) + tm;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -118,6 +130,8 @@ __global__ __launch_bounds__(256) void key_operands_kernel(const float *__restri
     // rotation: row = permuted coordinate, column = input coordinate 32k + 8g + s
     const int row = permuted_row(slab, r, td);
     v = rot[static_cast<int64_t>(row) * d + 32 * k + 8 * g + s];
+    // one magnitude: the operand is sign(v) (times 2^8 below), exact in f16 with a zero low part
+    if (*rot_scale > 0.0f) v = v > 0.0f ? 1.0f : -1.0f;
   } else {
     const int tz = slab - (w > 0 ? td : 0);
     const int row = permuted_row(tz, r, tm);
@@ -402,8 +416,9 @@ __device__ __forceinline__ void finish_words(IndexState<D, W> &S, uint32_t valid
 // k-step t / 2), e'^2 into esq.  The index is the thermometer count of the
 // comparisons; bit p of it is the xor of the comparisons q with
 // (q + 1) % 2^p == 0.
-// The rotation product of one 16-row tile (matrix cores only)
-template <int D, bool BF16>
+// The rotation product of one 16-row tile (matrix cores only); LO = false when
+// the rotation's operands are exact (+-1) and their low parts zero
+template <int D, bool BF16, bool LO = true>
 __device__ __forceinline__ void rot_tile(const SlabOps<D> &A, const Ops<D> &uh, const Ops<D> &ul,
                                          v4f (&acc)[Geo<D>::NT]) {
   constexpr int NT = Geo<D>::NT;
@@ -417,7 +432,7 @@ __device__ __forceinline__ void rot_tile(const SlabOps<D> &A, const Ops<D> &uh, 
     for (int nt = 0; nt < NT; ++nt) {
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(uh[nt][k]), acc[nt], 0, 0, 0);
       if (!BF16) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(ul[nt][k]), acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_v8h(uh[nt][k]), acc[nt], 0, 0, 0);
+      if (LO) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_v8h(uh[nt][k]), acc[nt], 0, 0, 0);
     }
   }
 }
@@ -488,19 +503,19 @@ __device__ __forceinline__ void index_vals(int t, const v4f (&acc)[Geo<D>::NT], 
   }
 }
 
-template <int D, int W, bool BF16, bool SYM>
+template <int D, int W, bool BF16, bool SYM, bool LO>
 __device__ __forceinline__ void index_tile(int t, const SlabOps<D> &A, const Ops<D> &uh, const Ops<D> &ul,
                                            const float (&yscale)[Geo<D>::NT], IndexState<D, W> &S, Ops<D> &bh,
                                            Ops<D> &bl) {
   v4f acc[Geo<D>::NT];
-  rot_tile<D, BF16>(A, uh, ul, acc);
+  rot_tile<D, BF16, LO>(A, uh, ul, acc);
   index_vals<D, W, SYM>(t, acc, yscale, S, bh, bl);
 }
 
 // Word group wl of the coordinates: its tiles (8, or 4 for a trailing group)
 // from the last down, so the bits arrive most significant first.  `group`
 // points at this lane's bytes of the group's first slab.
-template <int D, int W, bool BF16, bool SYM>
+template <int D, int W, bool BF16, bool SYM, bool LO>
 __device__ __forceinline__ void index_group(int wl, const uint8_t *group, int g, const Ops<D> &uh, const Ops<D> &ul,
                                             const float (&yscale)[Geo<D>::NT], IndexState<D, W> &S,
                                             uint32_t (&cw)[W][Geo<D>::NT][Geo<D>::WPL], Ops<D> &bh, Ops<D> &bl) {
@@ -515,7 +530,7 @@ __device__ __forceinline__ void index_group(int wl, const uint8_t *group, int g,
 #pragma unroll
   for (int j = cnt - 1; j >= 0; --j) {
     if (j > 0) fetch_slab<D>(A[(j - 1) & 1], group + (j - 1) * Geo<D>::SLAB);
-    index_tile<D, W, BF16, SYM>(8 * wl + j, A[j & 1], uh, ul, yscale, S, bh, bl);
+    index_tile<D, W, BF16, SYM, LO>(8 * wl + j, A[j & 1], uh, ul, yscale, S, bh, bl);
   }
   finish_words<D, W, SYM>(S, cnt == 8 ? 0xffffffffu : 0xffffu);
 #pragma unroll
@@ -695,7 +710,7 @@ __device__ __forceinline__ void store_signs(const KeyJob &job, const v4f (&z)[TM
 // after the two coordinate tiles of that k-step are rotated and indexed, so
 // matrix products and vector work interleave; only one k-step of the
 // residual operand is ever live.
-template <int D, int W, bool BF16, int TMS, bool SYM>
+template <int D, int W, bool BF16, int TMS, bool SYM, bool EXACT>
 __device__ __forceinline__ void resident_body(const KeyJob &job, int64_t n_tiles, uint8_t *smem) {
   using Gm = Geo<D>;
   constexpr int NT = Gm::NT;
@@ -713,12 +728,18 @@ __device__ __forceinline__ void resident_body(const KeyJob &job, int64_t n_tiles
   if (tile >= n_tiles) return;
   IndexState<D, W> S;
   if constexpr (W > 0) index_codebook<D, W>(job, S);
+  // EXACT: a one-magnitude rotation a * (+-1): operands +-1, y = a * (the product)
+  const float rot_a = EXACT ? job.rot_scale[0] : 0.0f;
+  constexpr bool lo_pass = !EXACT;
   RawKeys<D, BF16> R;
   load_keys<D, BF16>(job, locate<D>(job, tile * Gm::KT, n), g, R);
   for (; tile < n_tiles; tile += stride) {
     float nrm[NT], yscale[NT];
     Op uh[NT][KS], ul[NT][KS];
     prepare_keys<D, BF16>(R, nrm, yscale, uh, ul);
+    if constexpr (EXACT)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) yscale[nt] *= rot_a;
     uint32_t cw[W > 0 ? W : 1][NT][Gm::WPL];
     float gam[NT];
     Ops<D> bh, bl;   // the sketch's B operand, every k-step
@@ -734,7 +755,7 @@ __device__ __forceinline__ void resident_body(const KeyJob &job, int64_t n_tiles
       v4f acc_hi[NT], acc_lo[NT];
       fetch_slab<D>(A[1], pi_lds + (2 * KS - 1) * Gm::SLAB);
       fetch_slab<D>(A[0], pi_lds + (2 * KS - 2) * Gm::SLAB);
-      rot_tile<D, BF16>(A[1], uh, ul, acc_hi);
+      rot_tile<D, BF16, lo_pass>(A[1], uh, ul, acc_hi);
 #pragma unroll
       for (int k = KS - 1; k >= 0; --k) {
         const int t_hi = 2 * k + 1;
@@ -746,11 +767,11 @@ __device__ __forceinline__ void resident_body(const KeyJob &job, int64_t n_tiles
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) S.wv[p][nt] = 0u;
         }
-        rot_tile<D, BF16>(A[0], uh, ul, acc_lo);                      // tile t_hi - 1
+        rot_tile<D, BF16, lo_pass>(A[0], uh, ul, acc_lo);             // tile t_hi - 1
         if (k > 0) fetch_slab<D>(A[1], pi_lds + (t_hi - 2) * Gm::SLAB);
         index_vals<D, W, SYM>(t_hi, acc_hi, yscale, S, bh, bl);
         if (k > 0) {
-          rot_tile<D, BF16>(A[1], uh, ul, acc_hi);                    // tile t_hi - 2
+          rot_tile<D, BF16, lo_pass>(A[1], uh, ul, acc_hi);           // tile t_hi - 2
           fetch_slab<D>(A[0], pi_lds + (t_hi - 3) * Gm::SLAB);
         }
         index_vals<D, W, SYM>(t_hi - 1, acc_lo, yscale, S, bh, bl);
@@ -806,15 +827,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   copy_to_lds(job.ops, smem, (pi_slabs + TMS) * Geo<D>::SLAB, wave, lane);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (codebook_symmetric<W>(job)) resident_body<D, W, BF16, TMS, W != 0>(job, n_tiles, smem);
-  else resident_body<D, W, BF16, TMS, false>(job, n_tiles, smem);
+  // uniform choices, each a body of its own (no branch inside the scheduled loops)
+  const bool sym = codebook_symmetric<W>(job);
+  const bool exact = W > 0 && job.rot_scale[0] > 0.0f;
+  if (sym && exact) resident_body<D, W, BF16, TMS, W != 0, W != 0>(job, n_tiles, smem);
+  else if (sym) resident_body<D, W, BF16, TMS, W != 0, false>(job, n_tiles, smem);
+  else if (exact) resident_body<D, W, BF16, TMS, false, W != 0>(job, n_tiles, smem);
+  else resident_body<D, W, BF16, TMS, false, false>(job, n_tiles, smem);
 }
 
 // ---- streamed operands (sets larger than LDS): a block quantises one tile
 // of 8 x 32 (d = 256: 8 x 16) keys.  The rotation slabs come through LDS one
 // word group (8 slabs, at most 128 KiB) at a time, the sketch slabs in
 // double-buffered chunks of 2 or 4 slabs.
-template <int D, int W, bool BF16, bool SYM>
+template <int D, int W, bool BF16, bool SYM, bool EXACT>
 __device__ __forceinline__ void stream_body(const KeyJob &job, uint8_t *smem) {
   using Gm = Geo<D>;
   constexpr int NT = Gm::NT;
@@ -836,6 +862,13 @@ __device__ __forceinline__ void stream_body(const KeyJob &job, uint8_t *smem) {
     load_keys<D, BF16>(job, L, g, R);
     prepare_keys<D, BF16>(R, nrm, yscale, uh, ul);
   }
+  // EXACT: a one-magnitude rotation a * (+-1): operands +-1, y = a * (the product)
+  constexpr bool lo_pass = !EXACT;
+  if constexpr (EXACT) {
+    const float rot_a = job.rot_scale[0];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) yscale[nt] *= rot_a;
+  }
   uint32_t cw[W > 0 ? W : 1][NT][Gm::WPL];
   float gam[NT];
   Op bh[NT][Gm::KS], bl[NT][Gm::KS];
@@ -853,7 +886,7 @@ __device__ __forceinline__ void stream_body(const KeyJob &job, uint8_t *smem) {
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      index_group<D, W, BF16, SYM>(wl, smem + 16 * lane, g, uh, ul, yscale, S, cw, bh, bl);
+      index_group<D, W, BF16, SYM, lo_pass>(wl, smem + 16 * lane, g, uh, ul, yscale, S, cw, bh, bl);
     }
     index_end<D, W>(S, nrm, gam);
     __syncthreads();   // every wave is done with the rotation slabs
@@ -889,8 +922,12 @@ template <int D, int W, bool BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void quantize_keys_stream_kernel(
     KeyJob job) {
   extern __shared__ __align__(16) uint8_t smem[];
-  if (codebook_symmetric<W>(job)) stream_body<D, W, BF16, W != 0>(job, smem);
-  else stream_body<D, W, BF16, false>(job, smem);
+  const bool sym = codebook_symmetric<W>(job);
+  const bool exact = W > 0 && job.rot_scale[0] > 0.0f;
+  if (sym && exact) stream_body<D, W, BF16, W != 0, W != 0>(job, smem);
+  else if (sym) stream_body<D, W, BF16, W != 0, false>(job, smem);
+  else if (exact) stream_body<D, W, BF16, false, W != 0>(job, smem);
+  else stream_body<D, W, BF16, false, false>(job, smem);
 }
 
 constexpr size_t kLdsMax = 160 * 1024;
@@ -959,11 +996,22 @@ size_t key_operand_bytes(int d, int w, int m) {
   return static_cast<size_t>(slabs) * (d / 32) * 2048;
 }
 
+size_t key_operand_header(int d, int w, int m) { return (key_operand_bytes(d, w, m) + 255) / 256 * 256; }
+
 hipError_t launch_key_operands(const float *rotation, const float *sketch, uint8_t *ops, int d, int w, int m,
                                hipStream_t stream) {
+  float *scale = reinterpret_cast<float *>(ops + key_operand_header(d, w, m));
+  if (w > 0) {
+    rotation_scale_kernel<<<1, 256, 0, stream>>>(rotation, d, scale);
+  } else {
+    // no rotation: the header stays 0 (a one-thread fill, no memset node in a captured graph)
+    rotation_scale_kernel<<<1, 256, 0, stream>>>(sketch, 0, scale);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int64_t total = static_cast<int64_t>(key_operand_bytes(d, w, m) / 4);   // one thread per f16 pair
   key_operands_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(rotation, sketch, ops, d, w,
-                                                                                      m);
+                                                                                      m, scale);
   return hipGetLastError();
 }
 

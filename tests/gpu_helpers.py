@@ -45,9 +45,9 @@ class HostLayer:
     boundaries: np.ndarray # fp32
 
 
-def host_layer(d: int, w: int, m: int, layer: int = 0) -> HostLayer:
+def host_layer(d: int, w: int, m: int, layer: int = 0, rotation: str = "qr") -> HostLayer:
     g, s = inputs.layer_gaussians(layer, d, m)
-    pi = orot.rotation_fp32(g)
+    pi = orot.rotation_fp32(g) if rotation == "qr" else orot.randomized_hadamard_fp32(g)
     if w > 0:
         c, t = ocb.codebook_fp32(d, w)
     else:

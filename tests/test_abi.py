@@ -68,7 +68,8 @@ def test_workspace_sizes():
     # of the sketch, (d / 32) k-steps x (hi, lo) x 1 KiB each
     for d, w, m in [(128, 2, 128), (128, 0, 256), (256, 3, 256), (64, 1, 64), (128, 0, 192)]:
         slabs = (d // 16 if w > 0 else 0) + m // 16
-        assert aqkv.quantize_keys_workspace_bytes(aqkv.config(d, w, m)) == slabs * (d // 32) * 2048
+        # the operands, then a 256-byte header (the rotation's common magnitude)
+        assert aqkv.quantize_keys_workspace_bytes(aqkv.config(d, w, m)) == slabs * (d // 32) * 2048 + 256
     ws = aqkv.decode_workspace_bytes(cfg, 8, 32, 8, 131072)
     assert ws > 0 and ws % 256 == 0
     assert aqkv.decode_workspace_bytes(cfg, 1, 32, 5, 100) == 0   # Hq % Hkv != 0
@@ -230,3 +231,12 @@ def test_value_side_index_is_a_permutation():
         for t in range(32):
             if (t >> 2) & 1 == 0:
                 np.testing.assert_array_equal(idx[t + 4] // 4, idx[t] // 4)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_library_hadamard_rotation_equals_oracle(d):
+    g, _ = inputs.layer_gaussians(2, d, d)
+    np.testing.assert_array_equal(aqkv.build_hadamard_rotation(g), orot.randomized_hadamard_fp32(g))
+    with pytest.raises(aqkv.AqkvError) as e:
+        aqkv.build_hadamard_rotation(np.zeros((96, 96)))
+    assert e.value.status == -2

@@ -72,6 +72,50 @@ def test_quantize_keys_parity(d, w, m, dtype):
     say(f"index window: {tot_win} coords, {tot_mis_win} differ inside it")
 
 
+@pytest.mark.parametrize("d,w,m,dtype", [(128, 2, 128, "bf16"), (256, 3, 256, "bf16"), (64, 1, 64, "fp32"),
+                                         (128, 3, 256, "fp32")])
+def test_hadamard_rotation_keys_and_decode(d, w, m, dtype):
+    # a randomised Hadamard rotation through the same kernels (its +-1 operands take one
+    # matrix pass): key rows against the oracle, then decode over them end to end
+    torch, dev = torch_dev()
+    say("hadamard rotation", d, w, m, dtype)
+    B, H, T, G = 2, 2, 700, 2
+    k = _kv(B, H, T, d, seed=31 + d + w)
+    k[0, 1, 3, :4] *= 10.0                   # an outlier key
+    k = _as_dtype(k, dtype)
+    v = _as_dtype(_kv(B, H, T, d, seed=32 + d), dtype)
+    hl = host_layer(d, w, m, layer=5, rotation="hadamard")
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    cache = aqkv.Cache.allocate(cfg, B * H, T)
+    aqkv.quantize_keys(cfg, layer, to_device_kv(k, dtype), cache)
+    aqkv.quantize_values(cfg, to_device_kv(v, dtype), cache)
+    torch.cuda.synchronize()
+    refs = []
+    for s in range(B * H):
+        b, h = divmod(s, H)
+        gpu = read_planes(cache, s, 0, T)
+        qk, kr, vt, _ = oracle_rows(hl, k[b, h], v[b, h])
+        par = compare_keys(hl, k[b, h], qk, gpu)
+        assert par.idx_mismatch_outside == 0, par
+        assert par.sign_mismatch_outside == 0, par
+        np.testing.assert_allclose(gpu["norm"], qk.norm, rtol=2e-6, atol=0)
+        idx = olay.unpack_code_planes(gpu["codes"], d, w)
+        bits = olay.unpack_bits(gpu["signs"], m)
+        refs.append(((idx, bits, gpu["norm"].astype(np.float64), gpu["rnorm"].astype(np.float64)), vt))
+    q = np.random.default_rng(33).standard_normal((B, H * G, d)).astype(np.float32)
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, torch.from_numpy(q).to(dev))
+    out = aqkv.decode_attention(cfg, layer, cache, B, H * G, H, T, q_rot, q_sk).cpu().numpy()
+    worst = 0.0
+    for s in range(B * H):
+        b, h = divmod(s, H)
+        _, o_ref = oatt.decode_slot(q[b, h * G:(h + 1) * G], refs[s][0], refs[s][1], hl.rotation, hl.sketch,
+                                    hl.centroids, w)
+        worst = max(worst, float(np.max(np.abs(out[b, h * G:(h + 1) * G] - o_ref))))
+    say(f"out err {worst:.2e}")
+    assert worst <= OUT_ATOL
+
+
 @pytest.mark.parametrize("d,w,m,nt", [(128, 2, 128, 1), (128, 2, 128, 7), (256, 3, 256, 5), (128, 0, 512, 3)])
 def test_quantize_keys_small_append_many_slots(d, w, m, nt):
     """Decode-time appends: a few tokens for each of many slots, so one key
