@@ -90,3 +90,50 @@ def decode_slot_window(q, key_rows, value_rows, k_win, v_win, rotation, sketch, 
     if s.shape[1] == 0:
         return s_win, np.zeros((G, d))
     return s_win, softmax_attention(s, v, softmax_scale)
+
+
+def selection_query(q):
+    """QUOKA article §1 (pre-aggregation over the KV heads, cosine scoring): the
+    G query heads that share a KV head are reduced to one selection query, the
+    sum of their unit vectors, so that <q_sel, k>/||k|| is the sum of the heads'
+    cosine similarities with k times 1/||k|| -- a ranking by the group's mean
+    cosine.  q [G, d] -> [d] (float64); a zero head contributes nothing."""
+    q = np.asarray(q, dtype=np.float64)
+    n = np.linalg.norm(q, axis=1, keepdims=True)
+    u = np.divide(q, n, out=np.zeros_like(q), where=n > 0)
+    return u.sum(axis=0)
+
+
+def select_top_k(q, key_rows, rotation, sketch, centroids, w: int, budget: int):
+    """QUOKA article §1 (dynamic top-K KV selection): the `budget` cached tokens
+    with the largest cosine score cos_t = <q_sel, k^_t> / ||k_t|| (k^ the
+    dequantised key, ||k_t|| its stored norm; 0 for a zero key), ties to the
+    lower token index.  Returns the chosen token indices in increasing order
+    and the cosine scores [T]."""
+    q_sel = selection_query(q)
+    norm = np.asarray(key_rows[2], dtype=np.float64)
+    T = norm.shape[0]
+    s = scores(q_sel[None, :], key_rows, rotation, sketch, centroids, w)[0] if T else np.zeros(0)
+    cos = np.divide(s, norm, out=np.zeros_like(s), where=norm > 0)
+    k = min(int(budget), T)
+    order = np.argsort(-cos, kind="stable")[:k]
+    return np.sort(order), cos
+
+
+def decode_slot_top_k(q, key_rows, value_rows, rotation, sketch, centroids, w: int, budget: int,
+                      softmax_scale=None, group: int = 32):
+    """Decode attention of the G query heads of one KV slot over the QUOKA
+    selection of at most `budget` tokens only.  Returns (chosen indices, out [G, d])."""
+    sel, _ = select_top_k(q, key_rows, rotation, sketch, centroids, w, budget)
+    sub_k = tuple(np.asarray(a)[sel] for a in key_rows)
+    sub_v = _value_rows_subset(value_rows, sel)
+    q = np.asarray(q, dtype=np.float64)
+    if sel.size == 0:
+        return sel, np.zeros_like(q)
+    _, out = decode_slot(q, sub_k, sub_v, rotation, sketch, centroids, w, softmax_scale, group)
+    return sel, out
+
+
+def _value_rows_subset(value_rows, sel):
+    codes, scale, vmin = value_rows
+    return (np.asarray(codes)[sel], np.asarray(scale)[sel], np.asarray(vmin)[sel])

@@ -192,3 +192,54 @@ def test_window_empty_and_order():
     empty = (kr[0][:0], kr[1][:0], kr[2][:0], kr[3][:0])
     _, out3 = attention.decode_slot_window(q, empty, tuple(a[:0] for a in vr), kw[:0], vw[:0], pi, s, c, w)
     assert np.all(out3 == 0)
+
+
+def _topk_case(seed, T=200, G=4, d=128, w=2):
+    pi, s, c, t = _params(d, w, d)
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d))
+    v = rng.standard_normal((T, d)).astype(np.float32)
+    q = rng.standard_normal((G, d))
+    return q, x, v, (pi, s, c, t, w)
+
+
+def test_top_k_with_a_full_budget_is_full_attention():
+    q, x, v, (pi, s, c, t, w) = _topk_case(20)
+    qk = keys.quantize_keys(x, pi, s, c, t, w)
+    kr = (qk.idx, qk.bits, qk.norm, qk.rnorm)
+    vr = values.quantize_values(v)
+    sel, out = attention.decode_slot_top_k(q, kr, vr, pi, s, c, w, budget=len(x) + 5)
+    np.testing.assert_array_equal(sel, np.arange(len(x)))
+    np.testing.assert_allclose(out, attention.decode_slot(q, kr, vr, pi, s, c, w)[1], rtol=1e-13)
+
+
+def test_top_k_ranks_by_the_groups_summed_cosine():
+    # the selection query's score / ||k|| equals the sum over the heads of each head's
+    # estimated cosine (scores() per head, divided by both norms)
+    q, x, v, (pi, s, c, t, w) = _topk_case(21)
+    qk = keys.quantize_keys(x, pi, s, c, t, w)
+    kr = (qk.idx, qk.bits, qk.norm, qk.rnorm)
+    sel, cos = attention.select_top_k(q, kr, pi, s, c, w, budget=37)
+    per_head = attention.scores(q, kr, pi, s, c, w) / np.linalg.norm(q, axis=1)[:, None] / qk.norm[None, :]
+    np.testing.assert_allclose(cos, per_head.sum(axis=0), rtol=1e-11, atol=1e-13)
+    assert set(sel) == set(np.argsort(-per_head.sum(axis=0), kind="stable")[:37])
+    assert np.all(np.diff(sel) > 0)
+
+
+def test_top_k_scale_invariance_ties_and_an_aligned_key():
+    q, x, v, (pi, s, c, t, w) = _topk_case(22)
+    x[50] = 3.0 * attention.selection_query(q)          # the group's own direction ranks first
+    x[60] = x[61]                                       # duplicates: the lower index wins the tie
+    qk = keys.quantize_keys(x, pi, s, c, t, w)
+    sel, cos = attention.select_top_k(q, (qk.idx, qk.bits, qk.norm, qk.rnorm), pi, s, c, w, budget=1)
+    assert list(sel) == [50]
+    order = np.argsort(-cos, kind="stable")
+    assert list(order).index(60) < list(order).index(61)
+    # a power-of-two scale of one key changes its norm only: the same cosine, the same choice
+    x2 = x.copy()
+    x2[7] *= 8.0
+    qk2 = keys.quantize_keys(x2, pi, s, c, t, w)
+    sel2, cos2 = attention.select_top_k(q, (qk2.idx, qk2.bits, qk2.norm, qk2.rnorm), pi, s, c, w, budget=40)
+    sel1, cos1 = attention.select_top_k(q, (qk.idx, qk.bits, qk.norm, qk.rnorm), pi, s, c, w, budget=40)
+    np.testing.assert_allclose(cos2, cos1, rtol=1e-12)
+    np.testing.assert_array_equal(sel2, sel1)
