@@ -275,6 +275,33 @@ aqkv_status aqkv_decode_attention_window(const aqkv_config *cfg, const aqkv_laye
                                          float softmax_scale, float *scores, float *out, void *workspace,
                                          size_t workspace_bytes, void *stream);
 
+/* Workspace bytes aqkv_decode_attention_topk needs for these sizes (0 on bad
+ * arguments). */
+size_t aqkv_decode_topk_workspace_bytes(const aqkv_config *cfg, int32_t batch, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int64_t context_len, int64_t budget);
+
+/* Decode attention over a query-aware selection of the cached tokens (QUOKA
+ * article §1: pre-aggregation over the KV heads, cosine-similarity scoring,
+ * dynamic top-K selection).  For every KV slot the query heads that share it
+ * are reduced to one selection query, the sum of their unit vectors; every
+ * cache row t in [0, context_len) is scored by cos_t = est_t / n_t (est_t the
+ * estimator of <q_sel, k_t>, n_t the stored norm; 0 for a zero key), and the
+ * min(budget, context_len) rows with the largest cos_t (ties to the lower
+ * row) are chosen.  Each query head then attends those rows only, exactly as
+ * aqkv_decode_attention attends all of them.  q is the unrotated query
+ * [batch][n_q_heads][d] (dev fp32, contiguous); q_rot and q_sketch are its
+ * aqkv_prepare_query outputs.  selected, if not NULL, receives the chosen rows
+ * of every slot in increasing order ([batch * n_kv_heads][min(budget,
+ * context_len)] int32, dev).  budget in 1..2^20.  workspace (dev, 256-byte
+ * aligned) must hold aqkv_decode_topk_workspace_bytes(...) bytes.  Other rules
+ * as aqkv_decode_attention. */
+aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer *layer,
+                                       const aqkv_cache *cache, int32_t batch, int32_t n_q_heads,
+                                       int32_t n_kv_heads, int64_t context_len, const float *q,
+                                       const float *q_rot, const float *q_sketch, int64_t budget,
+                                       float softmax_scale, int32_t *selected, float *out,
+                                       void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -87,6 +87,12 @@ _SIGS = {
     "aqkv_prepare_key_operands": (C.c_int, [_P(Config), _P(LayerParams), C.c_void_p, C.c_size_t, C.c_void_p]),
     "aqkv_quantize_keys_prepared": (C.c_int, [_P(Config), _P(LayerParams), _P(KvView), C.c_int64, _P(CacheDesc),
                                               C.c_void_p, C.c_size_t, C.c_void_p]),
+    "aqkv_decode_topk_workspace_bytes": (C.c_size_t, [_P(Config), C.c_int32, C.c_int32, C.c_int32, C.c_int64,
+                                                     C.c_int64]),
+    "aqkv_decode_attention_topk": (C.c_int, [_P(Config), _P(LayerParams), _P(CacheDesc), C.c_int32, C.c_int32,
+                                             C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
+                                             C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                             C.c_void_p]),
     "aqkv_quantize_values": (C.c_int, [_P(Config), _P(KvView), C.c_int64, _P(CacheDesc), C.c_void_p]),
     "aqkv_prepare_query": (C.c_int, [_P(Config), _P(LayerParams), C.c_void_p, C.c_int, C.c_int64,
                                      C.c_void_p, C.c_void_p, C.c_void_p]),
@@ -396,4 +402,31 @@ def decode_attention_window(cfg: Config, layer: Layer, cache: Cache, batch: int,
                                             _ptr(scores), _ptr(out), _ptr(workspace), workspace.numel(),
                                             _stream(stream))
     _check(st, "aqkv_decode_attention_window")
+    return out
+
+
+def decode_topk_workspace_bytes(cfg: Config, batch: int, n_q_heads: int, n_kv_heads: int, context_len: int,
+                                budget: int) -> int:
+    return int(lib().aqkv_decode_topk_workspace_bytes(C.byref(cfg), batch, n_q_heads, n_kv_heads, context_len,
+                                                      budget))
+
+
+def decode_attention_topk(cfg: Config, layer: Layer, cache: Cache, batch: int, n_q_heads: int, n_kv_heads: int,
+                          context_len: int, q, q_rot, q_sketch, budget: int, softmax_scale: Optional[float] = None,
+                          selected=None, out=None, workspace=None, stream=None):
+    """Decode over the `budget` cached tokens per KV slot with the largest group cosine (q: unrotated fp32)."""
+    import torch
+    dev = q_sketch.device
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(np.sqrt(cfg.head_dim))
+    if out is None:
+        out = torch.empty((batch, n_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    if workspace is None:
+        ws_bytes = decode_topk_workspace_bytes(cfg, batch, n_q_heads, n_kv_heads, context_len, budget)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    st = lib().aqkv_decode_attention_topk(C.byref(cfg), C.byref(layer.desc()), C.byref(cache.desc()), batch,
+                                          n_q_heads, n_kv_heads, context_len, _ptr(q), _ptr(q_rot), _ptr(q_sketch),
+                                          budget, C.c_float(softmax_scale), _ptr(selected), _ptr(out),
+                                          _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "aqkv_decode_attention_topk")
     return out

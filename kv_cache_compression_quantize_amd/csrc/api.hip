@@ -415,6 +415,154 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
                 scores, out, workspace, workspace_bytes, stream, nullptr);
 }
 
+// Workspace of the top-K decode: the selection query, its rotation and sketch,
+// the selection scores, the scoring decode's output and split workspace, the
+// chosen indices and the chunk partials, each 256-byte aligned.
+struct TopkLayout {
+  size_t qsel, qsel_rot, qsel_sk, scores, dec_out, dec_ws, dec_ws_bytes, sel, acc, ml, total;
+};
+
+static TopkLayout topk_layout(const aqkv_config *cfg, int64_t n_slots, int g, int64_t context, int budget) {
+  const int d = cfg->head_dim, m = cfg->sketch_dim;
+  TopkLayout L{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at += round_up(bytes, 256);
+    return here;
+  };
+  L.qsel = take(sizeof(float) * n_slots * d);
+  L.qsel_rot = take(sizeof(float) * n_slots * d);
+  L.qsel_sk = take(sizeof(float) * n_slots * m);
+  L.scores = take(sizeof(float) * n_slots * context);
+  L.dec_out = take(sizeof(float) * n_slots * d);
+  L.dec_ws_bytes = decode_plan(d, cfg->mse_bits, m, cfg->value_bits, n_slots, 1, context).total_bytes;
+  L.dec_ws = take(L.dec_ws_bytes);
+  L.sel = take(sizeof(int32_t) * n_slots * budget);
+  const int chunks = topk_chunks(budget);
+  L.acc = take(sizeof(float) * n_slots * g * chunks * d);
+  L.ml = take(sizeof(float) * n_slots * g * chunks * 2);
+  L.total = at;
+  return L;
+}
+
+size_t aqkv_decode_topk_workspace_bytes(const aqkv_config *cfg, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int64_t context_len, int64_t budget) {
+  if (check_config(cfg) != AQKV_OK) return 0;
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads || context_len < 0 || budget < 1)
+    return 0;
+  const int64_t n_slots = static_cast<int64_t>(batch) * n_kv_heads;
+  const int k = static_cast<int>(std::min<int64_t>(std::min<int64_t>(budget, context_len), kMaxBudget));
+  return topk_layout(cfg, n_slots, n_q_heads / n_kv_heads, context_len, std::max(k, 1)).total;
+}
+
+aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache,
+                                       int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t context_len,
+                                       const float *q, const float *q_rot, const float *q_sketch, int64_t budget,
+                                       float softmax_scale, int32_t *selected, float *out, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+  aqkv_status st = check_config(cfg);
+  if (st != AQKV_OK) return st;
+  if (!layer) return AQKV_ERR_NULL;
+  if ((st = check_cache_shape(cache)) != AQKV_OK) return st;
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || context_len < 0 || budget < 1) return AQKV_ERR_SHAPE;
+  if (n_q_heads % n_kv_heads) return AQKV_ERR_SHAPE;
+  const int g = n_q_heads / n_kv_heads;
+  if (g > kMaxQPerKv) return AQKV_ERR_UNSUPPORTED;
+  if (budget > kMaxBudget) return AQKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(batch) * n_kv_heads != cache->n_slots) return AQKV_ERR_SHAPE;
+  if (context_len > cache->capacity) return AQKV_ERR_CAPACITY;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return AQKV_ERR_SHAPE;
+  const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
+  if (!decode_supported(d, w, 1, m, cfg->value_bits) && !decode_mfma_supported(d, w, 1, m, cfg->value_bits))
+    return AQKV_ERR_UNSUPPORTED;
+  if (batch == 0) return AQKV_OK;
+  if (!out || !q || !q_sketch || !layer->sketch) return AQKV_ERR_NULL;
+  if (w > 0 && (!q_rot || !layer->centroids || !layer->rotation)) return AQKV_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(q_sketch, 16) || (q_rot && !aligned(q_rot, 16)) ||
+      (selected && !aligned(selected, 4)))
+    return AQKV_ERR_ALIGN;
+  const int k = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(budget, context_len)));
+  const TopkLayout TL = topk_layout(cfg, cache->n_slots, g, context_len, k);
+  if (!workspace || workspace_bytes < TL.total) return AQKV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return AQKV_ERR_ALIGN;
+  char *ws = static_cast<char *>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (context_len == 0) {   // nothing cached: a combine over no parts writes out = 0
+    DecodeJob zj{};
+    zj.d = d;
+    zj.g = g;
+    zj.n_slots = cache->n_slots;
+    zj.part_stride = 0;
+    zj.part_acc = reinterpret_cast<float *>(ws + TL.acc);
+    zj.part_ml = reinterpret_cast<float *>(ws + TL.ml);
+    zj.out = out;
+    return hip_status(launch_combine(zj, s));
+  }
+  if ((st = check_blocks(cache)) != AQKV_OK) return st;
+
+  // 1. the selection query of every KV slot, rotated and sketched
+  float *qsel = reinterpret_cast<float *>(ws + TL.qsel);
+  float *qsel_rot = reinterpret_cast<float *>(ws + TL.qsel_rot);
+  float *qsel_sk = reinterpret_cast<float *>(ws + TL.qsel_sk);
+  if (launch_selection_query(q, cache->n_slots, d, g, qsel, s) != hipSuccess) return AQKV_ERR_HIP;
+  QueryJob qj{};
+  qj.q = qsel;
+  qj.dtype = AQKV_FP32;
+  qj.n_q = cache->n_slots;
+  qj.d = d;
+  qj.w = w;
+  qj.m = m;
+  qj.rotation = layer->rotation;
+  qj.sketch = layer->sketch;
+  qj.q_rot = w > 0 ? qsel_rot : nullptr;
+  qj.q_sketch = qsel_sk;
+  if (launch_prepare_query(qj, s) != hipSuccess) return AQKV_ERR_HIP;
+  // 2. its estimate for every cached token (the decoder's score output, one query per slot)
+  float *scores = reinterpret_cast<float *>(ws + TL.scores);
+  st = decode(cfg, layer, cache, batch, n_kv_heads, n_kv_heads, context_len, w > 0 ? qsel_rot : nullptr, qsel_sk,
+              softmax_scale, scores, reinterpret_cast<float *>(ws + TL.dec_out), ws + TL.dec_ws, TL.dec_ws_bytes,
+              stream, nullptr);
+  if (st != AQKV_OK) return st;
+  // 3. selection and decode over the chosen tokens, then the chunk combine
+  const BlockLayout L = layout_of(cfg);
+  TopkJob tj{};
+  tj.d = d;
+  tj.w = w;
+  tj.m = m;
+  tj.vb = cfg->value_bits;
+  tj.g = g;
+  tj.n_slots = cache->n_slots;
+  tj.capacity = cache->capacity;
+  tj.context = context_len;
+  tj.rec = L.rec;
+  tj.codes = cache->blocks + L.off[F_CODES];
+  tj.signs = cache->blocks + L.off[F_SIGNS];
+  tj.norm = cache->blocks + L.off[F_NORM];
+  tj.rnorm = cache->blocks + L.off[F_RNORM];
+  tj.vcodes = cache->blocks + L.off[F_VCODES];
+  tj.vside = cache->blocks + L.off[F_VSIDE];
+  tj.centroids = layer->centroids;
+  tj.scores = scores;
+  tj.q_rot = q_rot;
+  tj.q_sketch = q_sketch;
+  tj.budget = k;
+  tj.selected = selected ? selected : reinterpret_cast<int32_t *>(ws + TL.sel);
+  tj.softmax_scale = softmax_scale;
+  tj.part_acc = reinterpret_cast<float *>(ws + TL.acc);
+  tj.part_ml = reinterpret_cast<float *>(ws + TL.ml);
+  if (launch_topk(tj, s) != hipSuccess) return AQKV_ERR_HIP;
+  DecodeJob cj{};
+  cj.d = d;
+  cj.g = g;
+  cj.n_slots = cache->n_slots;
+  cj.part_stride = topk_chunks(k);
+  cj.part_acc = tj.part_acc;
+  cj.part_ml = tj.part_ml;
+  cj.out = out;
+  return hip_status(launch_combine(cj, s));
+}
+
 aqkv_status aqkv_decode_attention_window(const aqkv_config *cfg, const aqkv_layer *layer,
                                          const aqkv_cache *cache, int32_t batch, int32_t n_q_heads,
                                          int32_t n_kv_heads, int64_t context_len, const float *q,

@@ -121,6 +121,21 @@ struct WindowJob {
   float softmax_scale;
 };
 
+// Query-aware top-K preselection and decode over the chosen tokens
+constexpr int64_t kMaxBudget = int64_t{1} << 20;
+struct TopkJob {
+  int d, w, m, vb, g;
+  int64_t n_slots, capacity, context, rec;
+  const uint8_t *codes, *signs, *norm, *rnorm, *vcodes, *vside;   // fields at their place in record 0
+  const float *centroids;
+  const float *scores;             // [n_slots][context] estimates for the selection query
+  const float *q_rot, *q_sketch;   // per query head
+  int budget;                      // chosen tokens per slot (1..context)
+  int32_t *selected;               // [n_slots][budget]
+  float softmax_scale;
+  float *part_acc, *part_ml;       // [n_slots*g][topk_chunks(budget)][d], [..][2]
+};
+
 // Decode split-K plan shared by the workspace query and the launch.
 struct DecodePlan {
   bool mfma;             // matrix-core kernel (else the scalar fallback)
@@ -142,6 +157,9 @@ hipError_t launch_quantize_values(const ValueJob &job, hipStream_t stream);
 hipError_t launch_prepare_query(const QueryJob &job, hipStream_t stream);
 hipError_t launch_decode(const DecodeJob &job, hipStream_t stream);
 hipError_t launch_combine(const DecodeJob &job, hipStream_t stream);
+int topk_chunks(int budget);
+hipError_t launch_selection_query(const float *q, int64_t n_slots, int d, int g, float *qsel, hipStream_t stream);
+hipError_t launch_topk(const TopkJob &job, hipStream_t stream);
 // the split combine with a recent-token window merged in (in place of launch_combine)
 hipError_t launch_combine_window(const DecodeJob &job, const WindowJob &wj, hipStream_t stream);
 bool decode_supported(int d, int w, int g, int m, int vb);

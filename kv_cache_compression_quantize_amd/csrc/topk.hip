@@ -1,0 +1,380 @@
+// Query-aware top-K preselection (QUOKA article §1: pre-aggregation over the KV
+// heads, cosine-similarity scoring, dynamic top-K KV selection) on the packed
+// cache, and decode attention over the chosen tokens only.
+//
+//   selection_query_kernel  per KV slot: q_sel = sum of the unit query vectors
+//                           of its query heads
+//   (the estimator of <q_sel, k_t> for every cached token comes from the
+//   decoder's score output)
+//   topk_select_kernel      per KV slot: cos_t = score_t / ||k_t|| (0 for a zero
+//                           key), the `budget` largest by a 4-pass radix select
+//                           on order-preserving keys (ties to the lower token),
+//                           written as increasing token indices
+//   sparse_decode_kernel    per (KV slot, chunk of 64 chosen tokens): the chosen
+//                           rows are gathered from their block records into LDS
+//                           (key planes, signs, norms, value codes, scale and
+//                           min), scored for every query head of the slot with
+//                           the estimator, and reduced to a split partial
+//                           (max, sum, weighted value sum); the split combine
+//                           merges the chunks.
+#include "internal.h"
+
+namespace aqkv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kSqrtHalfPi = 1.2533141373155003f;   // sqrt(pi / 2)
+constexpr int kThreads = 256;
+constexpr int kChunkTokens = 64;
+
+__device__ __forceinline__ float block_reduce_sum(float x, float *red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__device__ __forceinline__ uint32_t block_scan_exclusive(uint32_t x, uint32_t *buf, uint32_t *total) {
+  // inclusive scan over the 256 threads in LDS (Hillis-Steele), then shift
+  const int tid = threadIdx.x;
+  __syncthreads();
+  buf[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const uint32_t v = tid >= off ? buf[tid - off] : 0u;
+    __syncthreads();
+    buf[tid] += v;
+    __syncthreads();
+  }
+  *total = buf[kThreads - 1];
+  return buf[tid] - x;
+}
+
+// --------------------------------------------------------------- selection query
+
+__global__ __launch_bounds__(kThreads) void selection_query_kernel(const float *__restrict__ q, int d, int g,
+                                                                   float *__restrict__ qsel) {
+  __shared__ float red[4];
+  const int64_t slot = blockIdx.x;
+  float acc = 0.0f;
+  for (int h = 0; h < g; ++h) {
+    const float *qh = q + (slot * g + h) * d;
+    float ss = 0.0f;
+    for (int j = threadIdx.x; j < d; j += kThreads) ss = fmaf(qh[j], qh[j], ss);
+    const float n = sqrtf(block_reduce_sum(ss, red));
+    const float inv = n > 0.0f ? 1.0f / n : 0.0f;
+    if (threadIdx.x < d) acc = fmaf(qh[threadIdx.x], inv, acc);
+  }
+  if (threadIdx.x < d) qsel[slot * d + threadIdx.x] = acc;
+}
+
+// --------------------------------------------------------------- top-K select
+
+// order-preserving image of a float: larger float -> larger key
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct SelectJob {
+  const float *scores;      // [n_slots][context]
+  const uint8_t *norm;      // key_norm field at its place in record 0
+  int64_t rec, capacity, context;
+  int budget;               // chosen tokens per slot (<= context)
+  int32_t *selected;        // [n_slots][budget]
+};
+
+__device__ __forceinline__ float cosine(const SelectJob &j, int64_t slot, int64_t t) {
+  const float n = *reinterpret_cast<const float *>(j.norm + rec_row(slot * j.capacity + t, 4, j.rec));
+  const float s = j.scores[slot * j.context + t];
+  return n > 0.0f ? s / n : 0.0f;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob job) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t scan[kThreads];
+  __shared__ uint32_t pick[2];
+  const int64_t slot = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t T = job.context;
+  uint32_t prefix = 0, mask = 0;
+  uint32_t need = static_cast<uint32_t>(job.budget);   // still to choose among keys matching prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int64_t t = tid; t < T; t += kThreads) {
+      const uint32_t k = order_key(cosine(job, slot, t));
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      // the digit whose bin holds the need-th largest remaining key
+      uint32_t above = 0;
+      int b = 255;
+      for (; b > 0; --b) {
+        if (above + hist[b] >= need) break;
+        above += hist[b];
+      }
+      pick[0] = static_cast<uint32_t>(b);
+      pick[1] = above;
+    }
+    __syncthreads();
+    prefix |= pick[0] << shift;
+    mask |= 255u << shift;
+    need -= pick[1];
+    __syncthreads();
+  }
+  // keys > prefix are all chosen; of the keys == prefix, the first `need` in token order
+  const int64_t per = (T + kThreads - 1) / kThreads;
+  const int64_t t0 = tid * per, t1 = min<int64_t>(T, t0 + per);
+  uint32_t gt = 0, eq = 0;
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint32_t k = order_key(cosine(job, slot, t));
+    gt += k > prefix;
+    eq += k == prefix;
+  }
+  uint32_t total;
+  const uint32_t eq_before = block_scan_exclusive(eq, scan, &total);
+  const uint32_t eq_take = eq_before >= need ? 0u : min(eq, need - eq_before);
+  const uint32_t base = block_scan_exclusive(gt + eq_take, scan, &total);
+  int32_t *out = job.selected + slot * job.budget;
+  uint32_t pos = base, eq_seen = 0;
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint32_t k = order_key(cosine(job, slot, t));
+    bool take = k > prefix;
+    if (k == prefix) take = eq_seen++ < eq_take;
+    if (take) out[pos++] = static_cast<int32_t>(t);
+  }
+}
+
+// --------------------------------------------------------------- sparse decode
+
+struct SparseJob {
+  int d, w, m, vb, g;
+  int64_t capacity, rec;
+  const uint8_t *codes, *signs, *norm, *rnorm, *vcodes, *vside;   // fields at their place in record 0
+  const float *centroids;
+  const float *q_rot, *q_sketch;   // [n_slots*g][d], [n_slots*g][m]
+  const int32_t *selected;         // [n_slots][budget]
+  int budget, n_chunks;
+  int64_t context;
+  float softmax_scale;
+  float *part_acc, *part_ml;       // [n_slots*g][n_chunks][d], [..][2]
+};
+
+// bit j of a bit row (32-bit words of 32 elements, element 4 i + k at bit 8 k + i)
+__device__ __forceinline__ uint32_t row_bit(const uint32_t *row, int j) {
+  const int jj = j & 31;
+  return (row[j >> 5] >> (8 * (jj & 3) + (jj >> 2))) & 1u;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void sparse_decode_kernel(SparseJob job) {
+  constexpr int T = kChunkTokens;
+  constexpr int kGroups = D / 32;
+  extern __shared__ uint32_t sm[];
+  const int W = job.w, M = job.m, G = job.g, VB = job.vb;
+  const int kw = W * D / 32;                      // key-code words per token
+  const int sw = M / 32;                          // sign words per token
+  uint32_t *kc = sm;                              // [T][kw]
+  uint32_t *sg = kc + T * kw;                     // [T][sw]
+  float *nr = reinterpret_cast<float *>(sg + T * sw);   // [T][2]: n, gamma
+  uint8_t *vc = reinterpret_cast<uint8_t *>(nr + 2 * T);   // [T][D] value codes
+  float *vsd = reinterpret_cast<float *>(vc + T * D);      // [T][kGroups][2] scale, min
+  float *lg = vsd + T * kGroups * 2;              // [G][T] logits, then weights
+  __shared__ float stat[2 * kMaxQPerKv];
+  __shared__ float cen[8];
+  const int tid = threadIdx.x;
+  if (tid < (1 << W)) cen[tid] = job.centroids[tid];
+  const int64_t slot = blockIdx.x / job.n_chunks;
+  const int chunk = static_cast<int>(blockIdx.x % job.n_chunks);
+  const int c0 = chunk * T;
+  const int nt = min(T, job.budget - c0);
+  const int32_t *sel_in = job.selected + slot * job.budget + c0;
+  // the chosen rows, clamped into the context (the select kernel writes them in
+  // range; the clamp keeps every gather inside the slot's records regardless)
+  __shared__ int32_t sel[T];
+  if (tid < nt) sel[tid] = min(max(sel_in[tid], 0), static_cast<int32_t>(job.context - 1));
+  __syncthreads();
+
+  // 1. gather the chosen rows
+  for (int i = tid; i < nt * kw; i += kThreads) {
+    const int t = i / kw, wd = i % kw;
+    const int64_t row = slot * job.capacity + sel[t];
+    kc[i] = reinterpret_cast<const uint32_t *>(job.codes + rec_row(row, W * D / 8, job.rec))[wd];
+  }
+  for (int i = tid; i < nt * sw; i += kThreads) {
+    const int t = i / sw, wd = i % sw;
+    const int64_t row = slot * job.capacity + sel[t];
+    sg[i] = reinterpret_cast<const uint32_t *>(job.signs + rec_row(row, M / 8, job.rec))[wd];
+  }
+  for (int t = tid; t < nt; t += kThreads) {
+    const int64_t row = slot * job.capacity + sel[t];
+    nr[2 * t] = *reinterpret_cast<const float *>(job.norm + rec_row(row, 4, job.rec));
+    nr[2 * t + 1] = W > 0 ? *reinterpret_cast<const float *>(job.rnorm + rec_row(row, 4, job.rec)) : 0.0f;
+  }
+  for (int i = tid; i < nt * D; i += kThreads) {
+    const int t = i / D, ch = i % D;
+    const int64_t ct = sel[t];
+    const int64_t row = slot * job.capacity + ct;
+    const int tt = static_cast<int>(ct & 31), r = tt & 3, ii = tt >> 2;
+    const int grp = ch >> 5, half = (ch >> 4) & 1, n = ch & 15;
+    const uint32_t *blk = reinterpret_cast<const uint32_t *>(job.vcodes + rec_row(row - tt, D * VB / 8, job.rec));
+    uint32_t code;
+    if (VB == 2) {
+      const uint32_t wv = blk[(16 * grp + n) * 4 + r];
+      code = (wv >> (8 * half + 16 * (ii & 1) + 2 * (ii >> 1))) & 3u;
+    } else {
+      const uint32_t wv = blk[((16 * grp + n) * 4 + r) * 2 + half];
+      code = (wv >> (16 * (ii & 1) + 4 * (ii >> 1))) & 15u;
+    }
+    vc[i] = static_cast<uint8_t>(code);
+  }
+  for (int i = tid; i < nt * kGroups * 2; i += kThreads) {
+    const int t = i / (kGroups * 2), gj = i % (kGroups * 2);
+    const int64_t ct = sel[t];
+    const int64_t row = slot * job.capacity + ct;
+    const int tt = static_cast<int>(ct & 31);
+    const float *side = reinterpret_cast<const float *>(job.vside + rec_row(row - tt, 0, job.rec));
+    vsd[i] = side[side_index(gj >> 1, tt, gj & 1)];
+  }
+  __syncthreads();
+
+  // 2. the estimator for every (query head, chosen token): n <q_rot, c[idx]> + sqrt(pi/2)/m gamma <q_sk, 2 b - 1>
+  const float qjl = kSqrtHalfPi / static_cast<float>(M);
+  const float lscale = job.softmax_scale * kLog2e;
+  for (int i = tid; i < G * T; i += kThreads) {
+    const int h = i / T, t = i % T;
+    if (t >= nt) {
+      lg[i] = -INFINITY;
+      continue;
+    }
+    const int64_t head = slot * G + h;
+    float mse = 0.0f;
+    if (W > 0) {
+      const float *qr = job.q_rot + head * D;
+      const uint32_t *kt = kc + t * kw;
+      for (int j = 0; j < D; ++j) {
+        int idx = 0;
+        for (int p = 0; p < W; ++p) idx |= static_cast<int>(row_bit(kt + p * (D / 32), j)) << p;
+        mse = fmaf(qr[j], cen[idx], mse);
+      }
+    }
+    const float *qs = job.q_sketch + head * M;
+    const uint32_t *st = sg + t * sw;
+    float sk = 0.0f;
+    for (int j = 0; j < M; ++j) sk += row_bit(st, j) ? qs[j] : -qs[j];
+    const float score = W > 0 ? nr[2 * t] * mse + qjl * nr[2 * t + 1] * sk : qjl * nr[2 * t] * sk;
+    lg[i] = score * lscale;
+  }
+  __syncthreads();
+
+  // 3. per head: max, weights, sum, weighted value sum -> the chunk's partial
+  for (int h = 0; h < G; ++h) {
+    if (tid < 64) {
+      float mx = tid < nt ? lg[h * T + tid] : -INFINITY;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float p = tid < nt ? __builtin_amdgcn_exp2f(lg[h * T + tid] - mx) : 0.0f;
+      lg[h * T + tid] = p;
+      float l = p;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+      if (tid == 0) {
+        stat[2 * h] = mx;
+        stat[2 * h + 1] = l;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int h = i / D, ch = i % D;
+    const int grp = ch >> 5;
+    float o = 0.0f;
+    for (int t = 0; t < nt; ++t) {
+      const float v = fmaf(static_cast<float>(vc[t * D + ch]), vsd[(t * kGroups + grp) * 2], vsd[(t * kGroups + grp) * 2 + 1]);
+      o = fmaf(lg[h * T + t], v, o);
+    }
+    const int64_t ph = (slot * G + h) * job.n_chunks + chunk;
+    job.part_acc[ph * D + ch] = o;
+    if (ch == 0) {
+      job.part_ml[ph * 2] = stat[2 * h];
+      job.part_ml[ph * 2 + 1] = stat[2 * h + 1];
+    }
+  }
+}
+
+template <int D>
+size_t sparse_smem(int w, int m, int g) {
+  constexpr int T = kChunkTokens;
+  return 4 * static_cast<size_t>(T) * (w * D / 32 + m / 32 + 2) + static_cast<size_t>(T) * D +
+         4 * static_cast<size_t>(T) * (D / 32) * 2 + 4 * static_cast<size_t>(g) * T;
+}
+
+template <int D>
+hipError_t launch_sparse_d(const SparseJob &job, int64_t n_slots, hipStream_t stream) {
+  const size_t smem = sparse_smem<D>(job.w, job.m, job.g);
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sparse_decode_kernel<D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    if (e != hipSuccess) return e;
+  }
+  sparse_decode_kernel<D><<<static_cast<unsigned>(n_slots * job.n_chunks), kThreads, smem, stream>>>(job);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int topk_chunks(int budget) { return (budget + kChunkTokens - 1) / kChunkTokens; }
+
+hipError_t launch_selection_query(const float *q, int64_t n_slots, int d, int g, float *qsel, hipStream_t stream) {
+  selection_query_kernel<<<static_cast<unsigned>(n_slots), kThreads, 0, stream>>>(q, d, g, qsel);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkJob &j, hipStream_t stream) {
+  SelectJob s{};
+  s.scores = j.scores;
+  s.norm = j.norm;
+  s.rec = j.rec;
+  s.capacity = j.capacity;
+  s.context = j.context;
+  s.budget = j.budget;
+  s.selected = j.selected;
+  topk_select_kernel<<<static_cast<unsigned>(j.n_slots), kThreads, 0, stream>>>(s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SparseJob p{};
+  p.d = j.d;
+  p.w = j.w;
+  p.m = j.m;
+  p.vb = j.vb;
+  p.g = j.g;
+  p.capacity = j.capacity;
+  p.rec = j.rec;
+  p.codes = j.codes;
+  p.signs = j.signs;
+  p.norm = j.norm;
+  p.rnorm = j.rnorm;
+  p.vcodes = j.vcodes;
+  p.vside = j.vside;
+  p.centroids = j.centroids;
+  p.q_rot = j.q_rot;
+  p.q_sketch = j.q_sketch;
+  p.selected = j.selected;
+  p.budget = j.budget;
+  p.n_chunks = topk_chunks(j.budget);
+  p.context = j.context;
+  p.softmax_scale = j.softmax_scale;
+  p.part_acc = j.part_acc;
+  p.part_ml = j.part_ml;
+  switch (j.d) {
+    case 64: return launch_sparse_d<64>(p, j.n_slots, stream);
+    case 128: return launch_sparse_d<128>(p, j.n_slots, stream);
+    default: return launch_sparse_d<256>(p, j.n_slots, stream);
+  }
+}
+
+}  // namespace aqkv

@@ -240,3 +240,23 @@ def test_library_hadamard_rotation_equals_oracle(d):
     with pytest.raises(aqkv.AqkvError) as e:
         aqkv.build_hadamard_rotation(np.zeros((96, 96)))
     assert e.value.status == -2
+
+
+def test_decode_topk_validation_codes():
+    lib = aqkv.lib()
+    cfg = aqkv.config(128, 2, 128)
+    layer = aqkv.LayerParams(FAKE, FAKE, FAKE, FAKE)
+    need = aqkv.decode_topk_workspace_bytes(cfg, 1, 4, 2, 64, 16)
+    assert need > 0 and need % 256 == 0
+    assert aqkv.decode_topk_workspace_bytes(cfg, 1, 4, 2, 64, 0) == 0
+
+    def call(budget=16, q=FAKE, hq=4, ws=need):
+        return lib.aqkv_decode_attention_topk(C.byref(cfg), C.byref(layer), C.byref(_cache()), 1, hq, 2, 64, q,
+                                              FAKE, FAKE, budget, C.c_float(0.1), None, FAKE, FAKE, ws, None)
+
+    assert call(budget=0) == -2
+    assert call(budget=(1 << 20) + 1) == -8
+    assert call(q=None) == -1
+    assert call(q=FAKE + 4) == -3
+    assert call(hq=5) == -2
+    assert call(ws=need - 1) == -5

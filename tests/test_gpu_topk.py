@@ -1,0 +1,83 @@
+"""GPU parity of query-aware top-K preselection and decode over the chosen
+tokens, through the C ABI, against the oracle on the same seeded inputs (the
+cache planes quantised by the oracle and uploaded).
+
+Bars: the chosen sets agree except for tokens whose oracle cosine lies within
+2e-3 x RMS of the selection threshold (estimates agree to ~1e-4 relative, so
+near-ties may swap); outputs, computed by the oracle over the GPU's chosen
+set, within 2e-3 absolute."""
+import numpy as np
+import pytest
+
+from kv_cache_compression_quantize_amd import aqkv
+from oracle import attention as oatt
+
+from gpu_helpers import OUT_ATOL, cfg_of, device_layer, host_layer, say, torch_dev
+from test_gpu_parity import _upload_oracle_cache
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # d, w, m, G, T, budget
+    (128, 2, 128, 4, 1000, 100), (128, 2, 128, 1, 700, 64), (128, 2, 128, 8, 2050, 1), (256, 3, 256, 2, 300, 129),
+    (128, 0, 192, 4, 513, 200), (64, 1, 64, 2, 400, 65), (128, 2, 128, 4, 300, 1000),
+]
+
+
+@pytest.mark.parametrize("d,w,m,G,T,budget", CASES)
+def test_topk_selection_and_decode(d, w, m, G, T, budget):
+    torch, dev = torch_dev()
+    say("top-k", d, w, m, G, T, budget)
+    B, Hkv = 2, 2
+    Hq = Hkv * G
+    hl = host_layer(d, w, m, layer=6)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    rng = np.random.default_rng(d + T + budget)
+    ks = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(B * Hkv)]
+    vs = [(rng.standard_normal((T, d)) * 2).astype(np.float32) for _ in range(B * Hkv)]
+    cache, refs = _upload_oracle_cache(hl, cfg, ks, vs, 2, capacity=T + 3)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    qd = torch.from_numpy(q).to(dev)
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, qd)
+    K = min(budget, T)
+    sel = torch.full((B * Hkv, K), -1, dtype=torch.int32, device=dev)
+    out = aqkv.decode_attention_topk(cfg, layer, cache, B, Hq, Hkv, T, qd, q_rot, q_sk, budget, selected=sel)
+    torch.cuda.synchronize()
+    out, sel = out.cpu().numpy(), sel.cpu().numpy()
+    worst = 0.0
+    swapped = 0
+    for s in range(B * Hkv):
+        b, h = divmod(s, Hkv)
+        qh = q[b, h * G:(h + 1) * G]
+        gs = sel[s]
+        assert np.all(np.diff(gs) > 0) and gs[0] >= 0 and gs[-1] < T
+        osel, cos = oatt.select_top_k(qh, refs[s][0], hl.rotation, hl.sketch, hl.centroids, w, budget)
+        thr = np.sort(cos)[::-1][K - 1]
+        tol = 2e-3 * np.sqrt(np.mean(cos ** 2))
+        diff = np.setxor1d(gs, osel)
+        assert np.all(np.abs(cos[diff] - thr) <= tol), (diff, cos[diff], thr)
+        swapped += diff.size // 2
+        # the output over the GPU's chosen rows
+        sub_k = tuple(np.asarray(a)[gs] for a in refs[s][0])
+        sub_v = tuple(np.asarray(a)[gs] for a in refs[s][1])
+        _, o_ref = oatt.decode_slot(qh, sub_k, sub_v, hl.rotation, hl.sketch, hl.centroids, w)
+        worst = max(worst, float(np.max(np.abs(out[b, h * G:(h + 1) * G] - o_ref))))
+    say(f"out err {worst:.2e}, near-tie swaps {swapped}")
+    assert worst <= OUT_ATOL
+    if K == T:
+        assert swapped == 0
+
+
+def test_topk_empty_context():
+    torch, dev = torch_dev()
+    d, w, m, G = 128, 2, 128, 2
+    hl = host_layer(d, w, m)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    cache = aqkv.Cache.allocate(cfg, 1, 64)
+    q = torch.randn((1, G, d), device=dev)
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, q)
+    out = aqkv.decode_attention_topk(cfg, layer, cache, 1, G, 1, 0, q, q_rot, q_sk, 16)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
