@@ -126,6 +126,11 @@ class Path:
         self.win_v = torch.randn((w.batch, w.n_kv_heads, self.n_window, w.head_dim), generator=g,
                                  device=dev).to(torch.bfloat16)
         self.q_f32 = self.x["q"].float().contiguous()
+        # query-aware top-K preselection with QUOKA's budget rule min(4096, max(1024, T / 8)) (detail timing)
+        self.budget = min(4096, max(1024, w.context // 8))
+        self.tws = torch.empty(max(aqkv.decode_topk_workspace_bytes(self.cfg, w.batch, w.n_q_heads, w.n_kv_heads,
+                                                                    w.context, self.budget), 256),
+                               dtype=torch.uint8, device=dev)
 
     def quantize_keys(self):
         self.aqkv.quantize_keys_prepared(self.cfg, self.layer, self.x["k"], self.cache, self.kws)
@@ -149,6 +154,12 @@ class Path:
         self.aqkv.decode_attention_window(self.cfg, self.layer, self.cache, w.batch, w.n_q_heads, w.n_kv_heads,
                                           w.context, self.q_f32, self.q_rot, self.q_sk, self.win_k, self.win_v,
                                           None, None, self.out, self.dws)
+
+    def decode_topk(self):
+        w = self.w
+        self.aqkv.decode_attention_topk(self.cfg, self.layer, self.cache, w.batch, w.n_q_heads, w.n_kv_heads,
+                                        w.context, self.q_f32, self.q_rot, self.q_sk, self.budget, None, None,
+                                        self.out, self.tws)
 
     def step(self):
         # values and the query do not depend on the keys: they run on a second stream
@@ -186,7 +197,8 @@ def time_calls(path, reps: int) -> dict:
     """Average duration of each call, HIP events on the launch stream."""
     import torch
     stream = torch.cuda.current_stream()
-    names = ["quantize_keys", "quantize_values", "prepare_query", "decode", "prepare_key_operands", "decode_window"]
+    names = ["quantize_keys", "quantize_values", "prepare_query", "decode", "prepare_key_operands", "decode_window",
+             "decode_topk"]
     ev = {n: [] for n in names}
     for _ in range(reps):
         for n in names:
@@ -432,6 +444,7 @@ def main():
             "values_GBps": qv_bytes / (per["quantize_values"] / 1e3) / 1e9}
         rec["decode_window"] = {"window_tokens": path.n_window, "ms": per["decode_window"],
                                 "extra_ms_over_decode": per["decode_window"] - per["decode"]}
+        rec["decode_topk"] = {"budget": path.budget, "ms": per["decode_topk"]}
         rec["prepare_query_ms"] = per["prepare_query"]
         rec["prepare_key_operands_ms_once_per_layer"] = per["prepare_key_operands"]
         dominant = max(["decode", "quantize_keys", "quantize_values"], key=lambda n: per[n])

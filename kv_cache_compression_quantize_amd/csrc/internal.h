@@ -128,7 +128,7 @@ struct TopkJob {
   int64_t n_slots, capacity, context, rec;
   const uint8_t *codes, *signs, *norm, *rnorm, *vcodes, *vside;   // fields at their place in record 0
   const float *centroids;
-  const float *scores;             // [n_slots][context] estimates for the selection query
+  float *scores;                   // [n_slots][context] estimates for the selection query (overwritten)
   const float *q_rot, *q_sketch;   // per query head
   int budget;                      // chosen tokens per slot (1..context)
   int32_t *selected;               // [n_slots][budget]

@@ -6,10 +6,10 @@
 //                           of its query heads
 //   (the estimator of <q_sel, k_t> for every cached token comes from the
 //   decoder's score output)
-//   topk_select_kernel      per KV slot: cos_t = score_t / ||k_t|| (0 for a zero
-//                           key), the `budget` largest by a 4-pass radix select
-//                           on order-preserving keys (ties to the lower token),
-//                           written as increasing token indices
+//   topk_select_kernel      per KV slot (1024 threads): cos_t = score_t / ||k_t||
+//                           (0 for a zero key) as order-preserving keys, the
+//                           `budget` largest by a 4-pass radix select (ties to
+//                           the lower token), written as increasing token indices
 //   sparse_decode_kernel    per (KV slot, chunk of 64 chosen tokens): the chosen
 //                           rows are gathered from their block records into LDS
 //                           (key planes, signs, norms, value codes, scale and
@@ -34,22 +34,6 @@ __device__ __forceinline__ float block_reduce_sum(float x, float *red) {
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
   return (red[0] + red[1]) + (red[2] + red[3]);
-}
-
-__device__ __forceinline__ uint32_t block_scan_exclusive(uint32_t x, uint32_t *buf, uint32_t *total) {
-  // inclusive scan over the 256 threads in LDS (Hillis-Steele), then shift
-  const int tid = threadIdx.x;
-  __syncthreads();
-  buf[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const uint32_t v = tid >= off ? buf[tid - off] : 0u;
-    __syncthreads();
-    buf[tid] += v;
-    __syncthreads();
-  }
-  *total = buf[kThreads - 1];
-  return buf[tid] - x;
 }
 
 // --------------------------------------------------------------- selection query
@@ -79,45 +63,72 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 struct SelectJob {
-  const float *scores;      // [n_slots][context]
+  float *scores;            // [n_slots][context]; overwritten with the order keys
   const uint8_t *norm;      // key_norm field at its place in record 0
   int64_t rec, capacity, context;
   int budget;               // chosen tokens per slot (<= context)
   int32_t *selected;        // [n_slots][budget]
 };
 
-__device__ __forceinline__ float cosine(const SelectJob &j, int64_t slot, int64_t t) {
-  const float n = *reinterpret_cast<const float *>(j.norm + rec_row(slot * j.capacity + t, 4, j.rec));
-  const float s = j.scores[slot * j.context + t];
-  return n > 0.0f ? s / n : 0.0f;
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int64_t kLdsKeys = 32768;       // slots of at most this many tokens keep their keys in LDS
+
+__device__ __forceinline__ uint32_t block_scan_1024(uint32_t x, uint32_t *buf) {
+  // exclusive scan over the 1024 threads (Hillis-Steele in LDS)
+  const int tid = threadIdx.x;
+  __syncthreads();
+  buf[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < kSelThreads; off <<= 1) {
+    const uint32_t v = tid >= off ? buf[tid - off] : 0u;
+    __syncthreads();
+    buf[tid] += v;
+    __syncthreads();
+  }
+  return buf[tid] - x;
 }
 
-__global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob job) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t scan[kThreads];
+// KEYS_LDS: the slot's keys live in dynamic LDS, else in place of its scores
+template <bool KEYS_LDS>
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job) {
+  extern __shared__ uint32_t lds_keys[];
+  __shared__ uint32_t hist[kSelWaves][256];   // one histogram per wave: no cross-wave atomic contention
+  __shared__ uint32_t scan[kSelThreads];
   __shared__ uint32_t pick[2];
   const int64_t slot = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t T = job.context;
+  uint32_t *keys = KEYS_LDS ? lds_keys : reinterpret_cast<uint32_t *>(job.scores + slot * T);
+  // 1. cos_t = score_t / n_t (0 for a zero key) as order-preserving keys
+#pragma unroll 8
+  for (int64_t t = tid; t < T; t += kSelThreads) {
+    const float n = *reinterpret_cast<const float *>(job.norm + rec_row(slot * job.capacity + t, 4, job.rec));
+    const float sc = job.scores[slot * T + t];
+    keys[t] = order_key(n > 0.0f ? sc / n : 0.0f);
+  }
+  __syncthreads();
+  // 2. radix select of the budget-th largest key, 8 bits a pass from the top
   uint32_t prefix = 0, mask = 0;
   uint32_t need = static_cast<uint32_t>(job.budget);   // still to choose among keys matching prefix
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int64_t t = tid; t < T; t += kThreads) {
-      const uint32_t k = order_key(cosine(job, slot, t));
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    for (int64_t t = tid; t < T; t += kSelThreads) {
+      const uint32_t k = keys[t];
+      if ((k & mask) == prefix) atomicAdd(&hist[wave][(k >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      // the digit whose bin holds the need-th largest remaining key
-      uint32_t above = 0;
-      int b = 255;
-      for (; b > 0; --b) {
-        if (above + hist[b] >= need) break;
-        above += hist[b];
-      }
-      pick[0] = static_cast<uint32_t>(b);
+    // thread i holds bin 255 - i: the exclusive scan gives the count in the bins above it,
+    // and the one bin where that count is below `need` and reaches it with its own is the digit
+    uint32_t c = 0;
+    if (tid < 256) {
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) c += hist[w][255 - tid];
+    }
+    const uint32_t above = block_scan_1024(c, scan);
+    if (tid < 256 && above < need && above + c >= need) {
+      pick[0] = static_cast<uint32_t>(255 - tid);
       pick[1] = above;
     }
     __syncthreads();
@@ -126,23 +137,23 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(SelectJob job) {
     need -= pick[1];
     __syncthreads();
   }
-  // keys > prefix are all chosen; of the keys == prefix, the first `need` in token order
-  const int64_t per = (T + kThreads - 1) / kThreads;
+  // 3. keys > prefix are all chosen; of the keys == prefix, the first `need` in token
+  //    order; each thread writes its contiguous range's choices at its scanned offset
+  const int64_t per = (T + kSelThreads - 1) / kSelThreads;
   const int64_t t0 = tid * per, t1 = min<int64_t>(T, t0 + per);
   uint32_t gt = 0, eq = 0;
   for (int64_t t = t0; t < t1; ++t) {
-    const uint32_t k = order_key(cosine(job, slot, t));
+    const uint32_t k = keys[t];
     gt += k > prefix;
     eq += k == prefix;
   }
-  uint32_t total;
-  const uint32_t eq_before = block_scan_exclusive(eq, scan, &total);
+  const uint32_t eq_before = block_scan_1024(eq, scan);
   const uint32_t eq_take = eq_before >= need ? 0u : min(eq, need - eq_before);
-  const uint32_t base = block_scan_exclusive(gt + eq_take, scan, &total);
+  const uint32_t base = block_scan_1024(gt + eq_take, scan);
   int32_t *out = job.selected + slot * job.budget;
   uint32_t pos = base, eq_seen = 0;
   for (int64_t t = t0; t < t1; ++t) {
-    const uint32_t k = order_key(cosine(job, slot, t));
+    const uint32_t k = keys[t];
     bool take = k > prefix;
     if (k == prefix) take = eq_seen++ < eq_take;
     if (take) out[pos++] = static_cast<int32_t>(t);
@@ -245,29 +256,36 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(SparseJob job) 
   // 2. the estimator for every (query head, chosen token): n <q_rot, c[idx]> + sqrt(pi/2)/m gamma <q_sk, 2 b - 1>
   const float qjl = kSqrtHalfPi / static_cast<float>(M);
   const float lscale = job.softmax_scale * kLog2e;
-  for (int i = tid; i < G * T; i += kThreads) {
+  // four neighbouring lanes per (head, token), each a quarter of the coordinates and sketch rows
+  const int quarter = tid & 3;
+  for (int i0 = 0; i0 < G * T; i0 += kThreads / 4) {
+    const int i = i0 + (tid >> 2);
     const int h = i / T, t = i % T;
-    if (t >= nt) {
-      lg[i] = -INFINITY;
-      continue;
-    }
-    const int64_t head = slot * G + h;
-    float mse = 0.0f;
-    if (W > 0) {
-      const float *qr = job.q_rot + head * D;
-      const uint32_t *kt = kc + t * kw;
-      for (int j = 0; j < D; ++j) {
-        int idx = 0;
-        for (int p = 0; p < W; ++p) idx |= static_cast<int>(row_bit(kt + p * (D / 32), j)) << p;
-        mse = fmaf(qr[j], cen[idx], mse);
+    const bool live = i < G * T && t < nt;
+    float mse = 0.0f, sk = 0.0f;
+    if (live) {
+      const int64_t head = slot * G + h;
+      if (W > 0) {
+        const float *qr = job.q_rot + head * D;
+        const uint32_t *kt = kc + t * kw;
+        for (int j = quarter; j < D; j += 4) {
+          int idx = 0;
+          for (int p = 0; p < W; ++p) idx |= static_cast<int>(row_bit(kt + p * (D / 32), j)) << p;
+          mse = fmaf(qr[j], cen[idx], mse);
+        }
       }
+      const float *qs = job.q_sketch + head * M;
+      const uint32_t *st = sg + t * sw;
+      for (int j = quarter; j < M; j += 4) sk += row_bit(st, j) ? qs[j] : -qs[j];
     }
-    const float *qs = job.q_sketch + head * M;
-    const uint32_t *st = sg + t * sw;
-    float sk = 0.0f;
-    for (int j = 0; j < M; ++j) sk += row_bit(st, j) ? qs[j] : -qs[j];
-    const float score = W > 0 ? nr[2 * t] * mse + qjl * nr[2 * t + 1] * sk : qjl * nr[2 * t] * sk;
-    lg[i] = score * lscale;
+    mse += __shfl_xor(mse, 1);
+    mse += __shfl_xor(mse, 2);
+    sk += __shfl_xor(sk, 1);
+    sk += __shfl_xor(sk, 2);
+    if (quarter == 0 && i < G * T) {
+      const float score = W > 0 ? nr[2 * t] * mse + qjl * nr[2 * t + 1] * sk : qjl * nr[2 * t] * sk;
+      lg[i] = live ? score * lscale : -INFINITY;
+    }
   }
   __syncthreads();
 
@@ -343,8 +361,19 @@ hipError_t launch_topk(const TopkJob &j, hipStream_t stream) {
   s.context = j.context;
   s.budget = j.budget;
   s.selected = j.selected;
-  topk_select_kernel<<<static_cast<unsigned>(j.n_slots), kThreads, 0, stream>>>(s);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (j.context <= kLdsKeys) {
+    const size_t smem = sizeof(uint32_t) * static_cast<size_t>(j.context);
+    if (smem > 64 * 1024) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(topk_select_kernel<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+      if (e != hipSuccess) return e;
+    }
+    topk_select_kernel<true><<<static_cast<unsigned>(j.n_slots), kSelThreads, smem, stream>>>(s);
+  } else {
+    topk_select_kernel<false><<<static_cast<unsigned>(j.n_slots), kSelThreads, 0, stream>>>(s);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   SparseJob p{};
   p.d = j.d;
