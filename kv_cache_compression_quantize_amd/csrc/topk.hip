@@ -8,7 +8,7 @@
 //   decoder's score output)
 //   topk_select_kernel      per KV slot (1024 threads): cos_t = score_t / ||k_t||
 //                           (0 for a zero key) as order-preserving keys, the
-//                           `budget` largest by a 4-pass radix select (ties to
+//                           `budget` largest by a 3-pass radix select (ties to
 //                           the lower token), written as increasing token indices
 //   sparse_decode_kernel    per (KV slot, chunk of 64 chosen tokens): the chosen
 //                           rows are gathered from their block records into LDS
@@ -72,91 +72,196 @@ struct SelectJob {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kHistBins = 4096;            // widest digit: 12 bits
 constexpr int64_t kLdsKeys = 32768;       // slots of at most this many tokens keep their keys in LDS
 
-__device__ __forceinline__ uint32_t block_scan_1024(uint32_t x, uint32_t *buf) {
-  // exclusive scan over the 1024 threads (Hillis-Steele in LDS)
-  const int tid = threadIdx.x;
-  __syncthreads();
-  buf[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    const uint32_t v = tid >= off ? buf[tid - off] : 0u;
-    __syncthreads();
-    buf[tid] += v;
-    __syncthreads();
+// exclusive scan over the block's threads: a scan within each wave, then the wave totals
+__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t *wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_up(inc, off);
+    if (lane >= off) inc += v;
   }
-  return buf[tid] - x;
+  __syncthreads();   // wsum is free again
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) before += w < wave ? wsum[w] : 0u;
+  return before + inc - x;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
 }
 
 // KEYS_LDS: the slot's keys live in dynamic LDS, else in place of its scores
 template <bool KEYS_LDS>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job) {
-  extern __shared__ uint32_t lds_keys[];
-  __shared__ uint32_t hist[kSelWaves][256];   // one histogram per wave: no cross-wave atomic contention
-  __shared__ uint32_t scan[kSelThreads];
+  extern __shared__ uint4 lds_keys4[];
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t wsum[kSelWaves];
+  __shared__ uint32_t wgt[kSelWaves], weq[kSelWaves];
   __shared__ uint32_t pick[2];
   const int64_t slot = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int64_t T = job.context;
-  uint32_t *keys = KEYS_LDS ? lds_keys : reinterpret_cast<uint32_t *>(job.scores + slot * T);
-  // 1. cos_t = score_t / n_t (0 for a zero key) as order-preserving keys
-#pragma unroll 8
-  for (int64_t t = tid; t < T; t += kSelThreads) {
-    const float n = *reinterpret_cast<const float *>(job.norm + rec_row(slot * job.capacity + t, 4, job.rec));
-    const float sc = job.scores[slot * T + t];
-    keys[t] = order_key(n > 0.0f ? sc / n : 0.0f);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = static_cast<int>(job.context);   // chosen indices are int32, so T < 2^31
+  const float *sc_row = job.scores + slot * job.context;
+  uint32_t *keys = KEYS_LDS ? reinterpret_cast<uint32_t *>(lds_keys4)
+                            : reinterpret_cast<uint32_t *>(job.scores + slot * job.context);
+  // keys 4 q .. 4 q + 3 (a 16-byte read in LDS; in place of the scores, which need not be
+  // 16-byte aligned, four reads)
+  auto quad = [&](int q) -> uint4 {
+    if (KEYS_LDS) return lds_keys4[q];
+    return make_uint4(keys[4 * q], keys[4 * q + 1], keys[4 * q + 2], keys[4 * q + 3]);
+  };
+  // 1. cos_t = score_t / n_t (0 for a zero key) as order-preserving keys; every load of a
+  //    batch is issued before the first is used, so a thread has 2 * kBatch reads in flight
+  constexpr int kBatch = 16;
+  const int64_t row0 = slot * job.capacity;
+  for (int t0 = 0; t0 < T; t0 += kSelThreads * kBatch) {
+    float sc[kBatch], nn[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + u * kSelThreads + tid;
+      sc[u] = t < T ? sc_row[t] : 0.0f;
+      nn[u] = t < T ? *reinterpret_cast<const float *>(job.norm + rec_row(row0 + t, 4, job.rec)) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = t0 + u * kSelThreads + tid;
+      if (t < T) keys[t] = order_key(nn[u] > 0.0f ? sc[u] / nn[u] : 0.0f);
+    }
   }
-  __syncthreads();
-  // 2. radix select of the budget-th largest key, 8 bits a pass from the top
+  // 2. radix select of the budget-th largest key, digits of 12, 10 and 10 bits from the
+  //    top (cosines share their sign and exponent bits, so a wide first digit spreads them)
+  const int nq = T >> 2;
   uint32_t prefix = 0, mask = 0;
   uint32_t need = static_cast<uint32_t>(job.budget);   // still to choose among keys matching prefix
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+    const int bins = pass == 0 ? kHistBins : 1024;
+    const uint32_t bm = static_cast<uint32_t>(bins - 1);
+    const int per = bins / kSelThreads;
+    __syncthreads();   // keys written, and the previous pass done with hist
+    for (int i = tid; i < bins; i += kSelThreads) hist[i] = 0;
     __syncthreads();
-    for (int64_t t = tid; t < T; t += kSelThreads) {
-      const uint32_t k = keys[t];
-      if ((k & mask) == prefix) atomicAdd(&hist[wave][(k >> shift) & 255u], 1u);
+    auto count = [&](uint32_t k) {
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & bm], 1u);
+    };
+#pragma unroll 2
+    for (int q = tid; q < nq; q += kSelThreads) {
+      const uint4 k = quad(q);
+      count(k.x);
+      count(k.y);
+      count(k.z);
+      count(k.w);
     }
+    if (4 * nq + tid < T) count(keys[4 * nq + tid]);
     __syncthreads();
-    // thread i holds bin 255 - i: the exclusive scan gives the count in the bins above it,
-    // and the one bin where that count is below `need` and reaches it with its own is the digit
+    // thread i holds `per` bins from the top down: the scan gives the count in the bins
+    // above them, and the one thread whose bins take that count to `need` finds the digit
+    const int top = bins - 1 - tid * per;
     uint32_t c = 0;
-    if (tid < 256) {
-#pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) c += hist[w][255 - tid];
-    }
-    const uint32_t above = block_scan_1024(c, scan);
-    if (tid < 256 && above < need && above + c >= need) {
-      pick[0] = static_cast<uint32_t>(255 - tid);
-      pick[1] = above;
+    for (int j = 0; j < per; ++j) c += hist[top - j];
+    uint32_t above = block_scan(c, wsum);
+    if (above < need && above + c >= need) {
+      for (int j = 0; j < per; ++j) {
+        const uint32_t h = hist[top - j];
+        if (above + h >= need) {
+          pick[0] = static_cast<uint32_t>(top - j);
+          pick[1] = above;
+          break;
+        }
+        above += h;
+      }
     }
     __syncthreads();
     prefix |= pick[0] << shift;
-    mask |= 255u << shift;
+    mask |= bm << shift;
     need -= pick[1];
-    __syncthreads();
   }
   // 3. keys > prefix are all chosen; of the keys == prefix, the first `need` in token
-  //    order; each thread writes its contiguous range's choices at its scanned offset
-  const int64_t per = (T + kSelThreads - 1) / kSelThreads;
-  const int64_t t0 = tid * per, t1 = min<int64_t>(T, t0 + per);
+  //    order.  Each wave owns a contiguous run of tokens (a multiple of 256) and takes it
+  //    256 at a time, lane l holding tokens 4 l .. 4 l + 3; choices are ranked by ballot,
+  //    so the output comes out in increasing token order.
+  const int seg = ((T + kSelWaves - 1) / kSelWaves + 255) / 256 * 256;
+  const int s0 = min(T, wave * seg), s1 = min(T, s0 + seg);
+  const uint64_t below = (uint64_t{1} << lane) - 1u;
+  auto lane_keys = [&](int b, uint32_t k[4]) -> int {   // valid keys of the lane at b
+    const int t = b + 4 * lane;
+    if (t + 3 < s1) {
+      const uint4 v = quad(t >> 2);
+      k[0] = v.x;
+      k[1] = v.y;
+      k[2] = v.z;
+      k[3] = v.w;
+      return 4;
+    }
+    const int nv = max(0, s1 - t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[j] = j < nv ? keys[t + j] : 0u;
+    return nv;
+  };
   uint32_t gt = 0, eq = 0;
-  for (int64_t t = t0; t < t1; ++t) {
-    const uint32_t k = keys[t];
-    gt += k > prefix;
-    eq += k == prefix;
+  for (int b = s0; b < s1; b += 256) {
+    uint32_t k[4];
+    const int nv = lane_keys(b, k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      gt += j < nv && k[j] > prefix;
+      eq += j < nv && k[j] == prefix;
+    }
   }
-  const uint32_t eq_before = block_scan_1024(eq, scan);
+  gt = wave_sum(gt);
+  eq = wave_sum(eq);
+  if (lane == 0) {
+    wgt[wave] = gt;
+    weq[wave] = eq;
+  }
+  __syncthreads();
+  uint32_t eq_before = 0, base = 0;
+  for (int w = 0; w < wave; ++w) {
+    const uint32_t take = eq_before >= need ? 0u : min(weq[w], need - eq_before);
+    base += wgt[w] + take;
+    eq_before += weq[w];
+  }
   const uint32_t eq_take = eq_before >= need ? 0u : min(eq, need - eq_before);
-  const uint32_t base = block_scan_1024(gt + eq_take, scan);
   int32_t *out = job.selected + slot * job.budget;
   uint32_t pos = base, eq_seen = 0;
-  for (int64_t t = t0; t < t1; ++t) {
-    const uint32_t k = keys[t];
-    bool take = k > prefix;
-    if (k == prefix) take = eq_seen++ < eq_take;
-    if (take) out[pos++] = static_cast<int32_t>(t);
+  for (int b = s0; b < s1; b += 256) {
+    uint32_t k[4];
+    const int nv = lane_keys(b, k);
+    bool e[4], take[4];
+    uint32_t e_below = 0, e_all = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[j] = j < nv && k[j] == prefix;
+      const uint64_t eb = __ballot(e[j]);
+      e_below += __popcll(eb & below);
+      e_all += __popcll(eb);
+    }
+    uint32_t r = eq_seen + e_below;   // rank among the slot's ties of this lane's next tie
+    uint32_t t_below = 0, t_all = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      take[j] = (j < nv && k[j] > prefix) || (e[j] && r < eq_take);
+      r += e[j];
+      const uint64_t tb = __ballot(take[j]);
+      t_below += __popcll(tb & below);
+      t_all += __popcll(tb);
+    }
+    uint32_t p = pos + t_below;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (take[j]) out[p++] = b + 4 * lane + j;
+    }
+    pos += t_all;
+    eq_seen += e_all;
   }
 }
 
@@ -363,7 +468,7 @@ hipError_t launch_topk(const TopkJob &j, hipStream_t stream) {
   s.selected = j.selected;
   hipError_t e;
   if (j.context <= kLdsKeys) {
-    const size_t smem = sizeof(uint32_t) * static_cast<size_t>(j.context);
+    const size_t smem = sizeof(uint4) * static_cast<size_t>((j.context + 3) / 4);
     if (smem > 64 * 1024) {
       e = hipFuncSetAttribute(reinterpret_cast<const void *>(topk_select_kernel<true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
