@@ -309,7 +309,7 @@ struct WindowArgs {
 static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache, int32_t batch,
                           int32_t n_q_heads, int32_t n_kv_heads, int64_t context_len, const float *q_rot,
                           const float *q_sketch, float softmax_scale, float *scores, float *out, void *workspace,
-                          size_t workspace_bytes, void *stream, const WindowArgs *win) {
+                          size_t workspace_bytes, void *stream, const WindowArgs *win, bool scores_only = false) {
   aqkv_status st = check_config(cfg);
   if (st != AQKV_OK) return st;
   if (!layer) return AQKV_ERR_NULL;
@@ -385,7 +385,8 @@ static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const
     const hipError_t e = plan.mfma ? launch_decode_mfma(job, s) : launch_decode(job, s);
     if (e != hipSuccess) return AQKV_ERR_HIP;
   }
-  if (!win) return hip_status(launch_combine(job, s));
+  // scores_only: the caller wants the score output alone, so the partials are not merged
+  if (!win) return scores_only ? AQKV_OK : hip_status(launch_combine(job, s));
   {
     WindowJob wj{};
     wj.k = win->k->data;
@@ -522,7 +523,7 @@ aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer 
   float *scores = reinterpret_cast<float *>(ws + TL.scores);
   st = decode(cfg, layer, cache, batch, n_kv_heads, n_kv_heads, context_len, w > 0 ? qsel_rot : nullptr, qsel_sk,
               softmax_scale, scores, reinterpret_cast<float *>(ws + TL.dec_out), ws + TL.dec_ws, TL.dec_ws_bytes,
-              stream, nullptr);
+              stream, nullptr, true);
   if (st != AQKV_OK) return st;
   // 3. selection and decode over the chosen tokens, then the chunk combine
   const BlockLayout L = layout_of(cfg);

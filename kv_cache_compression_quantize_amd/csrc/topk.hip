@@ -280,30 +280,65 @@ struct SparseJob {
   float *part_acc, *part_ml;       // [n_slots*g][n_chunks][d], [..][2]
 };
 
-// bit j of a bit row (32-bit words of 32 elements, element 4 i + k at bit 8 k + i)
-__device__ __forceinline__ uint32_t row_bit(const uint32_t *row, int j) {
-  const int jj = j & 31;
-  return (row[j >> 5] >> (8 * (jj & 3) + (jj >> 2))) & 1u;
+constexpr int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
 }
 
-template <int D>
+// centroid of the index whose bits are b0 (bit 0), b1, b2 (W of them); the
+// codebook is held in named registers, so the choice is a chain of selects
+struct Codebook8 {
+  float c0, c1, c2, c3, c4, c5, c6, c7;
+};
+template <int W>
+__device__ __forceinline__ float centroid(const Codebook8 &c, uint32_t b0, uint32_t b1, uint32_t b2) {
+  const float l01 = b0 ? c.c1 : c.c0;
+  if (W == 1) return l01;
+  const float l23 = b0 ? c.c3 : c.c2;
+  const float lo = b1 ? l23 : l01;
+  if (W == 2) return lo;
+  const float l45 = b0 ? c.c5 : c.c4;
+  const float l67 = b0 ? c.c7 : c.c6;
+  const float hi = b1 ? l67 : l45;
+  return b2 ? hi : lo;
+}
+
+// LDS bytes of one block
+template <int D, int W>
+size_t sparse_smem(int m, int g) {
+  constexpr int T = kChunkTokens;
+  return 4 * static_cast<size_t>(T) * (W * D / 32 + m / 32 + 2) +   // key words, sign words, n and gamma
+         static_cast<size_t>(T) * D +                                 // value codes
+         4 * static_cast<size_t>(T) * (D / 32) * 2 +                  // value scale and min
+         4 * static_cast<size_t>(g) * T +                             // logits, then weights
+         4 * static_cast<size_t>(g) * (D + m) +                       // the slot's rotated and sketched queries
+         4 * static_cast<size_t>(kThreads);                           // value partial sums
+}
+
+template <int D, int W>
 __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(SparseJob job) {
   constexpr int T = kChunkTokens;
   constexpr int kGroups = D / 32;
+  constexpr int kWords = D / 32;                  // 32-bit words of one bit plane
+  constexpr int kw = W * kWords;                  // key-code words per token
+  constexpr int kwp = pow2_at_least(kw > 0 ? kw : 1);
   extern __shared__ uint32_t sm[];
-  const int W = job.w, M = job.m, G = job.g, VB = job.vb;
-  const int kw = W * D / 32;                      // key-code words per token
+  const int M = job.m, G = job.g, VB = job.vb;
   const int sw = M / 32;                          // sign words per token
+  const int sws = sw > 1 ? 32 - __clz(sw - 1) : 0;   // ceil(log2(sw))
   uint32_t *kc = sm;                              // [T][kw]
   uint32_t *sg = kc + T * kw;                     // [T][sw]
-  float *nr = reinterpret_cast<float *>(sg + T * sw);   // [T][2]: n, gamma
-  uint8_t *vc = reinterpret_cast<uint8_t *>(nr + 2 * T);   // [T][D] value codes
-  float *vsd = reinterpret_cast<float *>(vc + T * D);      // [T][kGroups][2] scale, min
+  float *nr = reinterpret_cast<float *>(sg + T * sw);     // [T][2]: n, gamma
+  uint8_t *vc = reinterpret_cast<uint8_t *>(nr + 2 * T);  // [T][D] value codes
+  float *vsd = reinterpret_cast<float *>(vc + T * D);     // [T][kGroups][2] scale, min
   float *lg = vsd + T * kGroups * 2;              // [G][T] logits, then weights
+  float *qv = lg + G * T;                         // [G][D + M]: q_rot then q_sketch
+  float *red = qv + G * (D + M);                  // [kThreads] value partial sums
   __shared__ float stat[2 * kMaxQPerKv];
-  __shared__ float cen[8];
+  __shared__ int64_t rbase[T];                    // byte offset of the chosen row's record
+  __shared__ int rtt[T];                          // the row within its record
   const int tid = threadIdx.x;
-  if (tid < (1 << W)) cen[tid] = job.centroids[tid];
   const int64_t slot = blockIdx.x / job.n_chunks;
   const int chunk = static_cast<int>(blockIdx.x % job.n_chunks);
   const int c0 = chunk * T;
@@ -311,57 +346,86 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(SparseJob job) 
   const int32_t *sel_in = job.selected + slot * job.budget + c0;
   // the chosen rows, clamped into the context (the select kernel writes them in
   // range; the clamp keeps every gather inside the slot's records regardless)
-  __shared__ int32_t sel[T];
-  if (tid < nt) sel[tid] = min(max(sel_in[tid], 0), static_cast<int32_t>(job.context - 1));
-  __syncthreads();
-
-  // 1. gather the chosen rows
-  for (int i = tid; i < nt * kw; i += kThreads) {
-    const int t = i / kw, wd = i % kw;
-    const int64_t row = slot * job.capacity + sel[t];
-    kc[i] = reinterpret_cast<const uint32_t *>(job.codes + rec_row(row, W * D / 8, job.rec))[wd];
+  if (tid < nt) {
+    const int64_t row = slot * job.capacity + min(max(sel_in[tid], 0), static_cast<int32_t>(job.context - 1));
+    rbase[tid] = (row >> 5) * job.rec;
+    rtt[tid] = static_cast<int>(row & 31);
   }
-  for (int i = tid; i < nt * sw; i += kThreads) {
-    const int t = i / sw, wd = i % sw;
-    const int64_t row = slot * job.capacity + sel[t];
-    sg[i] = reinterpret_cast<const uint32_t *>(job.signs + rec_row(row, M / 8, job.rec))[wd];
+  // the slot's queries
+  for (int h = 0; h < G; ++h) {
+    const int64_t head = slot * G + h;
+    if (W > 0)
+      for (int j = tid; j < D; j += kThreads) qv[h * (D + M) + j] = job.q_rot[head * D + j];
+    for (int j = tid; j < M; j += kThreads) qv[h * (D + M) + D + j] = job.q_sketch[head * M + j];
   }
-  for (int t = tid; t < nt; t += kThreads) {
-    const int64_t row = slot * job.capacity + sel[t];
-    nr[2 * t] = *reinterpret_cast<const float *>(job.norm + rec_row(row, 4, job.rec));
-    nr[2 * t + 1] = W > 0 ? *reinterpret_cast<const float *>(job.rnorm + rec_row(row, 4, job.rec)) : 0.0f;
-  }
-  for (int i = tid; i < nt * D; i += kThreads) {
-    const int t = i / D, ch = i % D;
-    const int64_t ct = sel[t];
-    const int64_t row = slot * job.capacity + ct;
-    const int tt = static_cast<int>(ct & 31), r = tt & 3, ii = tt >> 2;
-    const int grp = ch >> 5, half = (ch >> 4) & 1, n = ch & 15;
-    const uint32_t *blk = reinterpret_cast<const uint32_t *>(job.vcodes + rec_row(row - tt, D * VB / 8, job.rec));
-    uint32_t code;
-    if (VB == 2) {
-      const uint32_t wv = blk[(16 * grp + n) * 4 + r];
-      code = (wv >> (8 * half + 16 * (ii & 1) + 2 * (ii >> 1))) & 3u;
-    } else {
-      const uint32_t wv = blk[((16 * grp + n) * 4 + r) * 2 + half];
-      code = (wv >> (16 * (ii & 1) + 4 * (ii >> 1))) & 15u;
+  Codebook8 cen{};
+  if constexpr (W > 0) {
+    const float *cg = job.centroids;
+    cen.c0 = cg[0];
+    cen.c1 = cg[1];
+    if constexpr (W > 1) {
+      cen.c2 = cg[2];
+      cen.c3 = cg[3];
     }
-    vc[i] = static_cast<uint8_t>(code);
-  }
-  for (int i = tid; i < nt * kGroups * 2; i += kThreads) {
-    const int t = i / (kGroups * 2), gj = i % (kGroups * 2);
-    const int64_t ct = sel[t];
-    const int64_t row = slot * job.capacity + ct;
-    const int tt = static_cast<int>(ct & 31);
-    const float *side = reinterpret_cast<const float *>(job.vside + rec_row(row - tt, 0, job.rec));
-    vsd[i] = side[side_index(gj >> 1, tt, gj & 1)];
+    if constexpr (W > 2) {
+      cen.c4 = cg[4];
+      cen.c5 = cg[5];
+      cen.c6 = cg[6];
+      cen.c7 = cg[7];
+    }
   }
   __syncthreads();
 
-  // 2. the estimator for every (query head, chosen token): n <q_rot, c[idx]> + sqrt(pi/2)/m gamma <q_sk, 2 b - 1>
+  // 1. gather the chosen rows: whole words, record offsets from LDS
+  if constexpr (W > 0) {
+    for (int i = tid; i < nt * kwp; i += kThreads) {
+      const int t = i / kwp, wd = i % kwp;
+      if (wd < kw)
+        kc[t * kw + wd] = reinterpret_cast<const uint32_t *>(job.codes + rbase[t] + rtt[t] * (W * D / 8))[wd];
+    }
+  }
+  for (int i = tid; i < (nt << sws); i += kThreads) {
+    const int t = i >> sws, wd = i & ((1 << sws) - 1);
+    if (wd < sw) sg[t * sw + wd] = reinterpret_cast<const uint32_t *>(job.signs + rbase[t] + rtt[t] * (M / 8))[wd];
+  }
+  if (tid < nt) {
+    nr[2 * tid] = *reinterpret_cast<const float *>(job.norm + rbase[tid] + rtt[tid] * 4);
+    nr[2 * tid + 1] = W > 0 ? *reinterpret_cast<const float *>(job.rnorm + rbase[tid] + rtt[tid] * 4) : 0.0f;
+  }
+  // value codes: item (group, n) of a token gives its channels 32 group + n and 32 group + 16 + n
+  for (int i = tid; i < nt * (D / 2); i += kThreads) {
+    const int t = i / (D / 2), it = i % (D / 2);
+    const int grp = it >> 4, n = it & 15;
+    const int tt = rtt[t], r = tt & 3, ii = tt >> 2;
+    const uint32_t *blk = reinterpret_cast<const uint32_t *>(job.vcodes + rbase[t]);
+    uint32_t c_lo, c_hi;
+    if (VB == 2) {
+      const uint32_t wv = blk[(16 * grp + n) * 4 + r] >> (16 * (ii & 1) + 2 * (ii >> 1));
+      c_lo = wv & 3u;
+      c_hi = (wv >> 8) & 3u;
+    } else {
+      const uint2 wv = *reinterpret_cast<const uint2 *>(blk + ((16 * grp + n) * 4 + r) * 2);
+      const int sh = 16 * (ii & 1) + 4 * (ii >> 1);
+      c_lo = (wv.x >> sh) & 15u;
+      c_hi = (wv.y >> sh) & 15u;
+    }
+    vc[t * D + 32 * grp + n] = static_cast<uint8_t>(c_lo);
+    vc[t * D + 32 * grp + 16 + n] = static_cast<uint8_t>(c_hi);
+  }
+  for (int i = tid; i < nt * kGroups; i += kThreads) {
+    const int t = i / kGroups, grp = i % kGroups;
+    const float *side = reinterpret_cast<const float *>(job.vside + rbase[t]);
+    const float2 sm2 = *reinterpret_cast<const float2 *>(side + side_index(grp, rtt[t], 0));
+    vsd[(t * kGroups + grp) * 2] = sm2.x;
+    vsd[(t * kGroups + grp) * 2 + 1] = sm2.y;
+  }
+  __syncthreads();
+
+  // 2. the estimator for every (query head, chosen token): n <q_rot, c[idx]> + sqrt(pi/2)/m gamma <q_sk, 2 b - 1>.
+  //    Four neighbouring lanes per (head, token); in a bit word element 4 i + k sits at bit 8 k + i, so
+  //    lane k of the four takes byte k of every word: elements 32 word + 4 b + k, b = 0..7.
   const float qjl = kSqrtHalfPi / static_cast<float>(M);
   const float lscale = job.softmax_scale * kLog2e;
-  // four neighbouring lanes per (head, token), each a quarter of the coordinates and sketch rows
   const int quarter = tid & 3;
   for (int i0 = 0; i0 < G * T; i0 += kThreads / 4) {
     const int i = i0 + (tid >> 2);
@@ -369,19 +433,29 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(SparseJob job) 
     const bool live = i < G * T && t < nt;
     float mse = 0.0f, sk = 0.0f;
     if (live) {
-      const int64_t head = slot * G + h;
-      if (W > 0) {
-        const float *qr = job.q_rot + head * D;
+      const float *qr = qv + h * (D + M) + quarter;
+      const float *qs = qr + D;
+      if constexpr (W > 0) {
         const uint32_t *kt = kc + t * kw;
-        for (int j = quarter; j < D; j += 4) {
-          int idx = 0;
-          for (int p = 0; p < W; ++p) idx |= static_cast<int>(row_bit(kt + p * (D / 32), j)) << p;
-          mse = fmaf(qr[j], cen[idx], mse);
+#pragma unroll 2
+        for (int wd = 0; wd < kWords; ++wd) {
+          const uint32_t p0 = kt[wd] >> (8 * quarter);
+          const uint32_t p1 = W > 1 ? kt[kWords + wd] >> (8 * quarter) : 0u;
+          const uint32_t p2 = W > 2 ? kt[2 * kWords + wd] >> (8 * quarter) : 0u;
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+            mse = fmaf(qr[32 * wd + 4 * b], centroid<W>(cen, (p0 >> b) & 1u, (p1 >> b) & 1u, (p2 >> b) & 1u), mse);
         }
       }
-      const float *qs = job.q_sketch + head * M;
       const uint32_t *st = sg + t * sw;
-      for (int j = quarter; j < M; j += 4) sk += row_bit(st, j) ? qs[j] : -qs[j];
+      for (int wd = 0; wd < sw; ++wd) {
+        const uint32_t sb = st[wd] >> (8 * quarter);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const float qq = qs[32 * wd + 4 * b];
+          sk += ((sb >> b) & 1u) ? qq : -qq;
+        }
+      }
     }
     mse += __shfl_xor(mse, 1);
     mse += __shfl_xor(mse, 2);
@@ -394,58 +468,78 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(SparseJob job) 
   }
   __syncthreads();
 
-  // 3. per head: max, weights, sum, weighted value sum -> the chunk's partial
-  for (int h = 0; h < G; ++h) {
-    if (tid < 64) {
-      float mx = tid < nt ? lg[h * T + tid] : -INFINITY;
+  // 3. per head: max, weights, sum (one wave a head)
+  for (int h = tid >> 6; h < G; h += kThreads / 64) {
+    const int lane = tid & 63;
+    const float x = lane < nt ? lg[h * T + lane] : -INFINITY;
+    float mx = x;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      const float p = tid < nt ? __builtin_amdgcn_exp2f(lg[h * T + tid] - mx) : 0.0f;
-      lg[h * T + tid] = p;
-      float l = p;
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float p = lane < nt ? __builtin_amdgcn_exp2f(x - mx) : 0.0f;
+    lg[h * T + lane] = p;
+    float l = p;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-      if (tid == 0) {
-        stat[2 * h] = mx;
-        stat[2 * h + 1] = l;
-      }
+    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+    if (lane == 0) {
+      stat[2 * h] = mx;
+      stat[2 * h + 1] = l;
     }
   }
   __syncthreads();
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int h = i / D, ch = i % D;
-    const int grp = ch >> 5;
+  // 4. weighted value sums; when G D < the block, `parts` threads share a channel's tokens
+  const int items = G * D;
+  const int parts = items >= kThreads ? 1 : kThreads / items;
+  for (int i0 = 0; i0 < items * parts; i0 += kThreads) {
+    const int i = i0 + tid;
+    const int item = i % items, part = i / items;
     float o = 0.0f;
-    for (int t = 0; t < nt; ++t) {
-      const float v = fmaf(static_cast<float>(vc[t * D + ch]), vsd[(t * kGroups + grp) * 2], vsd[(t * kGroups + grp) * 2 + 1]);
-      o = fmaf(lg[h * T + t], v, o);
+    if (i < items * parts) {
+      const int h = item / D, ch = item % D, grp = ch >> 5;
+      for (int t = part; t < nt; t += parts) {
+        const float v = fmaf(static_cast<float>(vc[t * D + ch]), vsd[(t * kGroups + grp) * 2],
+                             vsd[(t * kGroups + grp) * 2 + 1]);
+        o = fmaf(lg[h * T + t], v, o);
+      }
     }
-    const int64_t ph = (slot * G + h) * job.n_chunks + chunk;
-    job.part_acc[ph * D + ch] = o;
-    if (ch == 0) {
-      job.part_ml[ph * 2] = stat[2 * h];
-      job.part_ml[ph * 2 + 1] = stat[2 * h + 1];
+    if (parts > 1) {
+      red[tid] = o;
+      __syncthreads();
+      if (tid < items) {
+        for (int pp = 1; pp < parts; ++pp) o += red[pp * items + tid];
+      }
+    }
+    if (i < items) {
+      const int h = item / D, ch = item % D;
+      const int64_t ph = (slot * G + h) * job.n_chunks + chunk;
+      job.part_acc[ph * D + ch] = o;
+      if (ch == 0) {
+        job.part_ml[ph * 2] = stat[2 * h];
+        job.part_ml[ph * 2 + 1] = stat[2 * h + 1];
+      }
     }
   }
 }
 
-template <int D>
-size_t sparse_smem(int w, int m, int g) {
-  constexpr int T = kChunkTokens;
-  return 4 * static_cast<size_t>(T) * (w * D / 32 + m / 32 + 2) + static_cast<size_t>(T) * D +
-         4 * static_cast<size_t>(T) * (D / 32) * 2 + 4 * static_cast<size_t>(g) * T;
+template <int D, int W>
+hipError_t launch_sparse_dw(const SparseJob &job, int64_t n_slots, hipStream_t stream) {
+  const size_t smem = sparse_smem<D, W>(job.m, job.g);
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sparse_decode_kernel<D, W>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    if (e != hipSuccess) return e;
+  }
+  sparse_decode_kernel<D, W><<<static_cast<unsigned>(n_slots * job.n_chunks), kThreads, smem, stream>>>(job);
+  return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_sparse_d(const SparseJob &job, int64_t n_slots, hipStream_t stream) {
-  const size_t smem = sparse_smem<D>(job.w, job.m, job.g);
-  if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sparse_decode_kernel<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-    if (e != hipSuccess) return e;
+  switch (job.w) {
+    case 0: return launch_sparse_dw<D, 0>(job, n_slots, stream);
+    case 1: return launch_sparse_dw<D, 1>(job, n_slots, stream);
+    case 2: return launch_sparse_dw<D, 2>(job, n_slots, stream);
+    default: return launch_sparse_dw<D, 3>(job, n_slots, stream);
   }
-  sparse_decode_kernel<D><<<static_cast<unsigned>(n_slots * job.n_chunks), kThreads, smem, stream>>>(job);
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -18,25 +18,26 @@ from test_gpu_parity import _upload_oracle_cache
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # d, w, m, G, T, budget
-    (128, 2, 128, 4, 1000, 100), (128, 2, 128, 1, 700, 64), (128, 2, 128, 8, 2050, 1), (256, 3, 256, 2, 300, 129),
-    (128, 0, 192, 4, 513, 200), (64, 1, 64, 2, 400, 65), (128, 2, 128, 4, 300, 1000),
+    # d, w, m, G, T, budget, value bits
+    (128, 2, 128, 4, 1000, 100, 2), (128, 2, 128, 1, 700, 64, 2), (128, 2, 128, 8, 2050, 1, 2),
+    (256, 3, 256, 2, 300, 129, 2), (128, 0, 192, 4, 513, 200, 2), (64, 1, 64, 2, 400, 65, 2),
+    (128, 2, 128, 4, 300, 1000, 2), (128, 2, 128, 2, 900, 300, 4), (256, 3, 256, 1, 260, 70, 4),
 ]
 
 
-@pytest.mark.parametrize("d,w,m,G,T,budget", CASES)
-def test_topk_selection_and_decode(d, w, m, G, T, budget):
+@pytest.mark.parametrize("d,w,m,G,T,budget,vb", CASES)
+def test_topk_selection_and_decode(d, w, m, G, T, budget, vb):
     torch, dev = torch_dev()
-    say("top-k", d, w, m, G, T, budget)
+    say("top-k", d, w, m, G, T, budget, vb)
     B, Hkv = 2, 2
     Hq = Hkv * G
     hl = host_layer(d, w, m, layer=6)
-    cfg = cfg_of(hl)
+    cfg = cfg_of(hl, vb)
     layer = device_layer(hl)
     rng = np.random.default_rng(d + T + budget)
     ks = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(B * Hkv)]
     vs = [(rng.standard_normal((T, d)) * 2).astype(np.float32) for _ in range(B * Hkv)]
-    cache, refs = _upload_oracle_cache(hl, cfg, ks, vs, 2, capacity=T + 3)
+    cache, refs = _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity=T + 3)
     q = rng.standard_normal((B, Hq, d)).astype(np.float32)
     qd = torch.from_numpy(q).to(dev)
     q_rot, q_sk = aqkv.prepare_query(cfg, layer, qd)
