@@ -116,7 +116,6 @@ class Path:
         self.q_sk = torch.empty((w.batch, w.n_q_heads, self.cfg.sketch_dim), device=dev)
         self.out = torch.empty((w.batch, w.n_q_heads, w.head_dim), device=dev)
         self.scores = (torch.empty((w.batch, w.n_q_heads, w.context), device=dev) if w.scores else None)
-        self.side = torch.cuda.Stream(device=dev)   # default priority
         # a full-precision recent-token window beside the compressed history (detail timing only)
         g = torch.Generator(device=dev)
         g.manual_seed(5)
@@ -161,19 +160,20 @@ class Path:
                                         w.context, self.q_f32, self.q_rot, self.q_sk, self.budget, None, None,
                                         self.out, self.tws)
 
-    def step(self):
-        # the (HBM-bound) value quantiser does not depend on the keys: it runs on a second
-        # stream beside the (compute-bound) key quantiser; decode waits for both.  Values are
-        # enqueued first: their blocks start while the key blocks take their places, which
-        # measured 5-10 % faster per step than the key kernel first.
-        import torch
-        cur = torch.cuda.current_stream()
-        self.side.wait_stream(cur)
-        with torch.cuda.stream(self.side):
-            self.quantize_values()
+    def step(self, ev=None):
+        # one stream: values, keys, the query, then decode (split-K + combine).  A second stream
+        # for the value quantiser beside the key kernel measured about 5 % faster per step, but
+        # timing events between the calls take that overlap away again, and a profiler runs the
+        # two streams one after the other: on one stream the key kernel's duration inside the
+        # step, its duration under the profiler and its duration alone agree.  ev: an optional
+        # pair of timing events recorded around the key quantiser.
+        self.quantize_values()
+        if ev:
+            ev[0].record()
         self.quantize_keys()
+        if ev:
+            ev[1].record()
         self.prepare_query()
-        cur.wait_stream(self.side)
         self.decode()
 
 
@@ -194,7 +194,8 @@ def unit_costs(w, layer: int) -> dict:
 
 
 def time_calls(path, reps: int) -> dict:
-    """Average duration of each call, HIP events on the launch stream."""
+    """Average duration of each call launched on its own (HIP events on the launch
+    stream; an idle GPU also counts the host's launch latency of short calls)."""
     import torch
     stream = torch.cuda.current_stream()
     names = ["quantize_keys", "quantize_values", "prepare_query", "decode", "prepare_key_operands", "decode_window",
@@ -392,11 +393,24 @@ def main():
             run()
         torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
+    # HIP events around the key quantiser (the step's largest call on the default workload) in
+    # every timed step, on its launch stream (eager launches only: a replayed graph has no place
+    # for them); created beforehand, read after the clock stops.
+    in_step = None
+    if not args.graph:
+        in_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        run()
+    for i in range(args.steps):
+        if in_step is None:
+            run()
+        else:
+            run(in_step[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = None
+    if in_step is not None:
+        step_ms = {"quantize_keys": float(np.mean([a.elapsed_time(b) for a, b in in_step]))}
     ms_per_step = elapsed / max(args.steps, 1) * 1e3
     G = w.n_q_heads // w.n_kv_heads
     keys_per_step = w.batch * w.n_q_heads * w.context
@@ -417,9 +431,16 @@ def main():
                       "sketch_dim": w.sketch_dim(layer), "value_bits": w.value_bits,
                       "value_group": w.value_group, "kv_dtype": w.dtype, "recipe": w.recipe,
                       "launch": "hip_graph" if args.graph else "eager", "rotation": args.rotation}}
+    if step_ms is not None:
+        rec["in_step_ms"] = step_ms
     if not args.no_detail:
         log("per-call timing")
-        per = time_calls(path, reps=max(5, args.steps))
+        per = time_calls(path, reps=max(5, min(args.steps, 50)))
+        # the largest call by its own duration; the roofline then takes that call's duration
+        # inside the timed steps where it was measured there (the key quantiser), else its own
+        live = dict(per)
+        if step_ms is not None:
+            live.update(step_ms)
         cold = time_decode_cold(path, reps=5)
         uc = unit_costs(w, layer)
         th = w.n_slots * w.context
@@ -449,12 +470,12 @@ def main():
         rec["prepare_key_operands_ms_once_per_layer"] = per["prepare_key_operands"]
         dominant = max(["decode", "quantize_keys", "quantize_values"], key=lambda n: per[n])
         if dominant == "decode":
-            ach = dec_bytes / (per["decode"] / 1e3) / 1e9
+            ach = dec_bytes / (live["decode"] / 1e3) / 1e9
             rec["roofline"] = {"kernel": "decode_attention (decode + combine)", "bound": "hbm", "achieved": ach,
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
                                "traffic": traffic_from_profiles("decode", th)}
         elif dominant == "quantize_keys":
-            ach = qk_flops / (per["quantize_keys"] / 1e3) / 1e12
+            ach = qk_flops / (live["quantize_keys"] / 1e3) / 1e12
             # the contraction runs on f16 matrix cores (split hi/lo operands): priced
             # against the dense f16 peak with the algorithmic flop count
             rec["roofline"] = {"kernel": "quantize_keys", "bound": "mfma", "achieved": ach,
@@ -462,10 +483,14 @@ def main():
                                "frac": ach / MFMA_PEAK_TFLOPS["fp16"],
                                "traffic": traffic_from_profiles("quantize_keys", th)}
         else:
-            ach = qv_bytes / (per["quantize_values"] / 1e3) / 1e9
+            ach = qv_bytes / (live["quantize_values"] / 1e3) / 1e9
             rec["roofline"] = {"kernel": "quantize_values", "bound": "hbm", "achieved": ach,
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
                                "traffic": traffic_from_profiles("quantize_values", th)}
+        rec["roofline"]["launch_ms"] = live[dominant]
+        rec["roofline"]["timing"] = ("HIP events around the call in every timed step"
+                                     if step_ms is not None and dominant in step_ms
+                                     else "HIP events around isolated calls")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         rec["cpu_baseline"] = cpu_baseline(w, layer)
