@@ -81,10 +81,19 @@ __host__ __device__ inline int permuted_row(int t, int r, int tiles) {
 // conversion for one part only.  No instruction is written in asm here: the
 // compiler must see every VALU write to keep its wait states against
 // in-flight matrix instructions.
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi2, uint32_t &lo2) {
+// The low parts are fma(hi, minus1, a) with minus1 = -1 from opaque_minus1():
+// a mixed-precision fma reads the f16 hi directly (no conversion back to
+// fp32); a literal -1 would be folded into a subtraction.
+__device__ __forceinline__ float opaque_minus1() {
+  float m = -1.0f;
+  asm volatile("" : "+s"(m));   // no instruction: the value is only hidden from the optimiser
+  return m;
+}
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi2, uint32_t &lo2, float minus1) {
   asm volatile("" : "+v"(a), "+v"(b));
   const v2h h = __builtin_convertvector((v2f){a, b}, v2h);
-  const v2f r = {a - static_cast<float>(h[0]), b - static_cast<float>(h[1])};
+  const v2f r = {__builtin_fmaf(static_cast<float>(h[0]), minus1, a),
+                 __builtin_fmaf(static_cast<float>(h[1]), minus1, b)};
   hi2 = __builtin_bit_cast(uint32_t, h);
   lo2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, v2h));
 }
@@ -308,12 +317,13 @@ __device__ __forceinline__ void prepare_keys(const RawKeys<D, BF16> &R, float (&
         }
     } else {
       const float inv = n > 0.0f ? kUp / n : 0.0f;
+      const float minus1 = opaque_minus1();
       yscale[nt] = kDown8;
 #pragma unroll
       for (int k = 0; k < Geo<D>::KS; ++k)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          split_pair(x[k][2 * j] * inv, x[k][2 * j + 1] * inv, uh[nt][k].w[j], ul[nt][k].w[j]);
+          split_pair(x[k][2 * j] * inv, x[k][2 * j + 1] * inv, uh[nt][k].w[j], ul[nt][k].w[j], minus1);
     }
   }
 }
@@ -343,6 +353,7 @@ struct IndexState {
   uint32_t wv[W][Geo<D>::NT];                // words being built, most significant bit first
   float esq[Geo<D>::NT];                     // ||2^8 e||^2 (this lane's part)
   float bts[NU > 0 ? NU : 1][Geo<D>::NT];    // symmetric codebook: upper boundaries / yscale, per key
+  float minus1;                              // -1, opaque (split_pair)
 };
 
 // An odd-symmetric codebook (c[K-1-i] = -c[i], b[K-2-i] = -b[i], middle
@@ -368,6 +379,7 @@ __device__ __forceinline__ bool codebook_symmetric(const KeyJob &job) {
 
 template <int D, int W>
 __device__ __forceinline__ void index_codebook(const KeyJob &job, IndexState<D, W> &S) {
+  S.minus1 = opaque_minus1();
 #pragma unroll
   for (int i = 0; i < IndexState<D, W>::NB; ++i) S.bnd[i] = job.boundaries[i] * kUp;
 #pragma unroll
@@ -498,8 +510,8 @@ __device__ __forceinline__ void index_vals(int t, const v4f (&acc)[Geo<D>::NT], 
       S.esq[nt] = fmaf(e[i], e[i], S.esq[nt]);
     }
     }
-    split_pair(e[0], e[1], bh[nt][t >> 1].w[2 * (t & 1)], bl[nt][t >> 1].w[2 * (t & 1)]);
-    split_pair(e[2], e[3], bh[nt][t >> 1].w[2 * (t & 1) + 1], bl[nt][t >> 1].w[2 * (t & 1) + 1]);
+    split_pair(e[0], e[1], bh[nt][t >> 1].w[2 * (t & 1)], bl[nt][t >> 1].w[2 * (t & 1)], S.minus1);
+    split_pair(e[2], e[3], bh[nt][t >> 1].w[2 * (t & 1) + 1], bl[nt][t >> 1].w[2 * (t & 1) + 1], S.minus1);
   }
 }
 
