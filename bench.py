@@ -194,8 +194,10 @@ def unit_costs(w, layer: int) -> dict:
 
 
 def time_calls(path, reps: int) -> dict:
-    """Average duration of each call launched on its own (HIP events on the launch
-    stream; an idle GPU also counts the host's launch latency of short calls)."""
+    """Average duration of each call launched on its own, HIP events on the launch
+    stream.  A spin kernel (~0.4 ms) runs before each call's first event, so the GPU
+    is still busy while the host issues the call and its closing event: the interval
+    holds the call's own work, not the host's launch latency."""
     import torch
     stream = torch.cuda.current_stream()
     names = ["quantize_keys", "quantize_values", "prepare_query", "decode", "prepare_key_operands", "decode_window",
@@ -205,6 +207,7 @@ def time_calls(path, reps: int) -> dict:
         for n in names:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(1_000_000)
             a.record(stream)
             getattr(path, n)()
             b.record(stream)
