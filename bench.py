@@ -367,7 +367,7 @@ def main():
                          indent=1))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the path runs on one GPU only (no multi-GPU form); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -85,7 +85,7 @@ typedef enum {
   AQKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
   AQKV_ERR_DTYPE = -6,       /* unknown element type */
   AQKV_ERR_HIP = -7,         /* the HIP runtime reported an error */
-  AQKV_ERR_UNSUPPORTED = -8  /* valid request this build does not implement */
+  AQKV_ERR_UNSUPPORTED = -8  /* valid request the library does not implement */
 } aqkv_status;
 
 typedef enum { AQKV_FP32 = 0, AQKV_BF16 = 1 } aqkv_dtype;

@@ -108,7 +108,7 @@ const char *aqkv_status_string(aqkv_status s) {
     case AQKV_ERR_WORKSPACE: return "workspace missing or too small";
     case AQKV_ERR_DTYPE: return "unknown element type";
     case AQKV_ERR_HIP: return "HIP runtime error";
-    case AQKV_ERR_UNSUPPORTED: return "not supported by this build";
+    case AQKV_ERR_UNSUPPORTED: return "not supported by the library";
   }
   return "unknown status";
 }
