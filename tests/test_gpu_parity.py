@@ -272,6 +272,8 @@ DECODE_CASES = [
     (128, 2, 128, 4, 2, 1000), (128, 2, 128, 1, 2, 256), (128, 2, 128, 2, 2, 1), (128, 2, 128, 8, 2, 4097),
     (256, 3, 256, 2, 2, 700), (128, 0, 192, 4, 2, 513), (128, 0, 512, 4, 2, 300), (64, 1, 64, 4, 4, 255),
     (128, 2, 128, 4, 4, 999),
+    # shapes without a matrix-core kernel (sketch rows != 64 x d/64 with mse bits): the scalar decoder
+    (128, 2, 256, 4, 2, 700), (64, 2, 128, 2, 4, 300), (128, 1, 192, 8, 2, 257),
 ]
 
 
