@@ -140,7 +140,7 @@ def test_quantize_keys_small_append_many_slots(d, w, m, nt):
 
 
 @pytest.mark.parametrize("d,vb,dtype", [(128, 2, "bf16"), (128, 2, "fp32"), (256, 2, "bf16"), (64, 4, "fp32"),
-                                        (128, 4, "bf16")])
+                                        (128, 4, "bf16"), (256, 4, "bf16"), (64, 2, "bf16")])
 def test_quantize_values_bit_exact(d, vb, dtype):
     torch, dev = torch_dev()
     say("quantize_values", d, vb, dtype)
@@ -223,7 +223,8 @@ def test_chunked_append_matches_one_call():
     assert torch.equal(one.blocks, parts.blocks)
 
 
-@pytest.mark.parametrize("d,w,m,qdtype", [(128, 2, 128, "fp32"), (128, 0, 512, "bf16"), (256, 3, 256, "fp32")])
+@pytest.mark.parametrize("d,w,m,qdtype", [(128, 2, 128, "fp32"), (128, 0, 512, "bf16"), (256, 3, 256, "fp32"),
+                                           (64, 1, 64, "bf16"), (256, 0, 1024, "fp32")])
 def test_prepare_query_parity(d, w, m, qdtype):
     torch, dev = torch_dev()
     say("prepare_query", d, w, m, qdtype)
