@@ -238,10 +238,15 @@ def time_decode_cold(path, reps: int) -> float:
     return float(np.mean([a.elapsed_time(b) for a, b in ts]))
 
 
-def traffic_from_profiles(kernel: str, units: float):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
-    p = os.path.join(ROOT, "profiles", "counters.json")
+def counters_path(workload: str, layer: int) -> str:
+    """The committed HBM counter summary of one workload and layer."""
+    return os.path.join(ROOT, "profiles", f"hbm_counters_{workload}_layer{layer}.json")
+
+
+def traffic_from_profiles(kernel: str, workload: str, layer: int):
+    """HBM bytes per launch from the committed counter summary of this workload and
+    layer, if it was taken on the current kernel source; else None."""
+    p = counters_path(workload, layer)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -299,8 +304,8 @@ KERNEL_NAMES = {
 }
 
 
-def write_counters(fetch_csv: str, write_csv: str, out: str) -> dict:
-    """profiles/counters.json from two rocprofv3 --pmc passes (FETCH_SIZE, then
+def write_counters(fetch_csv: str, write_csv: str, out: str, workload: str, layer: int) -> dict:
+    """The HBM counter summary (counters_path) from two rocprofv3 --pmc passes (FETCH_SIZE, then
     WRITE_SIZE, both in KiB per dispatch) over `bench.py --calibrate-copy`: each
     counter is scaled by what it reads for the plain 1 GiB device copy (1 GiB
     fetched and 1 GiB written), and each call's HBM bytes per launch are the sum
@@ -324,7 +329,8 @@ def write_counters(fetch_csv: str, write_csv: str, out: str) -> dict:
         raise SystemExit("no 1 GiB copy dispatch in the counter files (run bench.py with --calibrate-copy)")
     f_fetch = gib_kib / float(np.mean(copy_f))
     f_write = gib_kib / float(np.mean(copy_w))
-    rec = {"calibration": {"copy_bytes": 1 << 30, "fetch_kib_read": float(np.mean(copy_f)),
+    rec = {"workload": workload, "layer": layer,
+           "calibration": {"copy_bytes": 1 << 30, "fetch_kib_read": float(np.mean(copy_f)),
                            "write_kib_read": float(np.mean(copy_w)), "fetch_factor": f_fetch,
                            "write_factor": f_write},
            "kernels": {}}
@@ -359,12 +365,13 @@ def main():
                     help="replay the step captured once as a HIP graph instead of launching each call from Python "
                          "(measured no faster for these kernel sizes)")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="no GPU work: write profiles/counters.json from two rocprofv3 counter_collection.csv "
+                    help="no GPU work: write the workload's profiles/hbm_counters_*.json from two rocprofv3 "
+                         "counter_collection.csv "
                          "files (FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy run")
     args = ap.parse_args()
     if args.write_counters:
-        print(json.dumps(write_counters(*args.write_counters, os.path.join(ROOT, "profiles", "counters.json")),
-                         indent=1))
+        print(json.dumps(write_counters(*args.write_counters, counters_path(args.workload, args.layer),
+                                        args.workload, args.layer), indent=1))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the path runs on one GPU only (no multi-GPU form); --gpus must be 1",
@@ -476,7 +483,7 @@ def main():
             ach = dec_bytes / (live["decode"] / 1e3) / 1e9
             rec["roofline"] = {"kernel": "decode_attention (decode + combine)", "bound": "hbm", "achieved": ach,
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
-                               "traffic": traffic_from_profiles("decode", th)}
+                               "traffic": traffic_from_profiles("decode", w.name, layer)}
         elif dominant == "quantize_keys":
             ach = qk_flops / (live["quantize_keys"] / 1e3) / 1e12
             # the contraction runs on f16 matrix cores (split hi/lo operands): priced
@@ -484,12 +491,12 @@ def main():
             rec["roofline"] = {"kernel": "quantize_keys", "bound": "mfma", "achieved": ach,
                                "peak": MFMA_PEAK_TFLOPS["fp16"], "unit": "TFLOP/s",
                                "frac": ach / MFMA_PEAK_TFLOPS["fp16"],
-                               "traffic": traffic_from_profiles("quantize_keys", th)}
+                               "traffic": traffic_from_profiles("quantize_keys", w.name, layer)}
         else:
             ach = qv_bytes / (live["quantize_values"] / 1e3) / 1e9
             rec["roofline"] = {"kernel": "quantize_values", "bound": "hbm", "achieved": ach,
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
-                               "traffic": traffic_from_profiles("quantize_values", th)}
+                               "traffic": traffic_from_profiles("quantize_values", w.name, layer)}
         rec["roofline"]["launch_ms"] = live[dominant]
         rec["roofline"]["timing"] = ("HIP events around the call in every timed step"
                                      if step_ms is not None and dominant in step_ms
