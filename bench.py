@@ -48,10 +48,16 @@ def log(*a):
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of a call's kernel sources with their comments removed (a comment
+    edit does not change what the counters measured)."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "kv_cache_compression_quantize_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "kv_cache_compression_quantize_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 

@@ -1,7 +1,7 @@
 // Value quantisation kernel: per token, per group of 32 contiguous channels,
-// min-max quantisation to 2 or 4 bits (TurboQuant article, component table
-// "Value 分组量化 2 bit/维, min-max", and §七, kv_cache.py "value group
-// quantisation and bit packing").
+// min-max quantisation to 2 or 4 bits (TurboQuant article, the value row of the
+// component table: grouped min-max at 2 bits per dimension; and §七, the value
+// group quantisation and bit packing of its kv_cache.py listing).
 //
 // code = clamp(rint((v - min) / scale), 0, 2^vb - 1) with scale = (max - min) /
 // (2^vb - 1), every step in IEEE fp32 (subtract, correctly rounded divide,

@@ -8,9 +8,9 @@ It is a plain, slow, float64 (numpy) restatement of what the pages describe,
 written step by step so a reader can check each step against the text:
 
 * ``codebook``  -- Lloyd-Max scalar quantiser for one coordinate of a random
-  unit vector after rotation (TurboQuant article §二, step "Lloyd-Max 粗量化").
+  unit vector after rotation (TurboQuant article §二, the coarse Lloyd-Max step).
 * ``rotation``  -- random orthogonal rotation from a QR decomposition
-  (TurboQuant article §二, step "归一化 + 随机旋转").
+  (TurboQuant article §二, the normalise-and-rotate step).
 * ``keys``      -- norm, rotation, Lloyd-Max index, residual, QJL sign sketch,
   residual norm, and the bit layouts those are stored in (§二, §五).
 * ``values``    -- min-max grouped value quantisation (component table, §七).

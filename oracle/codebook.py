@@ -1,6 +1,6 @@
 """Lloyd-Max codebook for a rotated unit-vector coordinate (oracle, float64).
 
-TurboQuant article §二, step "Lloyd-Max 粗量化 (b−1 bit)": after the key is
+TurboQuant article §二, the coarse Lloyd-Max step (b−1 bits): after the key is
 normalised and rotated, every coordinate follows the same (scaled Beta)
 distribution; the quantiser is the continuous 1-D k-means (Lloyd-Max) solution
 for that distribution, with 2**w levels, applied per coordinate by looking up

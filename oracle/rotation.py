@@ -1,6 +1,6 @@
 """Random orthogonal rotation (oracle, float64).
 
-TurboQuant article §二, step "归一化 + 随机旋转": the rotation matrix is made
+TurboQuant article §二, the normalise-and-rotate step: the rotation matrix is made
 by a QR decomposition of a random matrix (one fixed seed per layer; §六 gives
 seed = 42 + 7 * layer).  The article does not say how the signs of the QR
 factors are fixed; here the columns of Q are multiplied by sign(diag R), which

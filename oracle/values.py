@@ -1,7 +1,8 @@
 """Value quantisation (oracle).
 
-TurboQuant article, component table ("Value 分组量化, 2 bit/维, conventional
-min-max") and §七 (kv_cache.py: value group quantisation and bit packing).
+TurboQuant article, component table (the value row: grouped conventional
+min-max at 2 bits per dimension) and §七 (kv_cache.py: value group
+quantisation and bit packing).
 The article fixes only "min-max", "group" and the bit width.  Reading used on
 both sides:
 
