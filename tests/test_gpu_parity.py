@@ -34,6 +34,8 @@ KEY_CASES = [
     (128, 2, 128, "bf16"), (128, 2, 128, "fp32"), (256, 3, 256, "bf16"), (128, 0, 192, "bf16"),
     (128, 0, 512, "bf16"), (64, 1, 64, "fp32"), (128, 1, 128, "bf16"), (128, 3, 128, "bf16"),
     (128, 2, 256, "bf16"), (256, 0, 384, "fp32"),
+    # the largest sketch the library takes (1024 rows)
+    (128, 0, 1024, "bf16"), (256, 2, 1024, "fp32"),
 ]
 
 
@@ -275,6 +277,8 @@ DECODE_CASES = [
     (128, 2, 128, 4, 4, 999),
     # shapes without a matrix-core kernel (sketch rows != 64 x d/64 with mse bits): the scalar decoder
     (128, 2, 256, 4, 2, 700), (64, 2, 128, 2, 4, 300), (128, 1, 192, 8, 2, 257),
+    # the largest sketch (1024 rows)
+    (128, 0, 1024, 2, 2, 300), (256, 2, 1024, 1, 2, 200),
 ]
 
 
