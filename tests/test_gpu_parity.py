@@ -380,3 +380,24 @@ def test_end_to_end(d, w, m, G, dtype):
         rel = np.abs(sg - s_ref) / np.maximum(np.abs(s_ref), rms)
         assert np.max(rel[:, clean]) <= SCORE_RTOL
         say(f"slot {s}: {int((~clean).sum())} keys differ from the oracle inside the boundary window")
+
+
+def test_empty_calls_succeed_and_write_nothing():
+    """Zero tokens to quantise and zero queries are valid calls that leave the
+    cache as it was (a decode over zero cached rows is covered above)."""
+    torch, dev = torch_dev()
+    say("empty calls")
+    d, w, m = 128, 2, 128
+    hl = host_layer(d, w, m)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    cache = aqkv.Cache.allocate(cfg, 4, 64)
+    cache.blocks.fill_(0xAB)
+    before = cache.blocks.clone()
+    empty = torch.empty((2, 2, 0, d), dtype=torch.bfloat16, device=dev)
+    aqkv.quantize_keys(cfg, layer, empty, cache, token_offset=5)
+    aqkv.quantize_values(cfg, empty, cache, 5)
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, torch.empty((0, d), device=dev))
+    assert q_rot.shape == (0, d) and q_sk.shape == (0, m)
+    torch.cuda.synchronize()
+    assert torch.equal(cache.blocks, before)
