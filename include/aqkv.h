@@ -157,14 +157,14 @@ aqkv_status aqkv_cache_layout(const aqkv_config *cfg, aqkv_layout *out);
  * bits in 1..4, head_dim in 3..4096. */
 aqkv_status aqkv_build_codebook(int32_t head_dim, int32_t bits, float *centroids, float *boundaries);
 
-/* Random orthogonal rotation from a Gaussian matrix (TurboQuant §二, "QR
- * decomposition"): Householder QR of gaussian [d][d] (host, row-major
+/* Random orthogonal rotation from a Gaussian matrix (TurboQuant §二: a QR
+ * decomposition): Householder QR of gaussian [d][d] (host, row-major
  * double), Pi = Q diag(sign(diag R)), written row-major fp32 to rotation
  * (host).  d in 1..4096. */
 aqkv_status aqkv_build_rotation(int32_t d, const double *gaussian, float *rotation);
 
-/* Randomised Hadamard rotation (NexusQuant article, stage 4 "Hadamard
- * rotation": a Hadamard matrix spreads every coordinate's energy over all d,
+/* Randomised Hadamard rotation (NexusQuant article, stage 4, the Hadamard
+ * rotation: a Hadamard matrix spreads every coordinate's energy over all d,
  * removing outliers): Pi = H diag(s) / sqrt(d), H Sylvester's Hadamard matrix
  * (H_ij = (-1)^popcount(i & j)), s_j = +1 where gaussian[j] >= 0 (the first
  * row of the layer's d x d Gaussian draw, host double), else -1; written

@@ -205,8 +205,8 @@ struct Geo {
 };
 
 // Query side of the slot's G heads, built by the whole block once (the
-// TurboQuant article's "rotate and sketch the query once" step, here also
-// integerised): per head the scales sig = max |value| / 16383 and the constant
+// TurboQuant article's step that rotates and sketches each query once, here
+// also integerised): per head the scales sig = max |value| / 16383 and the constant
 // terms c[0] sum(q_rot), -sum(q_sk) go to hc; every A-operand value v = round
 // (value / sig) (kappa_A q_rot for the code planes in PL, 2 q_sk for the sign
 // chunks) is split into int8 parts hi = v >> 7, lo = v & 127 and written to

@@ -49,7 +49,7 @@ def hadamard_signs(g: np.ndarray) -> np.ndarray:
 
 
 def randomized_hadamard(g: np.ndarray) -> np.ndarray:
-    """NexusQuant article, stage 4 ("Hadamard rotation"): Pi = H D / sqrt(d),
+    """NexusQuant article, stage 4 (the Hadamard rotation): Pi = H D / sqrt(d),
     an orthogonal rotation that spreads every coordinate's energy over all d
     (float64)."""
     s = hadamard_signs(g)
