@@ -8,8 +8,10 @@
 //   decoder's score output)
 //   topk_select_kernel      per KV slot (1024 threads): cos_t = score_t / ||k_t||
 //                           (0 for a zero key) as order-preserving keys, the
-//                           `budget` largest by a 3-pass radix select (ties to
-//                           the lower token), written as increasing token indices
+//                           `budget` largest by a radix select with digits of
+//                           12, 10 and 10 bits, the last two on the candidates of
+//                           the first digit's bin (ties to the lower token),
+//                           written as increasing token indices
 //   sparse_decode_kernel    per (KV slot, chunk of 64 chosen tokens): the chosen
 //                           rows are gathered from their block records into LDS
 //                           (key planes, signs, norms, value codes, scale and
@@ -99,14 +101,22 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   return x;
 }
 
-// KEYS_LDS: the slot's keys live in dynamic LDS, else in place of its scores
+// KEYS_LDS: the slot's keys live in dynamic LDS, else in place of its scores.
+// Three passes over the keys: (1) compute them and histogram their top 12 bits;
+// (2) after the first digit, collect the keys of its bin (the candidates, at
+// most kCandMax of them, in the histogram's space) and count per wave the keys
+// above it; the last two digits are then found on the candidates alone; (3)
+// write the chosen indices in token order.  A bin with more candidates than
+// that (many equal keys) takes two more full passes and a counting pass instead.
+constexpr int kCandMax = kHistBins - 1024;
 template <bool KEYS_LDS>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job) {
   extern __shared__ uint4 lds_keys4[];
-  __shared__ uint32_t hist[kHistBins];
+  __shared__ uint32_t hist[kHistBins];   // first-digit histogram; then 1024 bins + the candidates
   __shared__ uint32_t wsum[kSelWaves];
   __shared__ uint32_t wgt[kSelWaves], weq[kSelWaves];
   __shared__ uint32_t pick[2];
+  __shared__ uint32_t n_cand;
   const int64_t slot = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = static_cast<int>(job.context);   // chosen indices are int32, so T < 2^31
@@ -119,8 +129,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job)
     if (KEYS_LDS) return lds_keys4[q];
     return make_uint4(keys[4 * q], keys[4 * q + 1], keys[4 * q + 2], keys[4 * q + 3]);
   };
-  // 1. cos_t = score_t / n_t (0 for a zero key) as order-preserving keys; every load of a
-  //    batch is issued before the first is used, so a thread has 2 * kBatch reads in flight
+  for (int i = tid; i < kHistBins; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  // 1. cos_t = score_t / n_t (0 for a zero key) as order-preserving keys, and the histogram
+  //    of their top 12 bits (cosines share their sign and exponent bits, so a wide first
+  //    digit spreads them); every load of a batch is issued before the first is used
   constexpr int kBatch = 16;
   const int64_t row0 = slot * job.capacity;
   for (int t0 = 0; t0 < T; t0 += kSelThreads * kBatch) {
@@ -134,37 +147,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job)
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int t = t0 + u * kSelThreads + tid;
-      if (t < T) keys[t] = order_key(nn[u] > 0.0f ? sc[u] / nn[u] : 0.0f);
+      if (t < T) {
+        const uint32_t k = order_key(nn[u] > 0.0f ? sc[u] / nn[u] : 0.0f);
+        keys[t] = k;
+        atomicAdd(&hist[k >> 20], 1u);
+      }
     }
   }
-  // 2. radix select of the budget-th largest key, digits of 12, 10 and 10 bits from the
-  //    top (cosines share their sign and exponent bits, so a wide first digit spreads them)
-  const int nq = T >> 2;
-  uint32_t prefix = 0, mask = 0;
-  uint32_t need = static_cast<uint32_t>(job.budget);   // still to choose among keys matching prefix
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
-    const int bins = pass == 0 ? kHistBins : 1024;
-    const uint32_t bm = static_cast<uint32_t>(bins - 1);
+  __syncthreads();
+  // the digit of `bins` histogram bins (from the top) that holds the need-th largest key:
+  // thread i holds `per` bins from the top down; the scan gives the count in the bins above
+  // them, and the one thread whose bins take that count to `need` writes the digit
+  auto find_digit = [&](int bins, uint32_t need) {
     const int per = bins / kSelThreads;
-    __syncthreads();   // keys written, and the previous pass done with hist
-    for (int i = tid; i < bins; i += kSelThreads) hist[i] = 0;
-    __syncthreads();
-    auto count = [&](uint32_t k) {
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & bm], 1u);
-    };
-#pragma unroll 2
-    for (int q = tid; q < nq; q += kSelThreads) {
-      const uint4 k = quad(q);
-      count(k.x);
-      count(k.y);
-      count(k.z);
-      count(k.w);
-    }
-    if (4 * nq + tid < T) count(keys[4 * nq + tid]);
-    __syncthreads();
-    // thread i holds `per` bins from the top down: the scan gives the count in the bins
-    // above them, and the one thread whose bins take that count to `need` finds the digit
     const int top = bins - 1 - tid * per;
     uint32_t c = 0;
     for (int j = 0; j < per; ++j) c += hist[top - j];
@@ -181,14 +176,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job)
       }
     }
     __syncthreads();
-    prefix |= pick[0] << shift;
-    mask |= bm << shift;
-    need -= pick[1];
-  }
-  // 3. keys > prefix are all chosen; of the keys == prefix, the first `need` in token
-  //    order.  Each wave owns a contiguous run of tokens (a multiple of 256) and takes it
-  //    256 at a time, lane l holding tokens 4 l .. 4 l + 3; choices are ranked by ballot,
-  //    so the output comes out in increasing token order.
+  };
+  uint32_t need = static_cast<uint32_t>(job.budget);   // still to choose among keys matching prefix
+  find_digit(kHistBins, need);
+  uint32_t prefix = pick[0] << 20, mask = 0xFFF00000u;
+  need -= pick[1];
+  const uint32_t nc = hist[pick[0]];
+  // wave segments for the collect and write passes: contiguous runs of tokens (a multiple
+  // of 256), taken 256 at a time, lane l holding tokens 4 l .. 4 l + 3
   const int seg = ((T + kSelWaves - 1) / kSelWaves + 255) / 256 * 256;
   const int s0 = min(T, wave * seg), s1 = min(T, s0 + seg);
   const uint64_t below = (uint64_t{1} << lane) - 1u;
@@ -207,23 +202,119 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job)
     for (int j = 0; j < 4; ++j) k[j] = j < nv ? keys[t + j] : 0u;
     return nv;
   };
-  uint32_t gt = 0, eq = 0;
-  for (int b = s0; b < s1; b += 256) {
-    uint32_t k[4];
-    const int nv = lane_keys(b, k);
+  const int nq = T >> 2;
+  if (tid == 0) n_cand = 0;
+  __syncthreads();   // nc read by every thread before hist is reused
+  for (int i = tid; i < 1024; i += kSelThreads) hist[i] = 0;
+  if (nc <= static_cast<uint32_t>(kCandMax)) {
+    // 2. the candidates (keys in the first digit's bin) and, per wave, the keys above it
+    uint32_t *cand = hist + 1024;
+    uint32_t gt = 0;
+    for (int b = s0; b < s1; b += 256) {
+      uint32_t k[4];
+      const int nv = lane_keys(b, k);
+      bool c[4];
+      uint32_t c_below = 0, c_all = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      gt += j < nv && k[j] > prefix;
-      eq += j < nv && k[j] == prefix;
+      for (int j = 0; j < 4; ++j) {
+        gt += j < nv && (k[j] & mask) > prefix;
+        c[j] = j < nv && (k[j] & mask) == prefix;
+        const uint64_t cb = __ballot(c[j]);
+        c_below += __popcll(cb & below);
+        c_all += __popcll(cb);
+      }
+      if (c_all > 0) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&n_cand, c_all);
+        base = __shfl(base, 0);
+        uint32_t o = base + c_below;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c[j]) cand[o++] = static_cast<uint32_t>(b + 4 * lane + j);
+      }
     }
+    gt = wave_sum(gt);
+    if (lane == 0) {
+      wgt[wave] = gt;
+      weq[wave] = 0;
+    }
+    __syncthreads();
+    const int ncand = static_cast<int>(n_cand);
+    // the last two digits on the candidates
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 10 : 0;
+      if (pass > 0) {
+        for (int i = tid; i < 1024; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+      }
+      for (int i = tid; i < ncand; i += kSelThreads) {
+        const uint32_t k = keys[cand[i]];
+        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 1023u], 1u);
+      }
+      __syncthreads();
+      find_digit(1024, need);
+      prefix |= pick[0] << shift;
+      mask |= 1023u << shift;
+      need -= pick[1];
+    }
+    // per wave: the candidates above the threshold, and those equal to it
+    for (int i = tid; i < ncand; i += kSelThreads) {
+      const uint32_t t = cand[i];
+      const uint32_t k = keys[t];
+      const int w = static_cast<int>(t) / seg;
+      if (k > prefix) atomicAdd(&wgt[w], 1u);
+      else if (k == prefix) atomicAdd(&weq[w], 1u);
+    }
+    __syncthreads();
+  } else {
+    // 2'. many keys in one bin: the last two digits over all keys, then the per-wave counts
+    __syncthreads();
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 10 : 0;
+      if (pass > 0) {
+        for (int i = tid; i < 1024; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+      }
+      auto count = [&](uint32_t k) {
+        if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 1023u], 1u);
+      };
+#pragma unroll 2
+      for (int q = tid; q < nq; q += kSelThreads) {
+        const uint4 k = quad(q);
+        count(k.x);
+        count(k.y);
+        count(k.z);
+        count(k.w);
+      }
+      if (4 * nq + tid < T) count(keys[4 * nq + tid]);
+      __syncthreads();
+      find_digit(1024, need);
+      prefix |= pick[0] << shift;
+      mask |= 1023u << shift;
+      need -= pick[1];
+    }
+    uint32_t gt = 0, eq = 0;
+    for (int b = s0; b < s1; b += 256) {
+      uint32_t k[4];
+      const int nv = lane_keys(b, k);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        gt += j < nv && k[j] > prefix;
+        eq += j < nv && k[j] == prefix;
+      }
+    }
+    gt = wave_sum(gt);
+    eq = wave_sum(eq);
+    if (lane == 0) {
+      wgt[wave] = gt;
+      weq[wave] = eq;
+    }
+    __syncthreads();
   }
-  gt = wave_sum(gt);
-  eq = wave_sum(eq);
-  if (lane == 0) {
-    wgt[wave] = gt;
-    weq[wave] = eq;
-  }
-  __syncthreads();
+  // 3. keys > prefix are all chosen; of the keys == prefix, the first `need` in token
+  //    order.  Each wave ranks its lanes' choices by ballot, so the output comes out in
+  //    increasing token order.
+  const uint32_t eq = weq[wave];
   uint32_t eq_before = 0, base = 0;
   for (int w = 0; w < wave; ++w) {
     const uint32_t take = eq_before >= need ? 0u : min(weq[w], need - eq_before);

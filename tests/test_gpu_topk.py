@@ -84,3 +84,35 @@ def test_topk_empty_context():
     out = aqkv.decode_attention_topk(cfg, layer, cache, 1, G, 1, 0, q, q_rot, q_sk, 16)
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+def test_topk_many_equal_keys():
+    """Every cached key the same: all cosines tie, so the chosen rows are the first
+    `budget` tokens (ties go to the lower token).  More keys share the top-digit bin
+    than the select kernel collects as candidates, so this takes its full-pass route."""
+    torch, dev = torch_dev()
+    d, w, m, G, T, budget = 128, 2, 128, 2, 5000, 300
+    B, Hkv = 1, 2
+    hl = host_layer(d, w, m, layer=2)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    rng = np.random.default_rng(17)
+    ks = [np.tile(rng.standard_normal((1, d)).astype(np.float32), (T, 1)) for _ in range(B * Hkv)]
+    vs = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(B * Hkv)]
+    cache, refs = _upload_oracle_cache(hl, cfg, ks, vs, 2, capacity=T)
+    q = rng.standard_normal((B, Hkv * G, d)).astype(np.float32)
+    qd = torch.from_numpy(q).to(dev)
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, qd)
+    sel = torch.full((B * Hkv, budget), -1, dtype=torch.int32, device=dev)
+    out = aqkv.decode_attention_topk(cfg, layer, cache, B, Hkv * G, Hkv, T, qd, q_rot, q_sk, budget, selected=sel)
+    torch.cuda.synchronize()
+    sel, out = sel.cpu().numpy(), out.cpu().numpy()
+    for s in range(B * Hkv):
+        np.testing.assert_array_equal(sel[s], np.arange(budget))
+        qh = q[0, s * G:(s + 1) * G]
+        osel, _ = oatt.select_top_k(qh, refs[s][0], hl.rotation, hl.sketch, hl.centroids, w, budget)
+        np.testing.assert_array_equal(np.sort(osel), np.arange(budget))
+        sub_k = tuple(np.asarray(a)[sel[s]] for a in refs[s][0])
+        sub_v = tuple(np.asarray(a)[sel[s]] for a in refs[s][1])
+        _, o_ref = oatt.decode_slot(qh, sub_k, sub_v, hl.rotation, hl.sketch, hl.centroids, w)
+        assert np.max(np.abs(out[0, s * G:(s + 1) * G] - o_ref)) <= OUT_ATOL
