@@ -420,7 +420,7 @@ aqkv_status aqkv_decode_attention(const aqkv_config *cfg, const aqkv_layer *laye
 // the selection scores, the scoring decode's output and split workspace, the
 // chosen indices and the chunk partials, each 256-byte aligned.
 struct TopkLayout {
-  size_t qsel, qsel_rot, qsel_sk, scores, dec_out, dec_ws, dec_ws_bytes, sel, acc, ml, total;
+  size_t qsel_rot, qsel_sk, scores, dec_out, dec_ws, dec_ws_bytes, sel, acc, ml, total;
 };
 
 static TopkLayout topk_layout(const aqkv_config *cfg, int64_t n_slots, int g, int64_t context, int budget) {
@@ -432,7 +432,6 @@ static TopkLayout topk_layout(const aqkv_config *cfg, int64_t n_slots, int g, in
     at += round_up(bytes, 256);
     return here;
   };
-  L.qsel = take(sizeof(float) * n_slots * d);
   L.qsel_rot = take(sizeof(float) * n_slots * d);
   L.qsel_sk = take(sizeof(float) * n_slots * m);
   L.scores = take(sizeof(float) * n_slots * context);
@@ -502,23 +501,12 @@ aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer 
   }
   if ((st = check_blocks(cache)) != AQKV_OK) return st;
 
-  // 1. the selection query of every KV slot, rotated and sketched
-  float *qsel = reinterpret_cast<float *>(ws + TL.qsel);
+  // 1. the selection query of every KV slot, rotated and sketched (one kernel)
   float *qsel_rot = reinterpret_cast<float *>(ws + TL.qsel_rot);
   float *qsel_sk = reinterpret_cast<float *>(ws + TL.qsel_sk);
-  if (launch_selection_query(q, cache->n_slots, d, g, qsel, s) != hipSuccess) return AQKV_ERR_HIP;
-  QueryJob qj{};
-  qj.q = qsel;
-  qj.dtype = AQKV_FP32;
-  qj.n_q = cache->n_slots;
-  qj.d = d;
-  qj.w = w;
-  qj.m = m;
-  qj.rotation = layer->rotation;
-  qj.sketch = layer->sketch;
-  qj.q_rot = w > 0 ? qsel_rot : nullptr;
-  qj.q_sketch = qsel_sk;
-  if (launch_prepare_query(qj, s) != hipSuccess) return AQKV_ERR_HIP;
+  if (launch_selection_query(q, cache->n_slots, d, g, m, layer->rotation, layer->sketch, w > 0 ? qsel_rot : nullptr,
+                             qsel_sk, s) != hipSuccess)
+    return AQKV_ERR_HIP;
   // 2. its estimate for every cached token (the decoder's score output, one query per slot)
   float *scores = reinterpret_cast<float *>(ws + TL.scores);
   st = decode(cfg, layer, cache, batch, n_kv_heads, n_kv_heads, context_len, w > 0 ? qsel_rot : nullptr, qsel_sk,

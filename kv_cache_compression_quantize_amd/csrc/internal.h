@@ -158,7 +158,9 @@ hipError_t launch_prepare_query(const QueryJob &job, hipStream_t stream);
 hipError_t launch_decode(const DecodeJob &job, hipStream_t stream);
 hipError_t launch_combine(const DecodeJob &job, hipStream_t stream);
 int topk_chunks(int budget);
-hipError_t launch_selection_query(const float *q, int64_t n_slots, int d, int g, float *qsel, hipStream_t stream);
+// the slots' selection queries (sum of their heads' unit queries), rotated (q_rot, may be null) and sketched
+hipError_t launch_selection_query(const float *q, int64_t n_slots, int d, int g, int m, const float *rotation,
+                                  const float *sketch, float *q_rot, float *q_sk, hipStream_t stream);
 hipError_t launch_topk(const TopkJob &job, hipStream_t stream);
 // the split combine with a recent-token window merged in (in place of launch_combine)
 hipError_t launch_combine_window(const DecodeJob &job, const WindowJob &wj, hipStream_t stream);

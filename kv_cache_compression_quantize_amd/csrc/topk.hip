@@ -3,7 +3,7 @@
 // cache, and decode attention over the chosen tokens only.
 //
 //   selection_query_kernel  per KV slot: q_sel = sum of the unit query vectors
-//                           of its query heads
+//                           of its query heads, rotated and sketched
 //   (the estimator of <q_sel, k_t> for every cached token comes from the
 //   decoder's score output)
 //   topk_select_kernel      per KV slot (1024 threads): cos_t = score_t / ||k_t||
@@ -40,20 +40,61 @@ __device__ __forceinline__ float block_reduce_sum(float x, float *red) {
 
 // --------------------------------------------------------------- selection query
 
-__global__ __launch_bounds__(kThreads) void selection_query_kernel(const float *__restrict__ q, int d, int g,
-                                                                   float *__restrict__ qsel) {
+// Per (KV slot, 64 output rows of the stacked [Pi; S]): the slot's selection
+// query q_sel = sum over its query heads of q_h / ||q_h|| is built in LDS, then
+// rotated and sketched as in query preparation (sixteen lanes per row, every
+// row load issued before the query is built).
+constexpr int kSelQRows = 64;
+template <int D>
+__global__ __launch_bounds__(kThreads) void selection_query_kernel(const float *__restrict__ q, int g, int m,
+                                                                   const float *__restrict__ rotation,
+                                                                   const float *__restrict__ sketch,
+                                                                   float *__restrict__ q_rot,
+                                                                   float *__restrict__ q_sk, int chunks) {
+  __shared__ float qs[D];
   __shared__ float red[4];
-  const int64_t slot = blockIdx.x;
+  const int64_t slot = blockIdx.x / chunks;
+  const int chunk = static_cast<int>(blockIdx.x % chunks);
+  const int tid = threadIdx.x;
+  const int d_rot = q_rot ? D : 0;
+  const int rows = d_rot + m;
+  constexpr int kLanes = 16;
+  constexpr int kGroups = kThreads / kLanes;
+  constexpr int kIter = kSelQRows / kGroups;
+  constexpr int kPer = D / kLanes;
+  const int sub = tid % kLanes, grp = tid / kLanes;
+  float a[kIter][kPer];
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int row = chunk * kSelQRows + it * kGroups + grp;
+    const float *src = row < d_rot ? rotation + static_cast<int64_t>(row) * D
+                                   : sketch + static_cast<int64_t>(row - d_rot) * D;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) a[it][i] = row < rows ? src[sub + kLanes * i] : 0.0f;
+  }
   float acc = 0.0f;
   for (int h = 0; h < g; ++h) {
-    const float *qh = q + (slot * g + h) * d;
-    float ss = 0.0f;
-    for (int j = threadIdx.x; j < d; j += kThreads) ss = fmaf(qh[j], qh[j], ss);
-    const float n = sqrtf(block_reduce_sum(ss, red));
-    const float inv = n > 0.0f ? 1.0f / n : 0.0f;
-    if (threadIdx.x < d) acc = fmaf(qh[threadIdx.x], inv, acc);
+    const float x = tid < D ? q[(slot * g + h) * D + tid] : 0.0f;
+    const float n = sqrtf(block_reduce_sum(x * x, red));
+    acc = fmaf(x, n > 0.0f ? 1.0f / n : 0.0f, acc);
   }
-  if (threadIdx.x < d) qsel[slot * d + threadIdx.x] = acc;
+  if (tid < D) qs[tid] = acc;
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int row = chunk * kSelQRows + it * kGroups + grp;
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v = fmaf(a[it][i], qs[sub + kLanes * i], v);
+#pragma unroll
+    for (int off = kLanes / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kLanes);
+    if (sub == 0 && row < rows) {
+      if (row < d_rot)
+        q_rot[slot * D + row] = v;
+      else
+        q_sk[slot * m + (row - d_rot)] = v;
+    }
+  }
 }
 
 // --------------------------------------------------------------- top-K select
@@ -637,8 +678,22 @@ hipError_t launch_sparse_d(const SparseJob &job, int64_t n_slots, hipStream_t st
 
 int topk_chunks(int budget) { return (budget + kChunkTokens - 1) / kChunkTokens; }
 
-hipError_t launch_selection_query(const float *q, int64_t n_slots, int d, int g, float *qsel, hipStream_t stream) {
-  selection_query_kernel<<<static_cast<unsigned>(n_slots), kThreads, 0, stream>>>(q, d, g, qsel);
+hipError_t launch_selection_query(const float *q, int64_t n_slots, int d, int g, int m, const float *rotation,
+                                  const float *sketch, float *q_rot, float *q_sk, hipStream_t stream) {
+  const int rows = (q_rot ? d : 0) + m;
+  const int chunks = (rows + kSelQRows - 1) / kSelQRows;
+  const unsigned grid = static_cast<unsigned>(n_slots * chunks);
+  switch (d) {
+    case 64:
+      selection_query_kernel<64><<<grid, kThreads, 0, stream>>>(q, g, m, rotation, sketch, q_rot, q_sk, chunks);
+      break;
+    case 128:
+      selection_query_kernel<128><<<grid, kThreads, 0, stream>>>(q, g, m, rotation, sketch, q_rot, q_sk, chunks);
+      break;
+    default:
+      selection_query_kernel<256><<<grid, kThreads, 0, stream>>>(q, g, m, rotation, sketch, q_rot, q_sk, chunks);
+      break;
+  }
   return hipGetLastError();
 }
 
