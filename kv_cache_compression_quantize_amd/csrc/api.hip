@@ -375,6 +375,7 @@ static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const
   job.part_acc = static_cast<float *>(workspace);
   char *ws = static_cast<char *>(workspace);
   job.part_ml = reinterpret_cast<float *>(ws + plan.acc_bytes);
+  job.scores_only = scores_only && scores && !win ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the matrix-core decoder addresses a slot's records with 32-bit byte offsets
   if (plan.mfma && cache->capacity / kBlockRows * L.rec >= (int64_t(1) << 31)) return AQKV_ERR_UNSUPPORTED;

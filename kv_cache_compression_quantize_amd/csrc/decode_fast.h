@@ -325,9 +325,16 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   const int64_t recs = job.capacity / kTT;
   const __amdgpu_buffer_rsrc_t rs_blocks =
       plane_rsrc(job.blocks + slot * recs * Gm::tile_bytes, static_cast<uint32_t>(recs * Gm::tile_bytes));
+  // a scores-only call needs the key fields of a record alone (they come first); the
+  // wait below is for all loads in flight, so the shorter tiles need no other count
+  static_assert(kRing == 2, "tile waits assume one tile in flight beside the current one");
+  const bool keys_only = job.scores_only != 0;
   auto issue = [&](int64_t tile) {
     const uint32_t rec = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t_begin / kTT + tile));
-    copy_region<Gm::tile_bytes>(rs_blocks, rec * Gm::tile_bytes, slot_buf(tile), lane);
+    if (keys_only)
+      copy_region<Gm::o_vcodes>(rs_blocks, rec * Gm::tile_bytes, slot_buf(tile), lane);
+    else
+      copy_region<Gm::tile_bytes>(rs_blocks, rec * Gm::tile_bytes, slot_buf(tile), lane);
   };
   // register-resident operands are staged in the last ring slots, which load
   // last, so the first tiles stream in while the query side is built (when the
@@ -495,6 +502,16 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
         logit[ct][r] = (valid && g < G) ? s * lscale : -INFINITY;
       }
     }
+    if (keys_only) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const int g = 4 * r + q, tok = 16 * ct + n16;
+          if (g < G && tok < nt) job.scores[(head0 + g) * job.context + t0 + tok] = score[ct][r];
+        }
+      continue;
+    }
 
     // ---------------- online softmax (lazy rescale); lane group q = head 4r + q
     float fac[RB];
@@ -637,6 +654,8 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
     }
     compiler_fence();
   }
+
+  if (keys_only) return;   // uniform over the block: no partials to merge
 
   // ---------------- per-wave results -> LDS, merge the 4 waves
   __syncthreads();

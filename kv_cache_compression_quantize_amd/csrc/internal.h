@@ -106,6 +106,8 @@ struct DecodeJob {
   float *part_acc;       // [n_slots*g][part_stride][d]
   float *part_ml;        // [n_slots*g][part_stride][2]
   int part_stride;       // partials per head (the decoder's splits; 0 when there is none)
+  int scores_only;       // non-zero: only the score output is wanted (the matrix-core decoder then
+                         // reads the key fields alone and writes no partials)
 };
 
 // The recent-token window of a decode call, merged in by the combine
