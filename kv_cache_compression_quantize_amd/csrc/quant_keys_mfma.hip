@@ -31,8 +31,9 @@
 // is, its B operand for k-step k of the sketch product, whose weight columns
 // follow the same permutation.  No fp key and no reconstruction is formed.
 //
-// The weights (Pi, and S Pi^T or S) are prepared once per call into the
-// workspace as ready-made MFMA A operands, [slab][k-step][hi, lo][lane][8 f16],
+// The weights (Pi, and S Pi^T or S) are prepared into the workspace (per
+// call, or once per layer through the prepared entry points) as ready-made
+// MFMA A operands, [slab][k-step][hi, lo][lane][8 f16],
 // one slab per 16-row tile.  When the whole set fits in LDS (d = 128, m = 128:
 // 128 KiB) a block of 8 waves loads it once and every wave then walks its own
 // 32-key tiles without block synchronisation, prefetching the next tile's
@@ -670,58 +671,11 @@ __device__ __forceinline__ void key_operand_as_sketch_input(const Ops<D> &uh, co
   }
 }
 
-// z[tz] += sketch slab tz, k-step k (this lane's bytes of the slab at `slab`)
-// x the B operand (hi, and lo when THREE) of that k-step, for every key block
-template <int D, bool THREE>
-__device__ __forceinline__ void sketch_kstep(v4f (&z)[Geo<D>::NT], const uint8_t *slab, int k, const Op (&bh)[Geo<D>::NT],
-                                             const Op (&bl)[Geo<D>::NT]) {
-  const v8h ah = lds_op(slab + (2 * k) * 1024);
-  const v8h al = lds_op(slab + (2 * k + 1) * 1024);
-#pragma unroll
-  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
-    z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(bh[nt]), z[nt], 0, 0, 0);
-    if (THREE) z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, as_v8h(bl[nt]), z[nt], 0, 0, 0);
-    z[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, as_v8h(bh[nt]), z[nt], 0, 0, 0);
-  }
-}
-
-// Sign words from the finished sketch accumulators z[TMS][NT] (TMS slabs;
-// full groups of 8 slabs give one word per lane group, a trailing group of 4
-// a half word per lane group), stored at once.
-template <int D, int TMS>
-__device__ __forceinline__ void store_signs(const KeyJob &job, const v4f (&z)[TMS][Geo<D>::NT], int g,
-                                            const float (&nrm)[Geo<D>::NT], const TileLoc<D> &L) {
-  constexpr int FM = TMS / 8;
-  constexpr int WM = FM + (TMS % 8 ? 1 : 0);
-  const int64_t srow_bytes = job.m / 8;
-#pragma unroll
-  for (int nt = 0; nt < Geo<D>::NT; ++nt) {
-    const bool zero_key = !(nrm[nt] > 0.0f);
-#pragma unroll
-    for (int wl = 0; wl < WM; ++wl) {
-      const int cnt = wl < FM ? 8 : 4;
-      uint32_t v = 0u;
-#pragma unroll
-      for (int j = cnt - 1; j >= 0; --j)
-#pragma unroll
-        for (int i = 3; i >= 0; --i) v = push_bit(v, z[8 * wl + j][nt][i] >= 0.0f || zero_key);
-      if (cnt == 4) {
-        v <<= 16 * (g & 1);
-        v |= __shfl_xor(v, 16);
-      }
-      if (L.valid[nt] && (cnt == 8 || (g & 1) == 0))
-        reinterpret_cast<uint32_t *>(job.signs + rec_row(L.row[nt], srow_bytes, job.rec))[cnt == 8 ? 4 * wl + g : 4 * FM + (g >> 1)] = v;
-    }
-  }
-}
-
 // ---- resident operands: the whole operand set sits in LDS; every wave then
 // walks its own key tiles (no block synchronisation), the next tile's keys
-// loading while the current one is computed.  Within a tile the sketch is
-// accumulated k-step by k-step for all TMS slabs (z stays in registers) right
-// after the two coordinate tiles of that k-step are rotated and indexed, so
-// matrix products and vector work interleave; only one k-step of the
-// residual operand is ever live.
+// loading while the current one is computed.  A tile is rotated and indexed
+// first (each rotation tile issued one tile ahead of its index work), then
+// sketched slab by slab from the residual operands built by the indexing.
 template <int D, int W, bool BF16, int TMS, bool SYM, bool EXACT>
 __device__ __forceinline__ void resident_body(const KeyJob &job, int64_t n_tiles, uint8_t *smem) {
   using Gm = Geo<D>;
