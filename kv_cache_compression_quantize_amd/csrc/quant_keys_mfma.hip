@@ -109,8 +109,6 @@ __device__ __forceinline__ uint32_t push_bit(uint32_t w, bool bit) { return w + 
 
 // ---------------------------------------------------------------- operands
 
-// One thread per (slab, k-step, lane, slot): writes the high and low f16
-// parts of one A-operand element (scaled by 2^8).
 // Whether every entry of the rotation has one magnitude a (a randomised
 // Hadamard rotation: +-1/sqrt(d)); writes a, or 0, to *scale.  One block.
 __global__ __launch_bounds__(256) void rotation_scale_kernel(const float *__restrict__ rot, int d,
@@ -122,6 +120,8 @@ __global__ __launch_bounds__(256) void rotation_scale_kernel(const float *__rest
   if (threadIdx.x == 0) *scale = same ? a : 0.0f;
 }
 
+// One thread per (slab, k-step, lane, slot): writes the high and low f16
+// parts of one A-operand element (scaled by 2^8).
 __global__ __launch_bounds__(256) void key_operands_kernel(const float *__restrict__ rot,
                                                            const float *__restrict__ sketch,
                                                            uint8_t *__restrict__ ops, int d, int w, int m,
@@ -483,10 +483,9 @@ __device__ __forceinline__ void index_vals(int t, const v4f (&acc)[Geo<D>::NT], 
             if (((j + 1) & ((1 << p) - 1)) == 0) bit ^= a[j];
           S.wv[p][nt] = push_bit(S.wv[p][nt], bit);
         }
-        // e' = sign(y) (|y'| - c'_m)
-        const float em = fmaf(aa, yscale[nt], -cm);
-        e[i] = __uint_as_float(__float_as_uint(em) ^ (__float_as_uint(av) & 0x80000000u));
-        S.esq[nt] = fmaf(em, em, S.esq[nt]);
+        // e' = sign(y) (|y'| - c'_m) = y' - sign(y) c'_m (yscale >= 0; rounding is symmetric)
+        e[i] = fmaf(av, yscale[nt], -copysignf(cm, av));
+        S.esq[nt] = fmaf(e[i], e[i], S.esq[nt]);
       }
     } else {
 #pragma unroll
@@ -598,24 +597,28 @@ __device__ __forceinline__ void sketch_slab(const KeyJob &job, const SlabOps<D> 
   const bool full = tz < 8 * FM;
   const int sub = full ? (tz & 7) : (tz & 3);
   const int64_t srow_bytes = job.m / 8;
+  // sw collects the sign bits of z (bit 4 sub + i from z[i]); a sign bit set
+  // means z < 0 (z is never -0: the accumulation starts at +0), so the stored
+  // word is its complement, all ones for a zero key
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const bool zero_key = !(nrm[nt] > 0.0f);
-    uint32_t bits = 0u;
+    uint32_t nib = 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bits |= static_cast<uint32_t>(z[nt][i] >= 0.0f || zero_key) << i;
-    sw[nt] |= bits << (4 * sub);
+    for (int i = 3; i >= 0; --i) nib = __builtin_amdgcn_alignbit(nib, __float_as_uint(z[nt][i]), 31);
+    sw[nt] |= nib << (4 * sub);
   }
   if (full && sub == 7) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      if (L.valid[nt]) reinterpret_cast<uint32_t *>(job.signs + rec_row(L.row[nt], srow_bytes, job.rec))[4 * (tz >> 3) + g] = sw[nt];
+      const uint32_t v = nrm[nt] > 0.0f ? ~sw[nt] : 0xffffffffu;
+      if (L.valid[nt]) reinterpret_cast<uint32_t *>(job.signs + rec_row(L.row[nt], srow_bytes, job.rec))[4 * (tz >> 3) + g] = v;
       sw[nt] = 0u;
     }
   } else if (!full && sub == 3) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      uint32_t v = sw[nt] << (16 * (g & 1));
+      uint32_t v = (nrm[nt] > 0.0f ? ~sw[nt] : 0xffffffffu) & 0xffffu;
+      v <<= 16 * (g & 1);
       v |= __shfl_xor(v, 16);
       if (L.valid[nt] && (g & 1) == 0)
         reinterpret_cast<uint32_t *>(job.signs + rec_row(L.row[nt], srow_bytes, job.rec))[4 * FM + (g >> 1)] = v;
