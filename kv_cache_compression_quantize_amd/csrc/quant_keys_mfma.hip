@@ -199,9 +199,12 @@ struct RawKeys {
 // Where this lane's keys of a wave tile live: key0 (wave-uniform) + nt*16 + n.
 template <int D>
 struct TileLoc {
-  int64_t src[Geo<D>::NT];   // element offset of the key row in the K view
-  int64_t row[Geo<D>::NT];   // cache row
+  int64_t src[Geo<D>::NT];    // element offset of the key row in the K view
+  int64_t rbase[Geo<D>::NT];  // byte offset of the cache row's record (rec_row's record term)
+  int rin[Geo<D>::NT];        // the row's place in its record (0 .. 31)
   bool valid[Geo<D>::NT];
+  // byte offset of the row in a field whose rows are rb bytes (= rec_row(row, rb, rec))
+  __device__ __forceinline__ int64_t at(int nt, int rb) const { return rbase[nt] + rin[nt] * rb; }
 };
 
 template <int D>
@@ -244,7 +247,9 @@ __device__ __forceinline__ TileLoc<D> locate(const KeyJob &job, int64_t key0, in
       h = slot - b * job.heads;
     }
     L.src[nt] = b * job.batch_stride + h * job.head_stride + t * job.token_stride;
-    L.row[nt] = slot * job.capacity + job.token_offset + t;
+    const int64_t row = slot * job.capacity + job.token_offset + t;
+    L.rbase[nt] = (row >> 5) * job.rec;
+    L.rin[nt] = static_cast<int>(row & 31);
   }
   return L;
 }
@@ -596,7 +601,7 @@ __device__ __forceinline__ void sketch_slab(const KeyJob &job, const SlabOps<D> 
   }
   const bool full = tz < 8 * FM;
   const int sub = full ? (tz & 7) : (tz & 3);
-  const int64_t srow_bytes = job.m / 8;
+  const int srow_bytes = job.m / 8;
   // sw collects the sign bits of z (bit 4 sub + i from z[i]); a sign bit set
   // means z < 0 (z is never -0: the accumulation starts at +0), so the stored
   // word is its complement, all ones for a zero key
@@ -611,7 +616,7 @@ __device__ __forceinline__ void sketch_slab(const KeyJob &job, const SlabOps<D> 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const uint32_t v = nrm[nt] > 0.0f ? ~sw[nt] : 0xffffffffu;
-      if (L.valid[nt]) reinterpret_cast<uint32_t *>(job.signs + rec_row(L.row[nt], srow_bytes, job.rec))[4 * (tz >> 3) + g] = v;
+      if (L.valid[nt]) reinterpret_cast<uint32_t *>(job.signs + L.at(nt, srow_bytes))[4 * (tz >> 3) + g] = v;
       sw[nt] = 0u;
     }
   } else if (!full && sub == 3) {
@@ -621,7 +626,7 @@ __device__ __forceinline__ void sketch_slab(const KeyJob &job, const SlabOps<D> 
       v <<= 16 * (g & 1);
       v |= __shfl_xor(v, 16);
       if (L.valid[nt] && (g & 1) == 0)
-        reinterpret_cast<uint32_t *>(job.signs + rec_row(L.row[nt], srow_bytes, job.rec))[4 * FM + (g >> 1)] = v;
+        reinterpret_cast<uint32_t *>(job.signs + L.at(nt, srow_bytes))[4 * FM + (g >> 1)] = v;
       sw[nt] = 0u;
     }
   }
@@ -635,7 +640,7 @@ __device__ __forceinline__ void store_codes_norms(const KeyJob &job, const TileL
   for (int nt = 0; nt < Geo<D>::NT; ++nt) {
     if (!L.valid[nt]) continue;
     if constexpr (W > 0) {
-      uint8_t *crow = job.codes + rec_row(L.row[nt], W * D / 8, job.rec);
+      uint8_t *crow = job.codes + L.at(nt, W * D / 8);
 #pragma unroll
       for (int p = 0; p < W; ++p) {
         uint32_t *plane = reinterpret_cast<uint32_t *>(crow + p * (D / 8));
@@ -646,8 +651,8 @@ __device__ __forceinline__ void store_codes_norms(const KeyJob &job, const TileL
       }
     }
     if (g == 0) {
-      *reinterpret_cast<float *>(job.norm + rec_row(L.row[nt], 4, job.rec)) = nrm[nt];
-      if constexpr (W > 0) *reinterpret_cast<float *>(job.rnorm + rec_row(L.row[nt], 4, job.rec)) = gam[nt];
+      *reinterpret_cast<float *>(job.norm + L.at(nt, 4)) = nrm[nt];
+      if constexpr (W > 0) *reinterpret_cast<float *>(job.rnorm + L.at(nt, 4)) = gam[nt];
     }
   }
 }
@@ -701,7 +706,9 @@ __device__ __forceinline__ void resident_body(const KeyJob &job, int64_t n_tiles
   const float rot_a = EXACT ? job.rot_scale[0] : 0.0f;
   constexpr bool lo_pass = !EXACT;
   RawKeys<D, BF16> R;
-  load_keys<D, BF16>(job, locate<D>(job, tile * Gm::KT, n), g, R);
+  // Lk: where the keys in R came from; kept for the tile's stores
+  TileLoc<D> Lk = locate<D>(job, tile * Gm::KT, n);
+  load_keys<D, BF16>(job, Lk, g, R);
   for (; tile < n_tiles; tile += stride) {
     float nrm[NT], yscale[NT];
     Op uh[NT][KS], ul[NT][KS];
@@ -770,8 +777,11 @@ __device__ __forceinline__ void resident_body(const KeyJob &job, int64_t n_tiles
     }
     // 2. the sketch, slab by slab (sign words stored as their groups complete),
     // while the next tile's keys stream in
-    if (tile + stride < n_tiles) load_keys<D, BF16>(job, locate<D>(job, (tile + stride) * Gm::KT, n), g, R);
-    const TileLoc<D> Lc = locate<D>(job, tile * Gm::KT, n);
+    const TileLoc<D> Lc = Lk;
+    if (tile + stride < n_tiles) {
+      Lk = locate<D>(job, (tile + stride) * Gm::KT, n);
+      load_keys<D, BF16>(job, Lk, g, R);
+    }
     uint32_t sw[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) sw[nt] = 0u;
