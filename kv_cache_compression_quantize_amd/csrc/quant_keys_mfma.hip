@@ -93,10 +93,14 @@ __device__ __forceinline__ float opaque_minus1() {
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi2, uint32_t &lo2, float minus1) {
   asm volatile("" : "+v"(a), "+v"(b));
   const v2h h = __builtin_convertvector((v2f){a, b}, v2h);
-  const v2f r = {__builtin_fmaf(static_cast<float>(h[0]), minus1, a),
-                 __builtin_fmaf(static_cast<float>(h[1]), minus1, b)};
+  // a - hi is exact in fp32, so rounding it to f16 in a mixed fma with an f16
+  // result is the same as rounding the fp32 difference.  (Compiler-emitted:
+  // a matrix instruction may read these operands soon after, and only the
+  // compiler's own instructions get the wait states that requires.)
+  const v2h l = {static_cast<_Float16>(__builtin_fmaf(static_cast<float>(h[0]), minus1, a)),
+                 static_cast<_Float16>(__builtin_fmaf(static_cast<float>(h[1]), minus1, b))};
   hi2 = __builtin_bit_cast(uint32_t, h);
-  lo2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, v2h));
+  lo2 = __builtin_bit_cast(uint32_t, l);
 }
 
 __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
@@ -489,7 +493,11 @@ __device__ __forceinline__ void index_vals(int t, const v4f (&acc)[Geo<D>::NT], 
           S.wv[p][nt] = push_bit(S.wv[p][nt], bit);
         }
         // e' = sign(y) (|y'| - c'_m) = y' - sign(y) c'_m (yscale >= 0; rounding is symmetric)
-        e[i] = fmaf(av, yscale[nt], -copysignf(cm, av));
+        // (the empty asm keeps the negation on the fma's operand instead of
+        // an extra sign flip of av)
+        float cs = copysignf(cm, av);
+        asm("" : "+v"(cs));
+        e[i] = fmaf(av, yscale[nt], -cs);
         S.esq[nt] = fmaf(e[i], e[i], S.esq[nt]);
       }
     } else {
