@@ -292,15 +292,26 @@ size_t aqkv_decode_topk_workspace_bytes(const aqkv_config *cfg, int32_t batch, i
  * [batch][n_q_heads][d] (dev fp32, contiguous); q_rot and q_sketch are its
  * aqkv_prepare_query outputs.  selected, if not NULL, receives the chosen rows
  * of every slot in increasing order ([batch * n_kv_heads][min(budget,
- * context_len)] int32, dev).  budget in 1..2^20.  workspace (dev, 256-byte
- * aligned) must hold aqkv_decode_topk_workspace_bytes(...) bytes.  Other rules
- * as aqkv_decode_attention. */
+ * context_len)] int32, dev).  budget in 1..2^20; context_len at most
+ * 2^31 - 2^20 rows (row indices are 32-bit), AQKV_ERR_UNSUPPORTED beyond.
+ * workspace (dev, 256-byte aligned) must hold
+ * aqkv_decode_topk_workspace_bytes(...) bytes.  Other rules as
+ * aqkv_decode_attention. */
 aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer *layer,
                                        const aqkv_cache *cache, int32_t batch, int32_t n_q_heads,
                                        int32_t n_kv_heads, int64_t context_len, const float *q,
                                        const float *q_rot, const float *q_sketch, int64_t budget,
                                        float softmax_scale, int32_t *selected, float *out,
                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------- measurement helper */
+
+/* Reads `bytes` of device memory at `data` once, as a plain stream of 16-byte
+ * loads spread over the whole GPU, and xors everything read into *sink (dev,
+ * one uint32): the practical ceiling of HBM reads against which the decode's
+ * streaming rate is compared (no step of the method).  data and bytes must be
+ * multiples of 16.  Enqueues on `stream` only. */
+aqkv_status aqkv_read_stream(const void *data, size_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

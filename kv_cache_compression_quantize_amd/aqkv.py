@@ -103,6 +103,7 @@ _SIGS = {
                                                C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
                                                _P(KvView), _P(KvView), C.c_float, C.c_void_p, C.c_void_p,
                                                C.c_void_p, C.c_size_t, C.c_void_p]),
+    "aqkv_read_stream": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
 }
 
 _lib_handle = None
@@ -430,3 +431,9 @@ def decode_attention_topk(cfg: Config, layer: Layer, cache: Cache, batch: int, n
                                           _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "aqkv_decode_attention_topk")
     return out
+
+
+def read_stream(buf, sink, stream=None):
+    """One plain read of a device buffer (the HBM read ceiling probe); sink: a 1-element int32 tensor."""
+    _check(lib().aqkv_read_stream(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
+           "aqkv_read_stream")

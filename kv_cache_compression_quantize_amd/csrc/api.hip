@@ -471,6 +471,7 @@ aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer 
   const int g = n_q_heads / n_kv_heads;
   if (g > kMaxQPerKv) return AQKV_ERR_UNSUPPORTED;
   if (budget > kMaxBudget) return AQKV_ERR_UNSUPPORTED;
+  if (context_len > kMaxTopkContext) return AQKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(batch) * n_kv_heads != cache->n_slots) return AQKV_ERR_SHAPE;
   if (context_len > cache->capacity) return AQKV_ERR_CAPACITY;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return AQKV_ERR_SHAPE;

@@ -89,20 +89,15 @@ __device__ __forceinline__ v4i spread_half(uint32_t x, int hf) {
   return r;
 }
 
-// max over the 16 lanes of a DPP row, result in every lane of the row: one
-// v_max_f32 with a DPP source per step (the s_nop covers the VALU-write ->
-// DPP-read hazard the compiler cannot see through the asm)
+// max over the 16 lanes of a DPP row, result in every lane of the row: the
+// same four lane permutations as row_sum16, through the compiler's DPP move
+// (so the compiler places the wait states a DPP read of a fresh VALU result
+// needs)
 __device__ __forceinline__ float row_max16(float x) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 1\n\t"
-      "v_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 1\n\t"
-      "v_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"
-      "s_nop 1\n\t"
-      "v_max_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf"
-      : "+v"(x));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
   return x;
 }
 __device__ __forceinline__ float row_sum16(float x) {

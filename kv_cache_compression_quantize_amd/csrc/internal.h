@@ -125,6 +125,9 @@ struct WindowJob {
 
 // Query-aware top-K preselection and decode over the chosen tokens
 constexpr int64_t kMaxBudget = int64_t{1} << 20;
+// the select kernel indexes a slot's rows with 32-bit integers, a batch of
+// rows past the last one included
+constexpr int64_t kMaxTopkContext = (int64_t{1} << 31) - (int64_t{1} << 20);
 struct TopkJob {
   int d, w, m, vb, g;
   int64_t n_slots, capacity, context, rec;

@@ -18,9 +18,17 @@ Seeding
   into the rotation, and the QJL sketch S) come from
   ``numpy.random.PCG64(42 + 7 * layer)``: first the d*d matrix, then the
   m*d sketch, from one stream (TurboQuant article §六, per-layer seed rule).
-* Every K/V slice is drawn per (workload, layer, batch, kv-head, tensor,
-  token block of ``BLOCK`` tokens) from its own ``SeedSequence``, so any part
-  of a large cache can be regenerated on the host without reading it back.
+* K/V elements come from a counter-based generator, so any slice of a large
+  cache can be drawn on the host (numpy) or in bulk on the GPU (torch) with
+  identical bits: element i = t * d + j of one (workload, layer, batch,
+  kv-head, tensor) slot takes u = the top 16 bits of fmix32(key + i * 0x9E3779B9)
+  (fmix32: the 32-bit finaliser of MurmurHash3; key: 32 bits from a
+  ``SeedSequence`` of the slot's identifiers) and the value
+  Phi^-1((u + 1/2) / 2^16) from a 2^16-entry fp32 table of standard normal
+  quantiles (|x| <= 4.33), times the recipe's per-channel scale in fp32, then
+  rounded to bf16 (RNE) for bf16 workloads.  The same integer code runs on
+  numpy and torch arrays; the table and the scales are the same fp32 numbers
+  on both sides.
 """
 from __future__ import annotations
 
@@ -28,8 +36,6 @@ from dataclasses import dataclass
 from typing import Optional, Tuple
 
 import numpy as np
-
-BLOCK = 4096  # tokens per independently seeded block of a K/V slot
 
 _TENSOR_IDS = {"k": 1, "v": 2, "q": 3, "outlier": 4, "kscale": 5, "vscale": 6}
 
@@ -141,6 +147,49 @@ def _rng(w: Workload, layer: int, b: int, h: int, tensor: str, block: int = 0) -
     return np.random.Generator(np.random.PCG64(ss))
 
 
+def slot_key(w: Workload, layer: int, b: int, h: int, tensor: str) -> int:
+    """32-bit key of one K/V slot for the counter-based generator."""
+    ss = np.random.SeedSequence([w.wid, layer, b, h, _TENSOR_IDS[tensor]])
+    return int(ss.generate_state(1, np.uint32)[0])
+
+
+_M32 = 0xFFFFFFFF
+_WEYL = 0x9E3779B9
+
+
+def _mul32(h, c: int):
+    """(h * c) mod 2^32 for int64 arrays h < 2^32 (numpy or torch): the constant is
+    split in 16-bit halves so no product leaves int64."""
+    return (h * (c & 0xFFFF) + (((h * (c >> 16)) & 0xFFFF) << 16)) & _M32
+
+
+def _fmix32(h):
+    """MurmurHash3's 32-bit finaliser on int64 arrays holding 32-bit values."""
+    h = h ^ (h >> 16)
+    h = _mul32(h, 0x85EBCA6B)
+    h = h ^ (h >> 13)
+    h = _mul32(h, 0xC2B2AE35)
+    return h ^ (h >> 16)
+
+
+def counter_u16(key, index):
+    """Top 16 bits of fmix32(key + index * 0x9E3779B9 mod 2^32); key and index are
+    int64 arrays (or ints) of the same backend, index < 2^32."""
+    return _fmix32((key + index * _WEYL) & _M32) >> 16
+
+
+_QTABLE = None
+
+
+def normal_table() -> np.ndarray:
+    """fp32 standard normal quantiles Phi^-1((u + 1/2) / 2^16), u = 0 .. 2^16 - 1."""
+    global _QTABLE
+    if _QTABLE is None:
+        from scipy.special import ndtri
+        _QTABLE = ndtri((np.arange(1 << 16, dtype=np.float64) + 0.5) / (1 << 16)).astype(np.float32)
+    return _QTABLE
+
+
 def _channel_scale(w: Workload, layer: int, h: int, tensor: str) -> Optional[np.ndarray]:
     d = w.head_dim
     if w.recipe == "outliers":
@@ -167,19 +216,42 @@ def kv_slot(w: Workload, layer: int, b: int, h: int, tensor: str,
     assert tensor in ("k", "v")
     t1 = w.context if t1 is None else t1
     d = w.head_dim
-    out = np.empty((t1 - t0, d), dtype=np.float32)
+    assert w.context * d <= (1 << 32)
+    idx = np.arange(t0 * d, t1 * d, dtype=np.int64)
+    u = counter_u16(np.int64(slot_key(w, layer, b, h, tensor)), idx)
+    out = normal_table()[u].reshape(t1 - t0, d)
     sc = _channel_scale(w, layer, h, tensor)
-    blk0, blk1 = t0 // BLOCK, (t1 + BLOCK - 1) // BLOCK
-    for blk in range(blk0, blk1):
-        bs, be = blk * BLOCK, min((blk + 1) * BLOCK, w.context)
-        rng = _rng(w, layer, b, h, tensor, blk)
-        x = rng.standard_normal((be - bs, d), dtype=np.float32)
-        if sc is not None:
-            x *= sc
-        lo, hi = max(bs, t0), min(be, t1)
-        out[lo - t0:hi - t0] = x[lo - bs:hi - bs]
+    if sc is not None:
+        out = out * sc
     if w.dtype == "bf16":
         out = bf16_bits_to_f32(to_bf16_bits(out))
+    return out
+
+
+def kv_device(w: Workload, layer: int, tensor: str, device="cuda", slots_per_pass: int = 16):
+    """The whole K or V tensor [B, Hkv, T, d] of a workload layer drawn on the GPU
+    (bf16 or fp32 torch tensor): the same numbers as kv_slot gives slot by slot."""
+    import torch
+    d, T = w.head_dim, w.context
+    assert T * d <= (1 << 32)
+    tdtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = torch.empty((w.batch, w.n_kv_heads, T, d), dtype=tdtype, device=device)
+    table = torch.from_numpy(normal_table()).to(device)
+    idx = torch.arange(T * d, dtype=torch.int64, device=device)
+    flat = out.view(w.n_slots, T, d)
+    for s0 in range(0, w.n_slots, slots_per_pass):
+        s1 = min(w.n_slots, s0 + slots_per_pass)
+        keys, scales = [], []
+        for s in range(s0, s1):
+            b, h = divmod(s, w.n_kv_heads)
+            keys.append(slot_key(w, layer, b, h, tensor))
+            scales.append(_channel_scale(w, layer, h, tensor))
+        key_t = torch.tensor(keys, dtype=torch.int64, device=device)[:, None]
+        x = table[counter_u16(key_t, idx[None, :])].view(s1 - s0, T, d)
+        if scales[0] is not None:   # a recipe scales every slot of a tensor or none
+            x = x * torch.from_numpy(np.stack(scales)).to(device)[:, None, :]
+        flat[s0:s1] = x.to(tdtype)
+        del x
     return out
 
 

@@ -260,3 +260,8 @@ def test_decode_topk_validation_codes():
     assert call(q=FAKE + 4) == -3
     assert call(hq=5) == -2
     assert call(ws=need - 1) == -5
+    # row indices of the select are 32-bit: longer contexts are refused before any launch
+    big = (1 << 31) - (1 << 20) + 32
+    cache = _cache(cap=big)
+    assert lib.aqkv_decode_attention_topk(C.byref(cfg), C.byref(layer), C.byref(cache), 1, 4, 2, big, FAKE, FAKE,
+                                          FAKE, 16, C.c_float(0.1), None, FAKE, FAKE, need, None) == -8

@@ -31,8 +31,11 @@ CASES = [
     ("llama2_7b_layer_mha32_t32k", 0),
     ("llama3_8b_layer_gqa32x8_b8_t128k", 0),
     ("d256_gqa32x16_b4_t64k", 0),
-    ("aqjl_32layer_gqa32x8_b16_t32k", 0),      # sketch k = 512
-    ("aqjl_32layer_gqa32x8_b16_t32k", 31),     # sketch k = 192
+    # one layer of every A-QJL group: sketch k = 512, 384, 256, 192
+    ("aqjl_32layer_gqa32x8_b16_t32k", 0),
+    ("aqjl_32layer_gqa32x8_b16_t32k", 8),
+    ("aqjl_32layer_gqa32x8_b16_t32k", 16),
+    ("aqjl_32layer_gqa32x8_b16_t32k", 31),
 ]
 
 

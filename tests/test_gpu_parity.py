@@ -34,6 +34,8 @@ KEY_CASES = [
     (128, 2, 128, "bf16"), (128, 2, 128, "fp32"), (256, 3, 256, "bf16"), (128, 0, 192, "bf16"),
     (128, 0, 512, "bf16"), (64, 1, 64, "fp32"), (128, 1, 128, "bf16"), (128, 3, 128, "bf16"),
     (128, 2, 256, "bf16"), (256, 0, 384, "fp32"),
+    # every A-QJL layer group's sketch size at d = 128 (k = 512, 384, 256, 192)
+    (128, 0, 384, "bf16"), (128, 0, 256, "bf16"), (128, 0, 384, "fp32"),
     # the largest sketch the library takes (1024 rows)
     (128, 0, 1024, "bf16"), (256, 2, 1024, "fp32"),
 ]
@@ -118,7 +120,8 @@ def test_hadamard_rotation_keys_and_decode(d, w, m, dtype):
     assert worst <= OUT_ATOL
 
 
-@pytest.mark.parametrize("d,w,m,nt", [(128, 2, 128, 1), (128, 2, 128, 7), (256, 3, 256, 5), (128, 0, 512, 3)])
+@pytest.mark.parametrize("d,w,m,nt", [(128, 2, 128, 1), (128, 2, 128, 7), (256, 3, 256, 5), (128, 0, 512, 3),
+                                      (128, 0, 384, 2)])
 def test_quantize_keys_small_append_many_slots(d, w, m, nt):
     """Decode-time appends: a few tokens for each of many slots, so one key
     tile spans several slots (and heads of several batches)."""
@@ -226,7 +229,7 @@ def test_chunked_append_matches_one_call():
 
 
 @pytest.mark.parametrize("d,w,m,qdtype", [(128, 2, 128, "fp32"), (128, 0, 512, "bf16"), (256, 3, 256, "fp32"),
-                                           (64, 1, 64, "bf16"), (256, 0, 1024, "fp32")])
+                                           (64, 1, 64, "bf16"), (256, 0, 1024, "fp32"), (128, 0, 384, "fp32")])
 def test_prepare_query_parity(d, w, m, qdtype):
     torch, dev = torch_dev()
     say("prepare_query", d, w, m, qdtype)
@@ -275,6 +278,9 @@ DECODE_CASES = [
     (128, 2, 128, 4, 2, 1000), (128, 2, 128, 1, 2, 256), (128, 2, 128, 2, 2, 1), (128, 2, 128, 8, 2, 4097),
     (256, 3, 256, 2, 2, 700), (128, 0, 192, 4, 2, 513), (128, 0, 512, 4, 2, 300), (64, 1, 64, 4, 4, 255),
     (128, 2, 128, 4, 4, 999),
+    # the A-QJL layer groups at d = 128, GQA 4 (k = 384 and 256 with 2- and 4-bit values)
+    (128, 0, 384, 4, 2, 700), (128, 0, 384, 4, 4, 333), (128, 0, 256, 4, 2, 4100), (128, 0, 256, 4, 4, 97),
+    (128, 0, 512, 4, 4, 1025), (128, 0, 192, 4, 4, 64),
     # shapes without a matrix-core kernel (sketch rows != 64 x d/64 with mse bits): the scalar decoder
     (128, 2, 256, 4, 2, 700), (64, 2, 128, 2, 4, 300), (128, 1, 192, 8, 2, 257),
     # the largest sketch (1024 rows)
@@ -340,7 +346,8 @@ def test_decode_empty_context_and_degenerate_softmax():
 
 
 @pytest.mark.parametrize("d,w,m,G,dtype", [(128, 2, 128, 4, "bf16"), (128, 2, 128, 1, "fp32"),
-                                           (256, 3, 256, 2, "bf16"), (128, 0, 256, 4, "bf16")])
+                                           (256, 3, 256, 2, "bf16"), (128, 0, 256, 4, "bf16"),
+                                           (128, 0, 384, 4, "bf16"), (128, 0, 512, 4, "bf16")])
 def test_end_to_end(d, w, m, G, dtype):
     torch, dev = torch_dev()
     say("end to end", d, w, m, G, dtype)

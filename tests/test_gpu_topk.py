@@ -22,6 +22,8 @@ CASES = [
     (128, 2, 128, 4, 1000, 100, 2), (128, 2, 128, 1, 700, 64, 2), (128, 2, 128, 8, 2050, 1, 2),
     (256, 3, 256, 2, 300, 129, 2), (128, 0, 192, 4, 513, 200, 2), (64, 1, 64, 2, 400, 65, 2),
     (128, 2, 128, 4, 300, 1000, 2), (128, 2, 128, 2, 900, 300, 4), (256, 3, 256, 1, 260, 70, 4),
+    # the A-QJL layer groups' sketch sizes (k = 384, 512) at GQA 4
+    (128, 0, 384, 4, 700, 90, 2), (128, 0, 512, 4, 400, 50, 4),
     # contexts past the select kernel's LDS capacity (32768 keys): keys in place of the scores
     (128, 2, 128, 1, 32769, 3000, 2), (128, 2, 128, 2, 40000, 500, 2),
 ]

@@ -18,6 +18,7 @@ CASES = [
     (128, 2, 128, 4, 300, 37, "bf16"), (128, 2, 128, 1, 1000, 128, "fp32"), (128, 2, 128, 8, 4097, 1024, "bf16"),
     (256, 3, 256, 2, 130, 16, "bf16"), (128, 0, 192, 4, 513, 64, "bf16"), (64, 1, 64, 8, 77, 5, "fp32"),
     (128, 2, 128, 4, 0, 15, "bf16"), (128, 2, 128, 2, 250, 1, "bf16"), (128, 2, 128, 2, 250, 0, "bf16"),
+    (128, 0, 384, 4, 400, 96, "bf16"),
 ]
 
 
