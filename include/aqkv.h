@@ -85,7 +85,8 @@ typedef enum {
   AQKV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
   AQKV_ERR_DTYPE = -6,       /* unknown element type */
   AQKV_ERR_HIP = -7,         /* the HIP runtime reported an error */
-  AQKV_ERR_UNSUPPORTED = -8  /* valid request the library does not implement */
+  AQKV_ERR_UNSUPPORTED = -8, /* valid request the library does not implement */
+  AQKV_ERR_SCRATCH = -9      /* needs more than the library's static scratch (allocation-free call) */
 } aqkv_status;
 
 typedef enum { AQKV_FP32 = 0, AQKV_BF16 = 1 } aqkv_dtype;
@@ -303,6 +304,29 @@ aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer 
                                        const float *q_rot, const float *q_sketch, int64_t budget,
                                        float softmax_scale, int32_t *selected, float *out,
                                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* -------------------------------------------------- allocation-free variant */
+
+/* For callers that cannot allocate device memory or hand over a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): aqkv_decode_attention with its split partials in a static
+ * device scratch of the library instead of a caller workspace.  Same
+ * arguments, results and rules as aqkv_decode_attention without workspace /
+ * workspace_bytes; calls nothing that allocates.  The scratch holds
+ * aqkv_decode_static_scratch_bytes() bytes (8 MiB) on every device the
+ * library runs on, kept until the process ends; a call whose partials
+ * (aqkv_decode_workspace_bytes for the same sizes) exceed it returns
+ * AQKV_ERR_SCRATCH before enqueuing anything.  Every call on one device
+ * shares that device's scratch, so calls that overlap on one device (on
+ * different streams, or from several threads) race; calls ordered on one
+ * stream do not.  The first call on a device looks up the device's copy of
+ * the scratch (once per device; thread-safe). */
+size_t aqkv_decode_static_scratch_bytes(void);
+aqkv_status aqkv_decode_attention_noalloc(const aqkv_config *cfg, const aqkv_layer *layer,
+                                          const aqkv_cache *cache, int32_t batch, int32_t n_q_heads,
+                                          int32_t n_kv_heads, int64_t context_len, const float *q_rot,
+                                          const float *q_sketch, float softmax_scale, float *scores,
+                                          float *out, void *stream);
 
 /* ------------------------------------------------------- measurement helper */
 

@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("AQKV_LIB", os.path.join(_HERE, "libaqkv.so"))
 STATUS = {
     0: "AQKV_OK", -1: "AQKV_ERR_NULL", -2: "AQKV_ERR_SHAPE", -3: "AQKV_ERR_ALIGN",
     -4: "AQKV_ERR_CAPACITY", -5: "AQKV_ERR_WORKSPACE", -6: "AQKV_ERR_DTYPE",
-    -7: "AQKV_ERR_HIP", -8: "AQKV_ERR_UNSUPPORTED",
+    -7: "AQKV_ERR_HIP", -8: "AQKV_ERR_UNSUPPORTED", -9: "AQKV_ERR_SCRATCH",
 }
 FP32, BF16 = 0, 1
 
@@ -104,6 +104,10 @@ _SIGS = {
                                                _P(KvView), _P(KvView), C.c_float, C.c_void_p, C.c_void_p,
                                                C.c_void_p, C.c_size_t, C.c_void_p]),
     "aqkv_read_stream": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
+    "aqkv_decode_static_scratch_bytes": (C.c_size_t, []),
+    "aqkv_decode_attention_noalloc": (C.c_int, [_P(Config), _P(LayerParams), _P(CacheDesc), C.c_int32, C.c_int32,
+                                                C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_float,
+                                                C.c_void_p, C.c_void_p, C.c_void_p]),
 }
 
 _lib_handle = None
@@ -378,6 +382,24 @@ def decode_attention(cfg: Config, layer: Layer, cache: Cache, batch: int, n_q_he
                                      C.c_float(softmax_scale), _ptr(scores), _ptr(out), _ptr(workspace),
                                      workspace.numel(), _stream(stream))
     _check(st, "aqkv_decode_attention")
+    return out
+
+
+def decode_static_scratch_bytes() -> int:
+    return int(lib().aqkv_decode_static_scratch_bytes())
+
+
+def decode_attention_noalloc(cfg: Config, layer: Layer, cache: Cache, batch: int, n_q_heads: int, n_kv_heads: int,
+                             context_len: int, q_rot, q_sketch, out, softmax_scale: Optional[float] = None,
+                             scores=None, stream=None):
+    """decode_attention with the library's static scratch instead of a workspace; `out` must be given
+    (nothing is allocated on this path)."""
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(np.sqrt(cfg.head_dim))
+    st = lib().aqkv_decode_attention_noalloc(C.byref(cfg), C.byref(layer.desc()), C.byref(cache.desc()), batch,
+                                             n_q_heads, n_kv_heads, context_len, _ptr(q_rot), _ptr(q_sketch),
+                                             C.c_float(softmax_scale), _ptr(scores), _ptr(out), _stream(stream))
+    _check(st, "aqkv_decode_attention_noalloc")
     return out
 
 

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 
@@ -109,6 +110,7 @@ const char *aqkv_status_string(aqkv_status s) {
     case AQKV_ERR_DTYPE: return "unknown element type";
     case AQKV_ERR_HIP: return "HIP runtime error";
     case AQKV_ERR_UNSUPPORTED: return "not supported by the library";
+    case AQKV_ERR_SCRATCH: return "request needs more than the library's static scratch";
   }
   return "unknown status";
 }
@@ -300,6 +302,34 @@ aqkv_status aqkv_prepare_query(const aqkv_config *cfg, const aqkv_layer *layer, 
   return hip_status(launch_prepare_query(job, static_cast<hipStream_t>(stream)));
 }
 
+// Static device scratch of the allocation-free decode: the split partials live
+// here instead of in a caller workspace.  Each device holds its own copy for
+// the life of the process; host code reaches it only through the address
+// hipGetSymbolAddress reports for the device (the array's name is a host-side
+// stand-in, not a device address).
+constexpr size_t kStaticScratchBytes = size_t{8} << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices];   // per device, set once under scratch_mutex
+
+// This device's copy of the scratch (nullptr on a HIP error); resolved once per
+// device, with that device current (it is the caller's current device).
+void *device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
 // The recent-token window of a decode call (all pointers already checked)
 struct WindowArgs {
   const float *q;
@@ -309,7 +339,8 @@ struct WindowArgs {
 static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache, int32_t batch,
                           int32_t n_q_heads, int32_t n_kv_heads, int64_t context_len, const float *q_rot,
                           const float *q_sketch, float softmax_scale, float *scores, float *out, void *workspace,
-                          size_t workspace_bytes, void *stream, const WindowArgs *win, bool scores_only = false) {
+                          size_t workspace_bytes, void *stream, const WindowArgs *win, bool scores_only = false,
+                          void *(*static_scratch)() = nullptr) {
   aqkv_status st = check_config(cfg);
   if (st != AQKV_OK) return st;
   if (!layer) return AQKV_ERR_NULL;
@@ -342,6 +373,14 @@ static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const
     return AQKV_ERR_ALIGN;
   if (context_len > 0 && (st = check_blocks(cache)) != AQKV_OK) return st;
   const DecodePlan plan = decode_plan(d, w, m, cfg->value_bits, cache->n_slots, g, context_len);
+  if (static_scratch) {
+    // the allocation-free call: the partials go to the library's static scratch (looked up
+    // only after every host-side check has passed)
+    if (plan.total_bytes > kStaticScratchBytes) return AQKV_ERR_SCRATCH;
+    workspace = static_scratch();
+    workspace_bytes = kStaticScratchBytes;
+    if (!workspace) return AQKV_ERR_HIP;
+  }
   if (!workspace || workspace_bytes < plan.total_bytes) return AQKV_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return AQKV_ERR_ALIGN;
 
@@ -552,6 +591,16 @@ aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer 
   cj.part_ml = tj.part_ml;
   cj.out = out;
   return hip_status(launch_combine(cj, s));
+}
+
+size_t aqkv_decode_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+aqkv_status aqkv_decode_attention_noalloc(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache,
+                                          int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t context_len,
+                                          const float *q_rot, const float *q_sketch, float softmax_scale,
+                                          float *scores, float *out, void *stream) {
+  return decode(cfg, layer, cache, batch, n_q_heads, n_kv_heads, context_len, q_rot, q_sketch, softmax_scale,
+                scores, out, nullptr, 0, stream, nullptr, false, device_scratch);
 }
 
 aqkv_status aqkv_decode_attention_window(const aqkv_config *cfg, const aqkv_layer *layer,

@@ -265,3 +265,26 @@ def test_decode_topk_validation_codes():
     cache = _cache(cap=big)
     assert lib.aqkv_decode_attention_topk(C.byref(cfg), C.byref(layer), C.byref(cache), 1, 4, 2, big, FAKE, FAKE,
                                           FAKE, 16, C.c_float(0.1), None, FAKE, FAKE, need, None) == -8
+
+
+def test_noalloc_decode_validation_codes():
+    # the allocation-free decode checks its sizes against the static scratch before any HIP call
+    lib = aqkv.lib()
+    cfg = aqkv.config(128, 2, 128)
+    layer = aqkv.LayerParams(FAKE, FAKE, FAKE, FAKE)
+    assert lib.aqkv_decode_static_scratch_bytes() == 8 << 20
+    big = aqkv.CacheDesc(FAKE, 4096 * 8, 4096)
+    assert lib.aqkv_decode_attention_noalloc(C.byref(cfg), C.byref(layer), C.byref(big), 4096, 64, 8, 4096, FAKE,
+                                             FAKE, C.c_float(0.1), None, FAKE, None) == -9
+    assert lib.aqkv_status_string(-9) == b"request needs more than the library's static scratch"
+
+    def call(b=1, hq=4, hkv=2, T=64, scale=0.1, out=FAKE):
+        return lib.aqkv_decode_attention_noalloc(C.byref(cfg), C.byref(layer), C.byref(_cache()), b, hq, hkv, T,
+                                                 FAKE, FAKE, C.c_float(scale), None, out, None)
+
+    assert call(hq=5) == -2
+    assert call(b=2) == -2
+    assert call(T=65) == -4
+    assert call(scale=0.0) == -2
+    assert call(out=None) == -1
+    assert call(b=0, hkv=2) == -2                       # zero batch against a two-slot cache
