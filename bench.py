@@ -50,7 +50,7 @@ ARITHMETIC = ("keys: f16 hi/lo split products on matrix cores, fp32 accumulate (
 KERNEL_SOURCES = {
     "decode": ["decode_fast.h", "decode_launch.hip", "decode_fast_d64.hip", "decode_fast_d128.hip",
                "decode_fast_d256.hip", "decode.hip"],
-    "quantize_keys": ["quant_keys_mfma.hip"],
+    "quantize_keys": ["quant_keys_mfma.hip", "quant_keys_qjl.hip"],
     "quantize_values": ["quant_values.hip"],
     "prepare_query": ["query.hip"],
 }

@@ -65,8 +65,10 @@ BlockLayout layout_of(const aqkv_config *cfg) {
 aqkv_status hip_status(hipError_t e) { return e == hipSuccess ? AQKV_OK : AQKV_ERR_HIP; }
 
 size_t key_workspace_bytes(int d, int w, int m) {
-  // matrix-core operands of Pi and S Pi^T (w > 0) or S (w == 0), f16 hi + lo
-  return aqkv::key_operand_header(d, w, m) + 256;   // the operands, then the rotation-scale float
+  // matrix-core operands of Pi and S Pi^T (w > 0) or S (w == 0), f16 hi + lo; then the
+  // rotation-scale float (256 bytes); then, for pure-QJL shapes, the sketch in the layout
+  // of the register-resident QJL kernel
+  return aqkv::key_operand_header(d, w, m) + 256 + (aqkv::qjl_shape(d, w, m) ? aqkv::qjl_operand_bytes(m) : 0);
 }
 
 }  // namespace

@@ -158,6 +158,14 @@ size_t key_operand_header(int d, int w, int m);
 hipError_t launch_key_operands(const float *rotation, const float *sketch, uint8_t *ops, int d, int w, int m,
                                hipStream_t stream);
 hipError_t launch_quantize_keys_mfma(const KeyJob &job, hipStream_t stream);
+// pure-QJL bf16 keys at d = 128 with the sketch resident in registers (quant_keys_qjl.hip);
+// its operands (qjl_operand_bytes(m), from launch_qjl_operands) follow the 256-byte
+// rotation-scale header of the prepared workspace for the shapes qjl_shape accepts
+bool qjl_shape(int d, int w, int m);
+size_t qjl_operand_bytes(int m);
+hipError_t launch_qjl_operands(const float *sketch, uint8_t *ops, int m, hipStream_t stream);
+bool quantize_keys_qjl_supported(const KeyJob &job);
+hipError_t launch_quantize_keys_qjl(const KeyJob &job, hipStream_t stream);
 hipError_t launch_quantize_values(const ValueJob &job, hipStream_t stream);
 hipError_t launch_prepare_query(const QueryJob &job, hipStream_t stream);
 hipError_t launch_decode(const DecodeJob &job, hipStream_t stream);

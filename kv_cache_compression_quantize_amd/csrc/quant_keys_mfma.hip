@@ -999,10 +999,13 @@ hipError_t launch_key_operands(const float *rotation, const float *sketch, uint8
   const int64_t total = static_cast<int64_t>(key_operand_bytes(d, w, m) / 4);   // one thread per f16 pair
   key_operands_kernel<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(rotation, sketch, ops, d, w,
                                                                                       m, scale);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || !qjl_shape(d, w, m)) return e;
+  return launch_qjl_operands(sketch, ops + key_operand_header(d, w, m) + 256, m, stream);
 }
 
 hipError_t launch_quantize_keys_mfma(const KeyJob &job, hipStream_t stream) {
+  if (quantize_keys_qjl_supported(job)) return launch_quantize_keys_qjl(job, stream);
   switch (job.d) {
     case 64: return launch_d<64>(job, stream);
     case 128: return launch_d<128>(job, stream);

@@ -66,10 +66,14 @@ def test_workspace_sizes():
     cfg = aqkv.config(128, 2, 128)
     # ready-made matrix-core operands: one 16-row slab per tile of Pi (w > 0) and
     # of the sketch, (d / 32) k-steps x (hi, lo) x 1 KiB each
-    for d, w, m in [(128, 2, 128), (128, 0, 256), (256, 3, 256), (64, 1, 64), (128, 0, 192)]:
+    for d, w, m in [(128, 2, 128), (128, 0, 256), (256, 3, 256), (64, 1, 64), (128, 0, 192), (128, 0, 384),
+                    (128, 0, 512)]:
         slabs = (d // 16 if w > 0 else 0) + m // 16
-        # the operands, then a 256-byte header (the rotation's common magnitude)
-        assert aqkv.quantize_keys_workspace_bytes(aqkv.config(d, w, m)) == slabs * (d // 32) * 2048 + 256
+        # the operands, then a 256-byte header (the rotation's common magnitude), then for pure-QJL
+        # shapes at d = 128 with 320 <= m <= 512 the sketch again in the register-resident kernel's
+        # layout (m / 32 tiles x 8 k-steps x hi/lo x 1 KiB)
+        qjl = m * 512 if (d == 128 and w == 0 and 320 <= m <= 512) else 0
+        assert aqkv.quantize_keys_workspace_bytes(aqkv.config(d, w, m)) == slabs * (d // 32) * 2048 + 256 + qjl
     ws = aqkv.decode_workspace_bytes(cfg, 8, 32, 8, 131072)
     assert ws > 0 and ws % 256 == 0
     assert aqkv.decode_workspace_bytes(cfg, 1, 32, 5, 100) == 0   # Hq % Hkv != 0
