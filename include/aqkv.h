@@ -50,19 +50,29 @@
  *              p of every coordinate's index.  (absent when w == 0.)
  *   key_signs  m / 8 bytes per row: one bit row, bit 1 = non-negative
  *              projection.
- *   key_norm   fp32 ||x|| per row.
- *   key_rnorm  fp32 ||r|| per row (absent when w == 0).
+ *   key_norm   ||x|| per row: fp32, or IEEE half when side_f16 is set.
+ *   key_rnorm  ||r|| per row (absent when w == 0): fp32, or half as key_norm.
  *   val_codes  d * value_bits / 8 bytes per row; the 32 rows of a record are
  *              one code block in which channel 32 g + 16 h + n (group g, half
  *              h, column n) of token 4 i + r (r in 0..3, i in 0..7) is at
  *                value_bits 2: word (16 g + n) * 4 + r, bits 8 h + 16 (i & 1) + 2 (i >> 1);
  *                value_bits 4: word ((16 g + n) * 4 + r) * 2 + h, bits 16 (i & 1) + 4 (i >> 1).
- *   val_side   fp32 scale and min of every value group, 8 * d / value_group
- *              bytes per row, stored group-major in the record so that one
- *              16-byte read returns what a decoder lane needs: the scale (j =
- *              0) and min (j = 1) of group g for token t = 8 a + 4 h + b (b in
- *              0..3, h in 0..1) is float ((g * 16 + 4 a + b) * 2 + h) * 2 + j of
+ *   val_side   scale and min of every value group, 2 * e * d / value_group
+ *              bytes per row (e = 4 for fp32, 2 for half when side_f16 is
+ *              set), stored group-major in the record so that one 4e-byte
+ *              read returns what a decoder lane needs: the scale (j = 0) and
+ *              min (j = 1) of group g for token t = 8 a + 4 h + b (b in 0..3,
+ *              h in 0..1) is element ((g * 16 + 4 a + b) * 2 + h) * 2 + j of
  *              the field.
+ * Side information in half precision (side_f16 = 1; the bytes-for-precision
+ * knob beside the TurboQuant article's head_dim 256 compression figure, §一
+ * Paper Validation table): every code (index, sign, value code) is decided
+ * exactly as with fp32 side information; only the stored n, gamma, scale and
+ * min are rounded, from their fp32 values, to the nearest half (ties to even),
+ * finite values beyond the half range saturating to +-65504, and every
+ * decoder reads back those halves.  At d = 256, 3-bit keys and 2-bit values a
+ * row then takes 196 bytes instead of 232 (5.22x against bf16 K and V rather
+ * than 4.41x).
  * The cache buffer must be 16-byte aligned (every block_bytes is a multiple
  * of 16).
  */
@@ -98,6 +108,7 @@ typedef struct {
   int32_t sketch_dim;  /* m: QJL sketch rows, multiple of 64, 64..1024 (m = d for TurboQuant keys) */
   int32_t value_bits;  /* 2 or 4 */
   int32_t value_group; /* channels per value group: 32 */
+  int32_t side_f16;    /* 0: n, gamma, value scale and min stored as fp32; 1: as IEEE half */
 } aqkv_config;
 
 /* Per-layer parameters (TurboQuant §二: Pi from a QR decomposition and S
@@ -146,7 +157,7 @@ const char *aqkv_status_string(aqkv_status status);
 
 /* Checks a configuration and reports the block-record geometry (out may be
  * NULL to only validate).  AQKV_ERR_SHAPE for unsupported head_dim /
- * mse_bits / sketch_dim / value_bits / value_group.  A cache of n_slots x
+ * mse_bits / sketch_dim / value_bits / value_group / side_f16 (0 or 1).  A cache of n_slots x
  * capacity tokens takes n_slots * capacity / 32 * block_bytes bytes. */
 aqkv_status aqkv_cache_layout(const aqkv_config *cfg, aqkv_layout *out);
 

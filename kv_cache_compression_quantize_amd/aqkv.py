@@ -33,7 +33,7 @@ class AqkvError(RuntimeError):
 
 class Config(C.Structure):
     _fields_ = [("head_dim", C.c_int32), ("mse_bits", C.c_int32), ("sketch_dim", C.c_int32),
-                ("value_bits", C.c_int32), ("value_group", C.c_int32)]
+                ("value_bits", C.c_int32), ("value_group", C.c_int32), ("side_f16", C.c_int32)]
 
 
 class LayerParams(C.Structure):
@@ -56,7 +56,7 @@ FLOAT_FIELDS = ("key_norm", "key_rnorm", "val_side")
 
 
 def side_index(groups: int) -> np.ndarray:
-    """[32 tokens, groups, 2] -> float index inside a record's val_side field
+    """[32 tokens, groups, 2] -> element index (fp32 or half) inside a record's val_side field
     (j = 0 scale, 1 min; include/aqkv.h): ((g * 16 + 4 a + b) * 2 + h) * 2 + j for
     token t = 8 a + 4 h + b."""
     t = np.arange(32)[:, None, None]
@@ -162,8 +162,9 @@ def _dtype_code(t) -> int:
 
 # ----------------------------------------------------------------- host only
 
-def config(head_dim: int, mse_bits: int, sketch_dim: int, value_bits: int = 2, value_group: int = 32) -> Config:
-    return Config(head_dim, mse_bits, sketch_dim, value_bits, value_group)
+def config(head_dim: int, mse_bits: int, sketch_dim: int, value_bits: int = 2, value_group: int = 32,
+           side_f16: bool = False) -> Config:
+    return Config(head_dim, mse_bits, sketch_dim, value_bits, value_group, int(bool(side_f16)))
 
 
 def cache_layout(cfg: Config) -> dict:
@@ -245,20 +246,22 @@ class Cache:
         return Cache(cfg, n_slots, capacity, blocks, lo)
 
     def field(self, name: str):
-        """Strided view [records, 32, row] of one field (uint8, or float32 for the norms,
-        scales and minima); None when the configuration has no such field."""
+        """Strided view [records, 32, row] of one field (uint8, or float32 / float16 for the
+        norms, scales and minima); None when the configuration has no such field."""
+        import torch
         rb, off, bb = self.layout["row"][name], self.layout["offset"][name], self.layout["block_bytes"]
         if rb == 0:
             return None
         n_rec = self.blocks.shape[0]
         if name in FLOAT_FIELDS:
-            f = self.blocks.view(-1).view(dtype=__import__("torch").float32)
-            return f.as_strided((n_rec, 32, rb // 4), (bb // 4, rb // 4, 1), off // 4)
+            e = 2 if self.cfg.side_f16 else 4
+            f = self.blocks.view(-1).view(dtype=torch.float16 if e == 2 else torch.float32)
+            return f.as_strided((n_rec, 32, rb // e), (bb // e, rb // e, 1), off // e)
         return self.blocks.view(-1).as_strided((n_rec, 32, rb), (bb, rb, 1), off)
 
     def rows(self, name: str, row0: int, n: int):
         """Copy of cache rows row0 .. row0 + n - 1 (row = slot * capacity + token) of a field:
-        [n, row] (uint8 or float32), [n] for the single-float norms."""
+        [n, row] (uint8, float32 or float16), [n] for the single-number norms."""
         f = self.field(name)
         if f is None:
             return None
@@ -277,7 +280,8 @@ class Cache:
             r += k
 
     def value_side(self, row0: int, n: int):
-        """(scale, min) of cache rows row0 .. row0 + n - 1, each [n, groups] float32, in token order."""
+        """(scale, min) of cache rows row0 .. row0 + n - 1, each [n, groups] in the stored
+        type (float32, or float16 for half side information), in token order."""
         import torch
         groups = self.cfg.head_dim // self.cfg.value_group
         f = self.field("val_side").flatten(1)                       # [records, 32 * groups * 2]

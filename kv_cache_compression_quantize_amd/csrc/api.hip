@@ -25,6 +25,7 @@ aqkv_status check_config(const aqkv_config *cfg) {
   if (m < 64 || m > kMaxSketch || m % 64 != 0) return AQKV_ERR_SHAPE;
   if (cfg->value_bits != 2 && cfg->value_bits != 4) return AQKV_ERR_SHAPE;
   if (cfg->value_group != 32) return AQKV_ERR_SHAPE;
+  if (cfg->side_f16 != 0 && cfg->side_f16 != 1) return AQKV_ERR_SHAPE;
   return AQKV_OK;
 }
 
@@ -59,7 +60,7 @@ aqkv_status check_blocks(const aqkv_cache *c) {
 }
 
 BlockLayout layout_of(const aqkv_config *cfg) {
-  return block_layout(cfg->head_dim, cfg->mse_bits, cfg->sketch_dim, cfg->value_bits);
+  return block_layout(cfg->head_dim, cfg->mse_bits, cfg->sketch_dim, cfg->value_bits, cfg->side_f16 != 0);
 }
 
 aqkv_status hip_status(hipError_t e) { return e == hipSuccess ? AQKV_OK : AQKV_ERR_HIP; }
@@ -75,14 +76,14 @@ size_t key_workspace_bytes(int d, int w, int m) {
 
 namespace aqkv {
 
-DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int64_t context) {
+DecodePlan decode_plan(int d, int w, int m, int vb, bool sf, int64_t n_slots, int g, int64_t context) {
   constexpr int64_t kGrain = 256;      // split granularity (tokens)
   constexpr int64_t kCUs = 256;        // MI355X compute units
   DecodePlan p{};
-  p.mfma = decode_mfma_supported(d, w, g, m, vb);
+  p.mfma = decode_mfma_supported(d, w, g, m, vb, sf);
   // one round of resident blocks for the matrix-core kernel (each block pays its
   // query-side prologue once), ~4 per CU otherwise
-  const int64_t target = p.mfma ? kCUs * decode_mfma_blocks_per_cu(d, w, g, m, vb) : 4 * kCUs;
+  const int64_t target = p.mfma ? kCUs * decode_mfma_blocks_per_cu(d, w, g, m, vb, sf) : 4 * kCUs;
   const int64_t grains = (context + kGrain - 1) / kGrain;
   int64_t split = n_slots > 0 ? (target + n_slots - 1) / n_slots : 1;
   if (split > grains) split = grains;
@@ -150,7 +151,7 @@ size_t aqkv_decode_workspace_bytes(const aqkv_config *cfg, int32_t batch, int32_
   if (check_config(cfg) != AQKV_OK) return 0;
   if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads || context_len < 0) return 0;
   const int64_t n_slots = static_cast<int64_t>(batch) * n_kv_heads;
-  return decode_plan(cfg->head_dim, cfg->mse_bits, cfg->sketch_dim, cfg->value_bits, n_slots,
+  return decode_plan(cfg->head_dim, cfg->mse_bits, cfg->sketch_dim, cfg->value_bits, cfg->side_f16 != 0, n_slots,
                      n_q_heads / n_kv_heads, context_len)
       .total_bytes;
 }
@@ -218,6 +219,7 @@ static aqkv_status quantize_keys(const aqkv_config *cfg, const aqkv_layer *layer
   job.d = d;
   job.w = w;
   job.m = m;
+  job.sf = cfg->side_f16;
   job.ops = ops;
   job.rot_scale = reinterpret_cast<const float *>(ops + key_operand_header(d, w, m));
   job.centroids = layer->centroids;
@@ -270,6 +272,7 @@ aqkv_status aqkv_quantize_values(const aqkv_config *cfg, const aqkv_kv_view *v, 
   job.d = d;
   job.vb = cfg->value_bits;
   job.group = cfg->value_group;
+  job.sf = cfg->side_f16;
   const BlockLayout L = layout_of(cfg);
   job.codes = cache->blocks + L.off[F_VCODES];
   job.side = cache->blocks + L.off[F_VSIDE];
@@ -355,7 +358,8 @@ static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const
   if (context_len > cache->capacity) return AQKV_ERR_CAPACITY;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return AQKV_ERR_SHAPE;
   const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
-  if (!decode_supported(d, w, g, m, cfg->value_bits) && !decode_mfma_supported(d, w, g, m, cfg->value_bits))
+  if (!decode_supported(d, w, g, m, cfg->value_bits) &&
+      !decode_mfma_supported(d, w, g, m, cfg->value_bits, cfg->side_f16 != 0))
     return AQKV_ERR_UNSUPPORTED;
   if (win) {
     if (!win->k || !win->v) return AQKV_ERR_NULL;
@@ -374,7 +378,7 @@ static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const
       (scores && !aligned(scores, 16)) || (win && !aligned(win->q, 16)))
     return AQKV_ERR_ALIGN;
   if (context_len > 0 && (st = check_blocks(cache)) != AQKV_OK) return st;
-  const DecodePlan plan = decode_plan(d, w, m, cfg->value_bits, cache->n_slots, g, context_len);
+  const DecodePlan plan = decode_plan(d, w, m, cfg->value_bits, cfg->side_f16 != 0, cache->n_slots, g, context_len);
   if (static_scratch) {
     // the allocation-free call: the partials go to the library's static scratch (looked up
     // only after every host-side check has passed)
@@ -392,6 +396,7 @@ static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const
   job.m = m;
   job.vb = cfg->value_bits;
   job.group = cfg->value_group;
+  job.sf = cfg->side_f16;
   job.n_slots = cache->n_slots;
   job.capacity = cache->capacity;
   job.context = context_len;
@@ -478,7 +483,8 @@ static TopkLayout topk_layout(const aqkv_config *cfg, int64_t n_slots, int g, in
   L.qsel_sk = take(sizeof(float) * n_slots * m);
   L.scores = take(sizeof(float) * n_slots * context);
   L.dec_out = take(sizeof(float) * n_slots * d);
-  L.dec_ws_bytes = decode_plan(d, cfg->mse_bits, m, cfg->value_bits, n_slots, 1, context).total_bytes;
+  L.dec_ws_bytes =
+      decode_plan(d, cfg->mse_bits, m, cfg->value_bits, cfg->side_f16 != 0, n_slots, 1, context).total_bytes;
   L.dec_ws = take(L.dec_ws_bytes);
   L.sel = take(sizeof(int32_t) * n_slots * budget);
   const int chunks = topk_chunks(budget);
@@ -517,7 +523,8 @@ aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer 
   if (context_len > cache->capacity) return AQKV_ERR_CAPACITY;
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return AQKV_ERR_SHAPE;
   const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
-  if (!decode_supported(d, w, 1, m, cfg->value_bits) && !decode_mfma_supported(d, w, 1, m, cfg->value_bits))
+  if (!decode_supported(d, w, 1, m, cfg->value_bits) &&
+      !decode_mfma_supported(d, w, 1, m, cfg->value_bits, cfg->side_f16 != 0))
     return AQKV_ERR_UNSUPPORTED;
   if (batch == 0) return AQKV_OK;
   if (!out || !q || !q_sketch || !layer->sketch) return AQKV_ERR_NULL;
@@ -563,6 +570,7 @@ aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer 
   tj.w = w;
   tj.m = m;
   tj.vb = cfg->value_bits;
+  tj.sf = cfg->side_f16;
   tj.g = g;
   tj.n_slots = cache->n_slots;
   tj.capacity = cache->capacity;

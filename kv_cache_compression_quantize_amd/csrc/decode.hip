@@ -77,10 +77,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
     const bool block_valid = c0 + (tid & ~31) < t_end;
     for (int i = 0; i < vwords; ++i)
       vcw[tid * vwords + i] = block_valid ? reinterpret_cast<const uint32_t *>(job.vcodes + rec_row(row, D * vb / 8, job.rec))[i] : 0u;
+    const bool sf = job.sf != 0;   // half side information (else fp32)
     for (int i = 0; i < kGroups; ++i) {
-      const float *side = reinterpret_cast<const float *>(job.vside + rec_row(row & ~int64_t(31), 0, job.rec));
-      vsc[tid * kGroups + i] = valid ? side[side_index(i, static_cast<int>(row & 31), 0)] : 0.0f;
-      vmn[tid * kGroups + i] = valid ? side[side_index(i, static_cast<int>(row & 31), 1)] : 0.0f;
+      const uint8_t *side = job.vside + rec_row(row & ~int64_t(31), 0, job.rec);
+      vsc[tid * kGroups + i] = valid ? load_side(side, side_index(i, static_cast<int>(row & 31), 0), sf) : 0.0f;
+      vmn[tid * kGroups + i] = valid ? load_side(side, side_index(i, static_cast<int>(row & 31), 1), sf) : 0.0f;
     }
 
     // A. scores
@@ -88,8 +89,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
 #pragma unroll
     for (int g = 0; g < G; ++g) s_acc[g] = 0.0f;
     if (valid) {
-      const float n = *reinterpret_cast<const float *>(job.norm + rec_row(row, 4, job.rec));
-      const float gamma = W > 0 ? *reinterpret_cast<const float *>(job.rnorm + rec_row(row, 4, job.rec)) : n;
+      const int64_t rb = rec_row(row & ~int64_t(31), 0, job.rec), ri = row & 31;
+      const float n = load_side(job.norm + rb, ri, sf);
+      const float gamma = W > 0 ? load_side(job.rnorm + rb, ri, sf) : n;
       float mse[G], qjl[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) { mse[g] = 0.0f; qjl[g] = 0.0f; }

@@ -79,6 +79,14 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // v_mul_legacy_f32: 0 * x = 0 for every x (Inf and NaN included)
 __device__ float fmul_legacy(float a, float b) __asm("llvm.amdgcn.fmul.legacy");
 
+// the low / high IEEE half of a 32-bit word, widened to fp32
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
 // Bit-row words hold element j = 4 i + k at bit 8 k + i, so (x >> i) & 0x01010101
 // is elements 4i .. 4i+3 as int8 {0,1} bytes.  Half hf of a word (elements
 // 16 hf .. 16 hf + 15) -> the 16 operand bytes of one K-chunk.
@@ -149,26 +157,28 @@ __host__ __device__ constexpr int pairs_of(int g, int d) { return (g * (d / 32) 
 // ring of kRing buffers (tiles t+1 .. t+kRing-1 stream in while t is computed;
 // two buffers and more resident waves beat deeper prefetch with fewer waves).
 constexpr int kRing = 2;
-__host__ __device__ constexpr int tile_bytes_of(int d, int w, int mc, int vb) {
-  return kTT * (w * d / 8 + mc * 8 + 4 + (w > 0 ? 4 : 0) + d * vb / 8 + 8 * (d / 32));   // = record bytes
+// (sf: side information stored as half, 2 bytes a number instead of 4)
+__host__ __device__ constexpr int tile_bytes_of(int d, int w, int mc, int vb, bool sf) {
+  const int e = sf ? 2 : 4;
+  return kTT * (w * d / 8 + mc * 8 + e + (w > 0 ? e : 0) + d * vb / 8 + 2 * e * (d / 32));   // = record bytes
 }
-// LDS bytes per block of decode_fast_kernel<D, W, m / 64, G, VB> (host and device):
+// LDS bytes per block of decode_fast_kernel<D, W, m / 64, G, VB, SF> (host and device):
 // per wave the tile ring and the value-weight operand [groups][4][2G + 1 rows][16 B],
 // whose first bytes also hold the softmax weights P [32 tokens][G] until they are
 // read; at the end the 4-wave merge
 __host__ __device__ constexpr int aval_rows_of(int g) { return 2 * g + 1; }   // + 1 row: writes spread over all banks
-__host__ __device__ constexpr int wave_lds_of(int d, int w, int mc, int g, int vb) {
-  return kRing * tile_bytes_of(d, w, mc, vb) + (d / 32) * 4 * aval_rows_of(g) * 16;
+__host__ __device__ constexpr int wave_lds_of(int d, int w, int mc, int g, int vb, bool sf) {
+  return kRing * tile_bytes_of(d, w, mc, vb, sf) + (d / 32) * 4 * aval_rows_of(g) * 16;
 }
-__host__ __device__ constexpr int smem_of(int d, int w, int mc, int g, int vb) {
-  const int waves = kWaves * wave_lds_of(d, w, mc, g, vb);
+__host__ __device__ constexpr int smem_of(int d, int w, int mc, int g, int vb, bool sf) {
+  const int waves = kWaves * wave_lds_of(d, w, mc, g, vb, sf);
   const int merge = kWaves * (g * d + 2 * g + g * (d / 32)) * 4;
   const int nc_all = chunks_max(d, w, 64 * mc);
   const int qa = heads_rb(g) * nc_all * 4 <= kRegAVgprs ? 0 : heads_rb(g) * nc_all * 1024;
   return qa + (waves > merge ? waves : merge);
 }
 
-template <int D, int W, int MC, int G, int VB>
+template <int D, int W, int MC, int G, int VB, bool SF>
 struct Geo {
   static constexpr int RB = heads_rb(G);
   static constexpr int HC = D / 64;                  // K-chunks per code plane
@@ -181,14 +191,15 @@ struct Geo {
   static constexpr int kSw = (MC + 1) / 2;               // sign words per lane per token
   static constexpr int kPairs = pairs_of(G, D);
   static constexpr int kLG = kGroups >= 4 ? kGroups / 4 : 1;   // value groups one lane reads per tile
+  static constexpr int E = SF ? 2 : 4;                  // bytes per side-information number
   static constexpr int o_signs = kTT * CB;
   static constexpr int o_norm = o_signs + kTT * SB;
-  static constexpr int o_rnorm = o_norm + kTT * 4;
-  static constexpr int o_vcodes = o_rnorm + (W > 0 ? kTT * 4 : 0);
+  static constexpr int o_rnorm = o_norm + kTT * E;
+  static constexpr int o_vcodes = o_rnorm + (W > 0 ? kTT * E : 0);
   static constexpr int o_vside = o_vcodes + kTT * VBY;
-  static constexpr int tile_bytes = o_vside + kTT * kGroups * 8;
-  static_assert(tile_bytes == tile_bytes_of(D, W, MC, VB), "tile geometry");
-  static constexpr int wave_lds = wave_lds_of(D, W, MC, G, VB);
+  static constexpr int tile_bytes = o_vside + kTT * kGroups * 2 * E;
+  static_assert(tile_bytes == tile_bytes_of(D, W, MC, VB, SF), "tile geometry");
+  static constexpr int wave_lds = wave_lds_of(D, W, MC, G, VB, SF);
   static constexpr int AR = aval_rows_of(G);        // 16-byte rows per (group, lane group) block
   static constexpr int aval_bytes = kGroups * 4 * AR * 16;
   // load instructions per tile (each wave waits on whole tiles)
@@ -196,7 +207,7 @@ struct Geo {
   static constexpr int nc_all = chunks_max(D, W, 64 * MC);
   static constexpr bool reg_a_all = RB * nc_all * 4 <= kRegAVgprs;
   static constexpr int qa_lds_bytes = reg_a_all ? 0 : RB * nc_all * 1024;
-  static constexpr int smem = smem_of(D, W, MC, G, VB);
+  static constexpr int smem = smem_of(D, W, MC, G, VB, SF);
 };
 
 // Query side of the slot's G heads, built by the whole block once (the
@@ -286,10 +297,10 @@ __device__ __forceinline__ void pack_query(const DecodeJob &job, int64_t head0, 
   __syncthreads();
 }
 
-template <int D, int W, int MC, int G, int VB, int PL>
+template <int D, int W, int MC, int G, int VB, bool SF, int PL>
 __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, int split, uint8_t *smem,
                                             const float *kappa) {
-  using Gm = Geo<D, W, MC, G, VB>;
+  using Gm = Geo<D, W, MC, G, VB, SF>;
   constexpr int RB = Gm::RB, HC = Gm::HC, kGroups = Gm::kGroups, CB = Gm::CB, SB = Gm::SB, VBY = Gm::VBY;
   constexpr int kWpl = Gm::kWpl, kSw = Gm::kSw, kPairs = Gm::kPairs, kLG = Gm::kLG;
   constexpr int NP = popc(PL);
@@ -482,8 +493,14 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const int tok = 16 * ct + n16;
-      const float nrm = reinterpret_cast<const float *>(tb + Gm::o_norm)[tok];
-      const float gam = W > 0 ? reinterpret_cast<const float *>(tb + Gm::o_rnorm)[tok] : nrm;
+      float nrm, gam;
+      if constexpr (SF) {
+        nrm = static_cast<float>(reinterpret_cast<const _Float16 *>(tb + Gm::o_norm)[tok]);
+        gam = W > 0 ? static_cast<float>(reinterpret_cast<const _Float16 *>(tb + Gm::o_rnorm)[tok]) : nrm;
+      } else {
+        nrm = reinterpret_cast<const float *>(tb + Gm::o_norm)[tok];
+        gam = W > 0 ? reinterpret_cast<const float *>(tb + Gm::o_rnorm)[tok] : nrm;
+      }
       const bool valid = tok < nt;
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
@@ -574,11 +591,19 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
     {
       const int qd = n16 & 3, i0 = 2 * (n16 >> 2);
       // {scale, min} of tokens ta and ta + 4 of group (q + 4u) % kGroups: one
-      // contiguous 16-byte read per lane (group-major val_side field)
+      // contiguous 16-byte (8-byte with half side information) read per lane
+      // (group-major val_side field)
       float4 side[kLG];
 #pragma unroll
-      for (int u = 0; u < kLG; ++u)
-        side[u] = reinterpret_cast<const float4 *>(tb + Gm::o_vside)[((q + 4 * u) % kGroups) * 16 + n16];
+      for (int u = 0; u < kLG; ++u) {
+        const int si = ((q + 4 * u) % kGroups) * 16 + n16;
+        if constexpr (SF) {
+          const uint2 hv = reinterpret_cast<const uint2 *>(tb + Gm::o_vside)[si];
+          side[u] = make_float4(half_lo(hv.x), half_hi(hv.x), half_lo(hv.y), half_hi(hv.y));
+        } else {
+          side[u] = reinterpret_cast<const float4 *>(tb + Gm::o_vside)[si];
+        }
+      }
       float pa[G], pb[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -720,7 +745,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
 // waves per SIMD the register allocation aims for (16 or 8 per CU)
 __host__ __device__ constexpr int waves_per_simd(int d, int g) { return (g >= 8 || d >= 256) ? 2 : 4; }
 
-template <int D, int W, int MC, int G, int VB>
+template <int D, int W, int MC, int G, int VB, bool SF>
 __global__ __launch_bounds__(kThreads, waves_per_simd(D, G)) void decode_fast_kernel(DecodeJob job) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float s_cen[8], s_kappa[8];
@@ -755,17 +780,17 @@ __global__ __launch_bounds__(kThreads, waves_per_simd(D, G)) void decode_fast_ke
 #pragma unroll
     for (int a = 1; a < L; ++a)
       if (!(popc(a) & 1) && s_kappa[a - 1] != 0.0f) odd = false;
-    if (odd) decode_body<D, W, MC, G, VB, odd_planes(W)>(job, slot, split, smem, s_kappa);
-    else decode_body<D, W, MC, G, VB, all_planes(W)>(job, slot, split, smem, s_kappa);
+    if (odd) decode_body<D, W, MC, G, VB, SF, odd_planes(W)>(job, slot, split, smem, s_kappa);
+    else decode_body<D, W, MC, G, VB, SF, all_planes(W)>(job, slot, split, smem, s_kappa);
   } else {
-    decode_body<D, W, MC, G, VB, all_planes(W)>(job, slot, split, smem, s_kappa);
+    decode_body<D, W, MC, G, VB, SF, all_planes(W)>(job, slot, split, smem, s_kappa);
   }
 }
 
-template <int D, int W, int MC, int G, int VB>
+template <int D, int W, int MC, int G, int VB, bool SF>
 hipError_t launch_fast(const DecodeJob &job, hipStream_t stream) {
-  using Gm = Geo<D, W, MC, G, VB>;
-  auto kern = decode_fast_kernel<D, W, MC, G, VB>;
+  using Gm = Geo<D, W, MC, G, VB, SF>;
+  auto kern = decode_fast_kernel<D, W, MC, G, VB, SF>;
   if (Gm::smem > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Gm::smem);
@@ -777,7 +802,8 @@ hipError_t launch_fast(const DecodeJob &job, hipStream_t stream) {
 
 template <int D, int W, int MC, int G>
 hipError_t launch_fast_g(const DecodeJob &job, hipStream_t stream) {
-  return job.vb == 2 ? launch_fast<D, W, MC, G, 2>(job, stream) : launch_fast<D, W, MC, G, 4>(job, stream);
+  if (job.sf) return job.vb == 2 ? launch_fast<D, W, MC, G, 2, true>(job, stream) : launch_fast<D, W, MC, G, 4, true>(job, stream);
+  return job.vb == 2 ? launch_fast<D, W, MC, G, 2, false>(job, stream) : launch_fast<D, W, MC, G, 4, false>(job, stream);
 }
 
 template <int D, int W, int MC>

@@ -22,15 +22,15 @@ bool fast_shape(int d, int w, int mc) {
 
 }  // namespace
 
-bool decode_mfma_supported(int d, int w, int g, int m, int vb) {
+bool decode_mfma_supported(int d, int w, int g, int m, int vb, bool sf) {
   if (g != 1 && g != 2 && g != 4 && g != 8) return false;
   if (vb != 2 && vb != 4) return false;
   if (m % 64 || !fast_shape(d, w, m / 64)) return false;
-  return fast::smem_of(d, w, m / 64, g, vb) <= 160 * 1024;
+  return fast::smem_of(d, w, m / 64, g, vb, sf) <= 160 * 1024;
 }
 
-int decode_mfma_blocks_per_cu(int d, int w, int g, int m, int vb) {
-  const int smem = fast::smem_of(d, w, m / 64, g, vb);
+int decode_mfma_blocks_per_cu(int d, int w, int g, int m, int vb, bool sf) {
+  const int smem = fast::smem_of(d, w, m / 64, g, vb, sf);
   int by_lds = (160 * 1024) / smem;
   const int by_regs = fast::waves_per_simd(d, g);   // blocks of 4 waves = waves per SIMD
   if (by_lds > by_regs) by_lds = by_regs;

@@ -21,14 +21,17 @@ struct BlockLayout {
   int64_t off[F_COUNT];
   int64_t rec;
 };
-inline BlockLayout block_layout(int d, int w, int m, int vb) {
+// sf: side information (norms, value scales and minima) stored as half
+// instead of fp32.
+inline BlockLayout block_layout(int d, int w, int m, int vb, bool sf) {
+  const int e = sf ? 2 : 4;   // bytes per side-information number
   BlockLayout L{};
   L.row[F_CODES] = static_cast<int64_t>(w) * d / 8;
   L.row[F_SIGNS] = m / 8;
-  L.row[F_NORM] = 4;
-  L.row[F_RNORM] = w > 0 ? 4 : 0;
+  L.row[F_NORM] = e;
+  L.row[F_RNORM] = w > 0 ? e : 0;
   L.row[F_VCODES] = static_cast<int64_t>(d) * vb / 8;
-  L.row[F_VSIDE] = 8 * (d / 32);
+  L.row[F_VSIDE] = 2 * e * (d / 32);
   int64_t o = 0;
   for (int f = 0; f < F_COUNT; ++f) {
     L.off[f] = o;
@@ -38,9 +41,10 @@ inline BlockLayout block_layout(int d, int w, int m, int vb) {
   return L;
 }
 
-// Float index, within a record's val_side field, of the scale (j = 0) or min
-// (j = 1) of value group g of the record's token t (0..31): group-major, tokens
-// t and t + 4 of a group side by side (include/aqkv.h).
+// Element index (fp32 or half), within a record's val_side field, of the
+// scale (j = 0) or min (j = 1) of value group g of the record's token t
+// (0..31): group-major, tokens t and t + 4 of a group side by side
+// (include/aqkv.h).
 __host__ __device__ inline int side_index(int g, int t, int j) {
   return ((g * 16 + 4 * (t >> 3) + (t & 3)) * 2 + ((t >> 2) & 1)) * 2 + j;
 }
@@ -59,6 +63,7 @@ struct KeyJob {
   int64_t batch_stride, head_stride, token_stride;  // elements
   int64_t n_slots, n_tokens, token_offset, capacity;
   int d, w, m;
+  int sf;                 // norms stored as half (else fp32)
   const uint8_t *ops;     // matrix-core operands of Pi and S Pi^T (or S), see quant_keys_mfma.hip
   const float *rot_scale; // a > 0 when every |Pi_ij| == a (then the Pi operands are +-1, exact); else 0
   const float *centroids, *boundaries;
@@ -74,6 +79,7 @@ struct ValueJob {
   int64_t batch_stride, head_stride, token_stride;
   int64_t n_slots, n_tokens, token_offset, capacity;
   int d, vb, group;
+  int sf;                 // scale and min stored as half (else fp32)
   // cache fields, each at its place in record 0; row r at + rec_row(r, row bytes, rec)
   uint8_t *codes, *side;
   int64_t rec;
@@ -90,6 +96,7 @@ struct QueryJob {
 
 struct DecodeJob {
   int d, w, m, vb, group;
+  int sf;                // side information stored as half (else fp32)
   int64_t n_slots, capacity, context;
   int g;                 // query heads per kv head
   int n_split;
@@ -130,6 +137,7 @@ constexpr int64_t kMaxBudget = int64_t{1} << 20;
 constexpr int64_t kMaxTopkContext = (int64_t{1} << 31) - (int64_t{1} << 20);
 struct TopkJob {
   int d, w, m, vb, g;
+  int sf;                          // side information stored as half (else fp32)
   int64_t n_slots, capacity, context, rec;
   const uint8_t *codes, *signs, *norm, *rnorm, *vcodes, *vside;   // fields at their place in record 0
   const float *centroids;
@@ -148,7 +156,7 @@ struct DecodePlan {
   int64_t split_tokens;
   size_t acc_bytes, ml_bytes, total_bytes;
 };
-DecodePlan decode_plan(int d, int w, int m, int vb, int64_t n_slots, int g, int64_t context);
+DecodePlan decode_plan(int d, int w, int m, int vb, bool sf, int64_t n_slots, int g, int64_t context);
 
 // Launchers (return a hipError_t from hipGetLastError after the launch).
 // matrix-core key quantisation: operand preparation (workspace) + kernel
@@ -179,8 +187,8 @@ hipError_t launch_topk(const TopkJob &job, hipStream_t stream);
 hipError_t launch_combine_window(const DecodeJob &job, const WindowJob &wj, hipStream_t stream);
 bool decode_supported(int d, int w, int g, int m, int vb);
 // matrix-core decode kernel (partials only; launch_combine merges them), shapes with a compiled kernel
-bool decode_mfma_supported(int d, int w, int g, int m, int vb);
-int decode_mfma_blocks_per_cu(int d, int w, int g, int m, int vb);
+bool decode_mfma_supported(int d, int w, int g, int m, int vb, bool sf);
+int decode_mfma_blocks_per_cu(int d, int w, int g, int m, int vb, bool sf);
 hipError_t launch_decode_mfma(const DecodeJob &job, hipStream_t stream);
 // per head_dim kernel launchers (decode_fast_d*.hip)
 hipError_t launch_decode_fast_d64(const DecodeJob &job, hipStream_t stream);
@@ -189,6 +197,22 @@ hipError_t launch_decode_fast_d256(const DecodeJob &job, hipStream_t stream);
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
+}
+
+// Side information as stored: fp32, or the nearest IEEE half (ties to even;
+// finite values beyond the half range saturate to +-65504, so a stored half is
+// never infinite unless the fp32 value was).
+__device__ __forceinline__ _Float16 side_half(float x) {
+  const float a = fabsf(x);
+  return static_cast<_Float16>(a > 65504.0f && a < __builtin_inff() ? copysignf(65504.0f, x) : x);
+}
+// side number i of a field that holds fp32 (sf false) or half (sf true) numbers
+__device__ __forceinline__ float load_side(const uint8_t *p, int64_t i, bool sf) {
+  return sf ? static_cast<float>(reinterpret_cast<const _Float16 *>(p)[i]) : reinterpret_cast<const float *>(p)[i];
+}
+__device__ __forceinline__ void store_side(uint8_t *p, int64_t i, bool sf, float x) {
+  if (sf) reinterpret_cast<_Float16 *>(p)[i] = side_half(x);
+  else reinterpret_cast<float *>(p)[i] = x;
 }
 
 }  // namespace aqkv

@@ -659,8 +659,10 @@ __device__ __forceinline__ void store_codes_norms(const KeyJob &job, const TileL
       }
     }
     if (g == 0) {
-      *reinterpret_cast<float *>(job.norm + L.at(nt, 4)) = nrm[nt];
-      if constexpr (W > 0) *reinterpret_cast<float *>(job.rnorm + L.at(nt, 4)) = gam[nt];
+      // fp32 or half rows (rec_row's record term is common to both widths)
+      const bool sf = job.sf != 0;
+      store_side(job.norm + L.rbase[nt], L.rin[nt], sf, nrm[nt]);
+      if constexpr (W > 0) store_side(job.rnorm + L.rbase[nt], L.rin[nt], sf, gam[nt]);
     }
   }
 }

@@ -314,8 +314,9 @@ __device__ __forceinline__ void store_batch(const KeyJob &job, int64_t batch0, i
   uint2 sv[NB];
   float nv[NB];
   uint2 *sp[NB];
-  float *np[NB];
+  uint8_t *np[NB];
   bool ok[NB];
+  const bool sf = job.sf != 0;   // half norms (else fp32)
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int64_t key0 = (batch0 + j * stride) * TK;
@@ -324,7 +325,7 @@ __device__ __forceinline__ void store_batch(const KeyJob &job, int64_t batch0, i
     const KeyAt a = key_at(job, B, key0, ok[j] ? key : 0);
     const int64_t rb = (a.row >> 5) * job.rec, ri = a.row & 31;
     sp[j] = reinterpret_cast<uint2 *>(job.signs + rb + ri * srow + 8 * u);
-    np[j] = reinterpret_cast<float *>(job.norm + rb + ri * 4);
+    np[j] = job.norm + rb + ri * (sf ? 2 : 4);
     sv[j] = *reinterpret_cast<const uint2 *>(sgn + (((s0 + j) % (NB + 1)) * TK + key) * SW + 2 * u);
     nv[j] = knorm[((n0 + j) % (NB + 2)) * TK + key];
   }
@@ -333,7 +334,10 @@ __device__ __forceinline__ void store_batch(const KeyJob &job, int64_t batch0, i
   for (int j = 0; j < NB; ++j) {
     if (ok[j]) {
       *sp[j] = sv[j];
-      if (u == 0) *np[j] = nv[j];
+      if (u == 0) {
+        if (sf) *reinterpret_cast<_Float16 *>(np[j]) = side_half(nv[j]);
+        else *reinterpret_cast<float *>(np[j]) = nv[j];
+      }
     }
   }
 }

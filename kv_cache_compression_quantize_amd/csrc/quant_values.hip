@@ -5,7 +5,9 @@
 //
 // code = clamp(rint((v - min) / scale), 0, 2^vb - 1) with scale = (max - min) /
 // (2^vb - 1), every step in IEEE fp32 (subtract, correctly rounded divide,
-// round-half-even); code 0 when scale == 0.
+// round-half-even); code 0 when scale == 0.  Scale and min are stored as
+// fp32, or rounded to the nearest half for a cache with half side information
+// (the codes are decided from the fp32 values either way).
 //
 // Lane layout.  The code block of a record stores, per (group g, column n,
 // token residue r), the codes of channel 32 g + 16 half + n for the tokens
@@ -115,9 +117,9 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueJob job, int 
   }
 
   const int g = chunk / 4, q = chunk % 4;         // group, lane within the group
-  // val_side float of (g, token c + 8 a, q): side_lane + 16 a
-  float *side_lane = reinterpret_cast<float *>(job.side + rec_row(s * job.capacity + ct0, 0, job.rec)) +
-                     side_index(g, c, q);
+  // val_side element of (g, token c + 8 a, q): side_i + 16 a of the record's field
+  uint8_t *side_rec = job.side + rec_row(s * job.capacity + ct0, 0, job.rec);
+  const int side_i = side_index(g, c, q);
   uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};     // per channel: its 4 codes, VB bits apart
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueJob job, int 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[j] |= codes[j] << (VB * a);
     const int tt = c + 8 * a;
-    if (q < 2 && tt >= t_lo && tt < t_hi) side_lane[16 * a] = q == 0 ? scale : mn;
+    if (q < 2 && tt >= t_lo && tt < t_hi) store_side(side_rec, side_i + 16 * a, job.sf != 0, q == 0 ? scale : mn);
   }
 
   // 2. bytes (vb = 2) / half-words (vb = 4) into the record's LDS words

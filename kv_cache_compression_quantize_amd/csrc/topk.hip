@@ -108,6 +108,7 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 struct SelectJob {
   float *scores;            // [n_slots][context]; overwritten with the order keys
   const uint8_t *norm;      // key_norm field at its place in record 0
+  int sf;                   // half norms (else fp32)
   int64_t rec, capacity, context;
   int budget;               // chosen tokens per slot (<= context)
   int32_t *selected;        // [n_slots][budget]
@@ -183,7 +184,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job)
     for (int u = 0; u < kBatch; ++u) {
       const int t = t0 + u * kSelThreads + tid;
       sc[u] = t < T ? sc_row[t] : 0.0f;
-      nn[u] = t < T ? *reinterpret_cast<const float *>(job.norm + rec_row(row0 + t, 4, job.rec)) : 0.0f;
+      nn[u] = t < T ? load_side(job.norm + rec_row((row0 + t) & ~int64_t(31), 0, job.rec), (row0 + t) & 31,
+                                job.sf != 0)
+                    : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -401,6 +404,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job)
 
 struct SparseJob {
   int d, w, m, vb, g;
+  int sf;                          // half side information (else fp32)
   int64_t capacity, rec;
   const uint8_t *codes, *signs, *norm, *rnorm, *vcodes, *vside;   // fields at their place in record 0
   const float *centroids;
@@ -521,8 +525,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(SparseJob job) 
     if (wd < sw) sg[t * sw + wd] = reinterpret_cast<const uint32_t *>(job.signs + rbase[t] + rtt[t] * (M / 8))[wd];
   }
   if (tid < nt) {
-    nr[2 * tid] = *reinterpret_cast<const float *>(job.norm + rbase[tid] + rtt[tid] * 4);
-    nr[2 * tid + 1] = W > 0 ? *reinterpret_cast<const float *>(job.rnorm + rbase[tid] + rtt[tid] * 4) : 0.0f;
+    nr[2 * tid] = load_side(job.norm + rbase[tid], rtt[tid], job.sf != 0);
+    nr[2 * tid + 1] = W > 0 ? load_side(job.rnorm + rbase[tid], rtt[tid], job.sf != 0) : 0.0f;
   }
   // value codes: item (group, n) of a token gives its channels 32 group + n and 32 group + 16 + n
   for (int i = tid; i < nt * (D / 2); i += kThreads) {
@@ -546,10 +550,9 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(SparseJob job) 
   }
   for (int i = tid; i < nt * kGroups; i += kThreads) {
     const int t = i / kGroups, grp = i % kGroups;
-    const float *side = reinterpret_cast<const float *>(job.vside + rbase[t]);
-    const float2 sm2 = *reinterpret_cast<const float2 *>(side + side_index(grp, rtt[t], 0));
-    vsd[(t * kGroups + grp) * 2] = sm2.x;
-    vsd[(t * kGroups + grp) * 2 + 1] = sm2.y;
+    const int si = side_index(grp, rtt[t], 0);
+    vsd[(t * kGroups + grp) * 2] = load_side(job.vside + rbase[t], si, job.sf != 0);
+    vsd[(t * kGroups + grp) * 2 + 1] = load_side(job.vside + rbase[t], si + 1, job.sf != 0);
   }
   __syncthreads();
 
@@ -701,6 +704,7 @@ hipError_t launch_topk(const TopkJob &j, hipStream_t stream) {
   SelectJob s{};
   s.scores = j.scores;
   s.norm = j.norm;
+  s.sf = j.sf;
   s.rec = j.rec;
   s.capacity = j.capacity;
   s.context = j.context;
@@ -725,6 +729,7 @@ hipError_t launch_topk(const TopkJob &j, hipStream_t stream) {
   p.w = j.w;
   p.m = j.m;
   p.vb = j.vb;
+  p.sf = j.sf;
   p.g = j.g;
   p.capacity = j.capacity;
   p.rec = j.rec;

@@ -38,12 +38,13 @@ class QuantizedKeys:
     y: np.ndarray          # [N, d] float64 rotated unit-sphere coordinates (diagnostic)
     z: np.ndarray          # [N, m] float64 projections S r (diagnostic)
 
-    def packed(self, w: int):
-        """The cache rows: (codes, signs, fp32 norm, fp32 residual norm)."""
+    def packed(self, w: int, side_f16: bool = False):
+        """The cache rows: (codes, signs, norm, residual norm), the norms as
+        stored (fp32, or half with the half side-information option)."""
         codes = layout.pack_code_planes(self.idx, w)
         signs = layout.pack_bits(self.bits)
-        return (codes, signs, self.norm.astype(np.float32),
-                self.rnorm.astype(np.float32))
+        return (codes, signs, layout.stored_side(self.norm, side_f16),
+                layout.stored_side(self.rnorm, side_f16))
 
 
 def quantize_keys(x, rotation, sketch, centroids, boundaries, w: int) -> QuantizedKeys:

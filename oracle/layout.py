@@ -19,7 +19,10 @@ bytes with one shift and one mask, and gets one value code per token of a
   32 g + 16 h + n -- and token T = 4 i + r of the block (r in 0..3, i in 0..7):
     vb = 2: 32-bit word (16 g + n) * 4 + r, bit 8 h + 16 (i & 1) + 2 (i >> 1);
     vb = 4: 32-bit word ((16 g + n) * 4 + r) * 2 + h, bit 16 (i & 1) + 4 (i >> 1);
-* norms, value scales and value minima are fp32, one row per token.
+* norms, value scales and value minima are fp32, one row per token; with the
+  half side-information option (the bytes-for-precision knob beside the
+  head_dim 256 compression figure of §一's Paper Validation table) they are
+  IEEE halves instead, see stored_side.
 """
 from __future__ import annotations
 
@@ -109,14 +112,38 @@ def unpack_value_codes(rows: np.ndarray, T: int, d: int, vb: int) -> np.ndarray:
     return codes.reshape(nblk * 32, d)[:T]
 
 
-def row_bytes(d: int, w: int, m: int, vb: int = 2, group: int = 32) -> dict:
-    """Bytes one token of one KV head occupies in each cache plane."""
+def row_bytes(d: int, w: int, m: int, vb: int = 2, group: int = 32, side_f16: bool = False) -> dict:
+    """Bytes one token of one KV head occupies in each cache plane (side
+    information 4 bytes a number, 2 with the half option)."""
+    e = 2 if side_f16 else 4
     return {
         "key_codes": w * d // 8,
         "key_signs": m // 8,
-        "key_norm": 4,
-        "key_rnorm": 4 if w > 0 else 0,
+        "key_norm": e,
+        "key_rnorm": e if w > 0 else 0,
         "val_codes": d * vb // 8,
-        "val_scale": 4 * (d // group),
-        "val_min": 4 * (d // group),
+        "val_scale": e * (d // group),
+        "val_min": e * (d // group),
     }
+
+
+HALF_MAX = 65504.0   # largest finite IEEE half: (2 - 2^-10) * 2^15
+
+
+def stored_side(x, side_f16: bool = False) -> np.ndarray:
+    """What the cache holds for side information x (the key norm and residual
+    norm that §五's quantize() keeps beside the bits, the value scale and
+    minimum of §七): the fp32 value; with the half option, that fp32 value
+    rounded to the nearest IEEE half, ties to the even significand, a finite
+    value past the half range saturating to +-HALF_MAX (a reading: the pages
+    give no half format; saturation keeps every stored number finite).
+    Returned in the stored type (float32 or float16).
+
+    The codes (indices, sign bits, value codes) never depend on this rounding:
+    they are decided from the unrounded numbers on both sides."""
+    x32 = np.asarray(x, dtype=np.float32)
+    if not side_f16:
+        return x32
+    big = (np.abs(x32) > np.float32(HALF_MAX)) & np.isfinite(x32)
+    x32 = np.where(big, np.copysign(np.float32(HALF_MAX), x32), x32)
+    return x32.astype(np.float16)

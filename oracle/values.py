@@ -14,7 +14,9 @@ both sides:
   precision the stored scale and minimum have; it is emulated here with
   numpy float32 arithmetic, which is IEEE round-to-nearest-even per operation;
 * dequantisation: v^ = code * scale + min, evaluated in float64 from the
-  stored fp32 scale and min.
+  stored scale and min (fp32, or their halves with the half side-information
+  option, layout.stored_side; the codes are decided from the fp32 numbers
+  either way).
 """
 from __future__ import annotations
 

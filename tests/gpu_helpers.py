@@ -71,8 +71,8 @@ def to_device_kv(x: np.ndarray, dtype: str):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
 
 
-def cfg_of(hl: HostLayer, vb: int = 2):
-    return aqkv.config(hl.d, hl.w, hl.m, vb, 32)
+def cfg_of(hl: HostLayer, vb: int = 2, side_f16: bool = False):
+    return aqkv.config(hl.d, hl.w, hl.m, vb, 32, side_f16)
 
 
 def read_planes(cache: aqkv.Cache, slot: int, t0: int, t1: int) -> dict:
@@ -87,12 +87,21 @@ def read_planes(cache: aqkv.Cache, slot: int, t0: int, t1: int) -> dict:
                 vcodes=vcodes, vscale=vscale.cpu().numpy(), vmin=vmin.cpu().numpy())
 
 
-def oracle_rows(hl: HostLayer, k: np.ndarray, v: np.ndarray, vb: int = 2):
-    """Oracle quantisation of one slot: (QuantizedKeys, packed key rows, value tuple, packed value codes)."""
+def oracle_rows(hl: HostLayer, k: np.ndarray, v: np.ndarray, vb: int = 2, side_f16: bool = False):
+    """Oracle quantisation of one slot: (QuantizedKeys, packed key rows, value tuple, packed
+    value codes); norms, scales and minima as the cache stores them (fp32, or halves)."""
     qk = okeys.quantize_keys(k, hl.rotation, hl.sketch, hl.centroids, hl.boundaries, hl.w)
-    kr = qk.packed(hl.w)
+    kr = qk.packed(hl.w, side_f16)
     vc, vs, vm = ovals.quantize_values(v, vb)
-    return qk, kr, (vc, vs, vm), olay.pack_value_codes(vc, vb)
+    vt = (vc, olay.stored_side(vs, side_f16), olay.stored_side(vm, side_f16))
+    return qk, kr, vt, olay.pack_value_codes(vc, vb)
+
+
+def half_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of the IEEE half grid at |x| (finite halves)."""
+    a = np.abs(np.asarray(x, dtype=np.float16)).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))      # subnormals share the smallest normal's spacing
+    return 2.0 ** (e - 10)
 
 
 @dataclass

@@ -60,6 +60,30 @@ def test_cache_layout_and_bad_configs():
     with pytest.raises(aqkv.AqkvError):
         aqkv.cache_layout(aqkv.config(128, 2, 128, value_bits=3))
     assert aqkv.lib().aqkv_cache_layout(None, None) == -1
+    bad = aqkv.config(128, 2, 128)
+    bad.side_f16 = 2
+    with pytest.raises(aqkv.AqkvError) as e:
+        aqkv.cache_layout(bad)
+    assert e.value.status == -2
+
+
+def test_half_side_information_layout():
+    # d = 256, 3-bit keys (w = 2, m = d), 2-bit values: 196 bytes a token, 1024 / 196 = 5.22x bf16 K + V
+    lo = aqkv.cache_layout(aqkv.config(256, 2, 256, side_f16=True))
+    rb = lo["row"]
+    assert rb == dict(key_codes=64, key_signs=32, key_norm=2, key_rnorm=2, val_codes=64, val_side=32)
+    assert sum(rb.values()) == 196 and round(1024 / 196, 2) == 5.22
+    assert sum(aqkv.cache_layout(aqkv.config(256, 2, 256))["row"].values()) == 232
+    for d, w, m, vb in [(64, 0, 64, 2), (128, 0, 192, 4), (256, 3, 1024, 2), (128, 1, 128, 4)]:
+        full = aqkv.cache_layout(aqkv.config(d, w, m, vb))
+        half = aqkv.cache_layout(aqkv.config(d, w, m, vb, side_f16=True))
+        off = 0
+        for name in aqkv.FIELDS:
+            assert half["offset"][name] == off
+            off += 32 * half["row"][name]
+            wide = name in aqkv.FLOAT_FIELDS
+            assert half["row"][name] == (full["row"][name] // 2 if wide else full["row"][name])
+        assert off == half["block_bytes"] and off % 16 == 0
 
 
 def test_workspace_sizes():

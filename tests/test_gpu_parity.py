@@ -257,7 +257,7 @@ def _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity):
     cache.blocks.zero_()
     refs = []
     for s in range(n_slots):
-        qk, kr, vt, vpacked = oracle_rows(hl, ks[s], vs[s], vb)
+        qk, kr, vt, vpacked = oracle_rows(hl, ks[s], vs[s], vb, bool(cfg.side_f16))
         T = ks[s].shape[0]
         r0 = s * cache.capacity          # allocate() rounds the capacity up to 32
         codes, signs, norm, rnorm = kr
@@ -268,7 +268,7 @@ def _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity):
         cache.set_rows("key_norm", r0, torch.from_numpy(norm).to(dev))
         cache.set_rows("val_codes", r0, torch.from_numpy(vpacked).to(dev))
         cache.set_value_side(r0, torch.from_numpy(vt[1]).to(dev), torch.from_numpy(vt[2]).to(dev))
-        # the oracle consumes exactly what was stored (fp32 norms)
+        # the oracle consumes exactly what was stored (fp32 or half norms, scales and minima)
         refs.append(((qk.idx, qk.bits, norm.astype(np.float64), rnorm.astype(np.float64)), vt))
     return cache, refs
 
@@ -290,12 +290,16 @@ DECODE_CASES = [
 
 @pytest.mark.parametrize("d,w,m,G,vb,T", DECODE_CASES)
 def test_decode_parity_on_oracle_planes(d, w, m, G, vb, T):
+    run_decode_parity(d, w, m, G, vb, T)
+
+
+def run_decode_parity(d, w, m, G, vb, T, side_f16=False):
     torch, dev = torch_dev()
-    say("decode", d, w, m, G, vb, T)
+    say("decode", d, w, m, G, vb, T, "half side" if side_f16 else "")
     B, Hkv = 2, 2
     Hq = Hkv * G
     hl = host_layer(d, w, m, layer=3)
-    cfg = cfg_of(hl, vb)
+    cfg = cfg_of(hl, vb, side_f16)
     layer = device_layer(hl)
     rng = np.random.default_rng(d * 7 + T)
     ks = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(B * Hkv)]

@@ -31,12 +31,16 @@ CASES = [
 
 @pytest.mark.parametrize("d,w,m,G,T,budget,vb", CASES)
 def test_topk_selection_and_decode(d, w, m, G, T, budget, vb):
+    run_topk(d, w, m, G, T, budget, vb)
+
+
+def run_topk(d, w, m, G, T, budget, vb, side_f16=False):
     torch, dev = torch_dev()
-    say("top-k", d, w, m, G, T, budget, vb)
+    say("top-k", d, w, m, G, T, budget, vb, "half side" if side_f16 else "")
     B, Hkv = 2, 2
     Hq = Hkv * G
     hl = host_layer(d, w, m, layer=6)
-    cfg = cfg_of(hl, vb)
+    cfg = cfg_of(hl, vb, side_f16)
     layer = device_layer(hl)
     rng = np.random.default_rng(d + T + budget)
     ks = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(B * Hkv)]
