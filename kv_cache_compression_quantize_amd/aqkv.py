@@ -253,11 +253,13 @@ class Cache:
         if rb == 0:
             return None
         n_rec = self.blocks.shape[0]
+        flat = self.blocks.view(-1)
+        # as_strided takes an offset into the whole storage: the buffer may itself be a view
         if name in FLOAT_FIELDS:
             e = 2 if self.cfg.side_f16 else 4
-            f = self.blocks.view(-1).view(dtype=torch.float16 if e == 2 else torch.float32)
-            return f.as_strided((n_rec, 32, rb // e), (bb // e, rb // e, 1), off // e)
-        return self.blocks.view(-1).as_strided((n_rec, 32, rb), (bb, rb, 1), off)
+            f = flat.view(dtype=torch.float16 if e == 2 else torch.float32)
+            return f.as_strided((n_rec, 32, rb // e), (bb // e, rb // e, 1), f.storage_offset() + off // e)
+        return flat.as_strided((n_rec, 32, rb), (bb, rb, 1), flat.storage_offset() + off)
 
     def rows(self, name: str, row0: int, n: int):
         """Copy of cache rows row0 .. row0 + n - 1 (row = slot * capacity + token) of a field:

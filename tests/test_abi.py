@@ -316,3 +316,21 @@ def test_noalloc_decode_validation_codes():
     assert call(scale=0.0) == -2
     assert call(out=None) == -1
     assert call(b=0, hkv=2) == -2                       # zero batch against a two-slot cache
+
+
+@pytest.mark.parametrize("side_f16", [False, True])
+def test_cache_field_views_over_a_buffer_view(side_f16):
+    # a cache whose records are a slice of a larger buffer (guard records around it): every
+    # field view reads the slice's bytes, not the larger buffer's
+    import torch
+    cfg = aqkv.config(128, 2, 128, side_f16=side_f16)
+    lo = aqkv.cache_layout(cfg)
+    big = (torch.arange(10 * lo["block_bytes"]) % 251).to(torch.uint8).reshape(10, -1)
+    inner = aqkv.Cache(cfg, 2, 64, big[3:7], lo)
+    copy = aqkv.Cache(cfg, 2, 64, big[3:7].clone(), lo)
+    for name in aqkv.FIELDS:
+        a, b = inner.field(name), copy.field(name)
+        assert a.dtype == b.dtype and torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+    s1, m1 = inner.value_side(5, 40)
+    s2, m2 = copy.value_side(5, 40)
+    assert torch.equal(s1.view(torch.uint8), s2.view(torch.uint8)) and torch.equal(m1.view(torch.uint8), m2.view(torch.uint8))
