@@ -17,7 +17,11 @@
 // v_mfma_i32_16x16x64_i8 then contracts 64 coordinates of 16 tokens for 16
 // rows = 4 heads x {mse hi, mse lo, qjl hi, qjl lo} with exact integer
 // accumulation; a key bit becomes an int8 {0,1} operand byte with one shift
-// and one mask per 4 bits (bit rows are byte-transposed for this).
+// and one mask per 4 bits (bit rows are byte-transposed for this).  Pure-QJL
+// keys have no mse rows, and spend them on a cheaper sign operand: one mask
+// per 4 bits, each bit left at its place e in its byte (value 2^e, -128 for
+// e = 7), against query values pre-multiplied by 2^(7 - e) (-1 for e = 7) and
+// written as three base-128 digits, rows {Q >> 14, (Q >> 7) & 127, Q & 127}.
 //
 // Values: out[g] = sum_t p_t (code_t scale_t + min_t).  The f16 operand is the
 // code itself in the low mantissa bits with a zero exponent, i.e. the exact
@@ -96,6 +100,15 @@ __device__ __forceinline__ v4i spread_half(uint32_t x, int hf) {
   for (int k = 0; k < 4; ++k) r[k] = static_cast<int>((x >> (4 * hf + k)) & 0x01010101u);
   return r;
 }
+// The same bits left in place, one mask per register: byte b of register k is
+// bit (4 hf + k) of byte b of x times 2^(4 hf + k) (as int8: -128 for bit 7);
+// the A operand carries the inverse weights (pure-QJL sign chunks).
+__device__ __forceinline__ v4i mask_half(uint32_t x, int hf) {
+  v4i r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = static_cast<int>(x & (0x01010101u << (4 * hf + k)));
+  return r;
+}
 
 // max over the 16 lanes of a DPP row, result in every lane of the row: the
 // same four lane permutations as row_sum16, through the compiler's DPP move
@@ -154,21 +167,23 @@ struct HeadConst {
 __host__ __device__ constexpr int pairs_of(int g, int d) { return (g * (d / 32) + 3) / 4; }
 
 // Tile staging: every cache plane of 32 tokens, copied whole into a per-wave
-// ring of kRing buffers (tiles t+1 .. t+kRing-1 stream in while t is computed;
-// two buffers and more resident waves beat deeper prefetch with fewer waves).
-constexpr int kRing = 2;
+// ring of R buffers (tiles t+1 .. t+R-1 stream in while t is computed).
 // (sf: side information stored as half, 2 bytes a number instead of 4)
 __host__ __device__ constexpr int tile_bytes_of(int d, int w, int mc, int vb, bool sf) {
   const int e = sf ? 2 : 4;
   return kTT * (w * d / 8 + mc * 8 + e + (w > 0 ? e : 0) + d * vb / 8 + 2 * e * (d / 32));   // = record bytes
 }
+// Two buffers for every shape: measured on the large workloads, three or four
+// (two or three tiles in flight, fewer resident waves for the LDS they take)
+// decode 3-10 % slower.
+__host__ __device__ constexpr int ring_of(int d, int w, int mc, int vb, bool sf) { return 2; }
 // LDS bytes per block of decode_fast_kernel<D, W, m / 64, G, VB, SF> (host and device):
 // per wave the tile ring and the value-weight operand [groups][4][2G + 1 rows][16 B],
 // whose first bytes also hold the softmax weights P [32 tokens][G] until they are
 // read; at the end the 4-wave merge
 __host__ __device__ constexpr int aval_rows_of(int g) { return 2 * g + 1; }   // + 1 row: writes spread over all banks
 __host__ __device__ constexpr int wave_lds_of(int d, int w, int mc, int g, int vb, bool sf) {
-  return kRing * tile_bytes_of(d, w, mc, vb, sf) + (d / 32) * 4 * aval_rows_of(g) * 16;
+  return ring_of(d, w, mc, vb, sf) * tile_bytes_of(d, w, mc, vb, sf) + (d / 32) * 4 * aval_rows_of(g) * 16;
 }
 __host__ __device__ constexpr int smem_of(int d, int w, int mc, int g, int vb, bool sf) {
   const int waves = kWaves * wave_lds_of(d, w, mc, g, vb, sf);
@@ -199,6 +214,7 @@ struct Geo {
   static constexpr int o_vside = o_vcodes + kTT * VBY;
   static constexpr int tile_bytes = o_vside + kTT * kGroups * 2 * E;
   static_assert(tile_bytes == tile_bytes_of(D, W, MC, VB, SF), "tile geometry");
+  static constexpr int kR = ring_of(D, W, MC, VB, SF);   // tile buffers per wave
   static constexpr int wave_lds = wave_lds_of(D, W, MC, G, VB, SF);
   static constexpr int AR = aval_rows_of(G);        // 16-byte rows per (group, lane group) block
   static constexpr int aval_bytes = kGroups * 4 * AR * 16;
@@ -218,7 +234,8 @@ struct Geo {
 // chunks) is split into int8 parts hi = v >> 7, lo = v & 127 and written to
 // `ops`, lane-major: byte i of lane (row, q) of chunk c in row block r sits at
 // ((r * NC + c) * 64 + lane) * 16 + i and is K-slot 16 q + i; row = 4 (g % 4) + t
-// with t = mse hi, mse lo, qjl hi, qjl lo and g = 4 r + row / 4.  K-slot 16 q + i of
+// with t = mse hi, mse lo, qjl hi, qjl lo (pure QJL: the three digits of the
+// bit-place-weighted value, then a zero row) and g = 4 r + row / 4.  K-slot 16 q + i of
 // chunk h of a plane is coordinate (D/4) q + 16 h + i; of sign chunk h, sketch row
 // 16 MC q + 16 h + i.
 template <int D, int W, int MC, int G, int PL>
@@ -278,16 +295,26 @@ __device__ __forceinline__ void pack_query(const DecodeJob &job, int64_t head0, 
           src = job.q_rot + (head0 + g) * D + (D / 4) * q + 16 * (c % HC) + i0;
           scl = kappa[a - 1] / hc[g].sig_mse;
         }
-      } else if (t >= 2) {
+      } else if (W == 0 ? t < 3 : t >= 2) {
         src = job.q_sketch + (head0 + g) * m + 16 * MC * q + 16 * (c - NP * HC) + i0;
         scl = 2.0f / hc[g].sig_qjl;
       }
       if (src) {
+        // pure QJL: the B bytes of this K-slot carry the bit times 2^e (e = 4 hf + i0 / 4, the
+        // bit's place in its byte; -128 for e = 7), so the value becomes Q = v 2^(7 - e)
+        // (-v for e = 7), < 2^21 in magnitude, in base-128 digits Q >> 14, (Q >> 7) & 127, Q & 127
+        const int e = 4 * ((MC * q + (c - NP * HC)) & 1) + i0 / 4;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           int v = static_cast<int>(rintf(src[bb] * scl));
           v = max(-16383, min(16383, v));
-          const int part = (t & 1) ? (v & 127) : (v >> 7);
+          int part;
+          if constexpr (W == 0) {
+            const int Q = e == 7 ? -v : v * (1 << (7 - e));
+            part = t == 0 ? (Q >> 14) : t == 1 ? ((Q >> 7) & 127) : (Q & 127);
+          } else {
+            part = (t & 1) ? (v & 127) : (v >> 7);
+          }
           word |= (static_cast<uint32_t>(part) & 0xffu) << (8 * bb);
         }
       }
@@ -320,6 +347,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   // the waves' value-weight operands
   uint8_t *qa_lds = smem;
   uint8_t *ring = smem + Gm::qa_lds_bytes;
+  constexpr int kRing = Gm::kR;
   uint8_t *aval = ring + kRing * kWaves * Gm::tile_bytes + wave * Gm::aval_bytes;   // [grp][q][AR][16 B]
   float *P = reinterpret_cast<float *>(aval);   // [kTT][G], read out before aval is written
   auto slot_buf = [&](int64_t tile) -> uint8_t * {
@@ -331,10 +359,12 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   const int64_t recs = job.capacity / kTT;
   const __amdgpu_buffer_rsrc_t rs_blocks =
       plane_rsrc(job.blocks + slot * recs * Gm::tile_bytes, static_cast<uint32_t>(recs * Gm::tile_bytes));
-  // a scores-only call needs the key fields of a record alone (they come first); the
-  // wait below is for all loads in flight, so the shorter tiles need no other count
-  static_assert(kRing == 2, "tile waits assume one tile in flight beside the current one");
+  // a scores-only call needs the key fields of a record alone (they come first), so
+  // its tiles take fewer loads
   const bool keys_only = job.scores_only != 0;
+  // score stores share the vector-memory counter with the tile loads, and a wait
+  // for a partial count is only sound with loads alone in flight
+  const bool partial_waits = job.scores == nullptr;
   auto issue = [&](int64_t tile) {
     const uint32_t rec = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t_begin / kTT + tile));
     if (keys_only)
@@ -400,7 +430,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
     // wait for this tile: the (up to kRing - 2) later tiles already issued may stay in flight
     static_assert(kRing >= 2 && kRing <= 4, "wait ladder");
     {
-      const int64_t after = (n_tiles - 1 - tile) / kWaves;
+      const int64_t after = partial_waits ? (n_tiles - 1 - tile) / kWaves : 0;
       if (kRing >= 4 && after >= 2) wait_vm<(kRing >= 4 ? 2 : 0) * Gm::loads_per_tile>();
       else if (kRing >= 3 && after >= 1) wait_vm<(kRing >= 3 ? 1 : 0) * Gm::loads_per_tile>();
       else wait_vm<0>();
@@ -481,7 +511,8 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
             for (int u = 1; u < kSw; ++u) word = (wi == u) ? sw[ct][u] : word;
             hf = (c >> 4) & 1;
           }
-          const v4i bop = spread_half(word, hf);
+          // pure QJL: bits in place (three-digit query rows); else one {0,1} byte per bit
+          const v4i bop = W == 0 ? mask_half(word, hf) : spread_half(word, hf);
 #pragma unroll
           for (int r = 0; r < RB; ++r)
             acc[ct][r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A(r, chunk), bop, acc[ct][r], 0, 0, 0);
@@ -508,7 +539,13 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
         float s = 0.0f;
         if constexpr (W > 0)
           s = nrm * fmaf(hc[r].sig_mse, static_cast<float>(acc[ct][r][0] * 128 + acc[ct][r][1]), hc[r].c_mse);
-        const float qjl = fmaf(hc[r].sig_qjl, static_cast<float>(acc[ct][r][2] * 128 + acc[ct][r][3]), hc[r].c_qjl);
+        // sum of the head's integer query values over the set sign bits: hi * 128 + lo, or
+        // for pure QJL the three base-128 digits of 128 x that sum
+        const float qs = W == 0 ? fmaf(static_cast<float>(acc[ct][r][0]), 128.0f,
+                                       fmaf(static_cast<float>(acc[ct][r][2]), 0.0078125f,
+                                            static_cast<float>(acc[ct][r][1])))
+                                : static_cast<float>(acc[ct][r][2] * 128 + acc[ct][r][3]);
+        const float qjl = fmaf(hc[r].sig_qjl, qs, hc[r].c_qjl);
         s = fmaf(kappa_qjl * gam, qjl, s);
         score[ct][r] = s;
         logit[ct][r] = (valid && g < G) ? s * lscale : -INFINITY;
