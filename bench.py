@@ -142,6 +142,9 @@ class Path:
             self.tws = torch.empty(max(aqkv.decode_topk_workspace_bytes(self.cfg, w.batch, w.n_q_heads,
                                                                         w.n_kv_heads, w.context, self.budget), 256),
                                    dtype=torch.uint8, device=dev)
+            self.bws = torch.empty(max(aqkv.decode_topk_blocks_workspace_bytes(
+                self.cfg, w.batch, w.n_q_heads, w.n_kv_heads, w.context, self.budget), 256),
+                dtype=torch.uint8, device=dev)
 
     def quantize_keys(self):
         self.aqkv.quantize_keys_prepared(self.cfg, self.layer, self.x["k"], self.cache, self.kws)
@@ -171,6 +174,12 @@ class Path:
         self.aqkv.decode_attention_topk(self.cfg, self.layer, self.cache, w.batch, w.n_q_heads, w.n_kv_heads,
                                         w.context, self.q_f32, self.q_rot, self.q_sk, self.budget, None, None,
                                         self.out, self.tws)
+
+    def decode_topk_blocks(self):
+        w = self.w
+        self.aqkv.decode_attention_topk_blocks(self.cfg, self.layer, self.cache, w.batch, w.n_q_heads,
+                                               w.n_kv_heads, w.context, self.q_f32, self.q_rot, self.q_sk,
+                                               self.budget, None, None, self.out, self.bws)
 
     def step(self, ev=None):
         # one stream: values, keys, the query, then decode (split-K + combine).  A second stream
@@ -241,7 +250,7 @@ def time_calls(path, reps: int, names=None) -> dict:
     import torch
     stream = torch.cuda.current_stream()
     names = names or ["quantize_keys", "quantize_values", "prepare_query", "decode", "prepare_key_operands",
-                      "decode_window", "decode_topk"]
+                      "decode_window", "decode_topk", "decode_topk_blocks"]
     ev = {n: [] for n in names}
     for _ in range(reps):
         for n in names:
@@ -637,7 +646,9 @@ def main():
                 "prepare_query_ms": per["prepare_query"],
                 "prepare_key_operands_ms_once_per_layer": per["prepare_key_operands"],
                 "decode_window_ms": per["decode_window"], "window_tokens": path.n_window,
-                "decode_topk_ms": per["decode_topk"], "topk_budget": path.budget}
+                "decode_topk_ms": per["decode_topk"], "topk_budget": path.budget,
+                "decode_topk_blocks_ms": per["decode_topk_blocks"],
+                "topk_blocks_records": -(-path.budget // 32)}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         rec["cpu_baseline"] = cpu_baseline(w, layers)

@@ -316,6 +316,34 @@ aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer 
                                        float softmax_scale, int32_t *selected, float *out,
                                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes aqkv_decode_attention_topk_blocks needs for these sizes (0
+ * on bad arguments). */
+size_t aqkv_decode_topk_blocks_workspace_bytes(const aqkv_config *cfg, int32_t batch, int32_t n_q_heads,
+                                               int32_t n_kv_heads, int64_t context_len, int64_t budget);
+
+/* The same query-aware selection at the granularity of the cache's 32-row
+ * block records (QUOKA article §2: the KV cache organised as contiguous
+ * memory blocks; a reading, the article ranks keys, not blocks): a record
+ * ranks by the largest cos_t of its rows below context_len, and the
+ * nb = min(ceil(budget / 32), ceil(context_len / 32)) records with the largest
+ * ranks (ties to the lower record) are chosen; each query head then attends
+ * every row below context_len of the chosen records, exactly as
+ * aqkv_decode_attention attends all rows.  Reading whole records keeps every
+ * load a contiguous stream, where a row-level choice touches most of the
+ * cache's bytes through its rows' shared block words.  selected, if not NULL,
+ * receives the chosen records of every slot in increasing order
+ * ([batch * n_kv_heads][nb] int32, dev).  Shapes the matrix-core decoder does
+ * not cover (for one query head per slot and for n_q_heads / n_kv_heads)
+ * return AQKV_ERR_UNSUPPORTED.  Other arguments and rules as
+ * aqkv_decode_attention_topk, workspace of
+ * aqkv_decode_topk_blocks_workspace_bytes(...) bytes. */
+aqkv_status aqkv_decode_attention_topk_blocks(const aqkv_config *cfg, const aqkv_layer *layer,
+                                              const aqkv_cache *cache, int32_t batch, int32_t n_q_heads,
+                                              int32_t n_kv_heads, int64_t context_len, const float *q,
+                                              const float *q_rot, const float *q_sketch, int64_t budget,
+                                              float softmax_scale, int32_t *selected, float *out,
+                                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* -------------------------------------------------- allocation-free variant */
 
 /* For callers that cannot allocate device memory or hand over a workspace

@@ -103,6 +103,12 @@ _SIGS = {
                                                C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
                                                _P(KvView), _P(KvView), C.c_float, C.c_void_p, C.c_void_p,
                                                C.c_void_p, C.c_size_t, C.c_void_p]),
+    "aqkv_decode_topk_blocks_workspace_bytes": (C.c_size_t, [_P(Config), C.c_int32, C.c_int32, C.c_int32,
+                                                             C.c_int64, C.c_int64]),
+    "aqkv_decode_attention_topk_blocks": (C.c_int, [_P(Config), _P(LayerParams), _P(CacheDesc), C.c_int32,
+                                                    C.c_int32, C.c_int32, C.c_int64, C.c_void_p, C.c_void_p,
+                                                    C.c_void_p, C.c_int64, C.c_float, C.c_void_p, C.c_void_p,
+                                                    C.c_void_p, C.c_size_t, C.c_void_p]),
     "aqkv_read_stream": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p]),
     "aqkv_decode_static_scratch_bytes": (C.c_size_t, []),
     "aqkv_decode_attention_noalloc": (C.c_int, [_P(Config), _P(LayerParams), _P(CacheDesc), C.c_int32, C.c_int32,
@@ -458,6 +464,35 @@ def decode_attention_topk(cfg: Config, layer: Layer, cache: Cache, batch: int, n
                                           budget, C.c_float(softmax_scale), _ptr(selected), _ptr(out),
                                           _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "aqkv_decode_attention_topk")
+    return out
+
+
+def decode_topk_blocks_workspace_bytes(cfg: Config, batch: int, n_q_heads: int, n_kv_heads: int,
+                                       context_len: int, budget: int) -> int:
+    return int(lib().aqkv_decode_topk_blocks_workspace_bytes(C.byref(cfg), batch, n_q_heads, n_kv_heads,
+                                                             context_len, budget))
+
+
+def decode_attention_topk_blocks(cfg: Config, layer: Layer, cache: Cache, batch: int, n_q_heads: int,
+                                 n_kv_heads: int, context_len: int, q, q_rot, q_sketch, budget: int,
+                                 softmax_scale: Optional[float] = None, selected=None, out=None, workspace=None,
+                                 stream=None):
+    """Decode over the ceil(budget / 32) block records per KV slot with the largest group cosine of any
+    of their rows (q: unrotated fp32)."""
+    import torch
+    dev = q_sketch.device
+    if softmax_scale is None:
+        softmax_scale = 1.0 / float(np.sqrt(cfg.head_dim))
+    if out is None:
+        out = torch.empty((batch, n_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+    if workspace is None:
+        ws_bytes = decode_topk_blocks_workspace_bytes(cfg, batch, n_q_heads, n_kv_heads, context_len, budget)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    st = lib().aqkv_decode_attention_topk_blocks(C.byref(cfg), C.byref(layer.desc()), C.byref(cache.desc()), batch,
+                                                 n_q_heads, n_kv_heads, context_len, _ptr(q), _ptr(q_rot),
+                                                 _ptr(q_sketch), budget, C.c_float(softmax_scale), _ptr(selected),
+                                                 _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "aqkv_decode_attention_topk_blocks")
     return out
 
 

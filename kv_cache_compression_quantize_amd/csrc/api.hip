@@ -341,11 +341,21 @@ struct WindowArgs {
   const aqkv_kv_view *k, *v;
 };
 
+// Matrix-core decoder options of the record top-K: the scoring pass's per-record maximum
+// cosine output, or a decode over listed records only (context_len is then 32 x the list
+// length and list_context the cached length)
+struct DecodeExtra {
+  float *rec_max;
+  int64_t rec_max_stride;
+  const int32_t *rec_list;
+  int64_t list_stride, list_context;
+};
+
 static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const aqkv_cache *cache, int32_t batch,
                           int32_t n_q_heads, int32_t n_kv_heads, int64_t context_len, const float *q_rot,
                           const float *q_sketch, float softmax_scale, float *scores, float *out, void *workspace,
                           size_t workspace_bytes, void *stream, const WindowArgs *win, bool scores_only = false,
-                          void *(*static_scratch)() = nullptr) {
+                          void *(*static_scratch)() = nullptr, const DecodeExtra *extra = nullptr) {
   aqkv_status st = check_config(cfg);
   if (st != AQKV_OK) return st;
   if (!layer) return AQKV_ERR_NULL;
@@ -421,7 +431,15 @@ static aqkv_status decode(const aqkv_config *cfg, const aqkv_layer *layer, const
   job.part_acc = static_cast<float *>(workspace);
   char *ws = static_cast<char *>(workspace);
   job.part_ml = reinterpret_cast<float *>(ws + plan.acc_bytes);
-  job.scores_only = scores_only && scores && !win ? 1 : 0;
+  job.scores_only = scores_only && (scores || (extra && extra->rec_max)) && !win ? 1 : 0;
+  if (extra) {
+    if (!plan.mfma) return AQKV_ERR_UNSUPPORTED;
+    job.rec_max = extra->rec_max;
+    job.rec_max_stride = extra->rec_max_stride;
+    job.rec_list = extra->rec_list;
+    job.list_stride = extra->list_stride;
+    job.list_context = extra->list_context;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the matrix-core decoder addresses a slot's records with 32-bit byte offsets
   if (plan.mfma && cache->capacity / kBlockRows * L.rec >= (int64_t(1) << 31)) return AQKV_ERR_UNSUPPORTED;
@@ -601,6 +619,125 @@ aqkv_status aqkv_decode_attention_topk(const aqkv_config *cfg, const aqkv_layer 
   cj.part_ml = tj.part_ml;
   cj.out = out;
   return hip_status(launch_combine(cj, s));
+}
+
+// Workspace of the record top-K decode: the selection query, its rotation and sketch,
+// the per-record maximum cosines, the scoring pass's output and split workspace, the
+// chosen records and the split workspace of the decode over them, each 256-byte aligned.
+struct BlockTopkLayout {
+  size_t qsel_rot, qsel_sk, rec_max, dec_out, dec_ws, dec_ws_bytes, sel, list_ws, list_ws_bytes, total;
+};
+static BlockTopkLayout block_topk_layout(const aqkv_config *cfg, int64_t n_slots, int g, int64_t context,
+                                         int64_t n_rec, int64_t nb) {
+  const int d = cfg->head_dim, m = cfg->sketch_dim;
+  const bool sf = cfg->side_f16 != 0;
+  BlockTopkLayout L{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at += round_up(bytes, 256);
+    return here;
+  };
+  L.qsel_rot = take(sizeof(float) * n_slots * d);
+  L.qsel_sk = take(sizeof(float) * n_slots * m);
+  L.rec_max = take(sizeof(float) * n_slots * n_rec);
+  L.dec_out = take(sizeof(float) * n_slots * d);
+  L.dec_ws_bytes = decode_plan(d, cfg->mse_bits, m, cfg->value_bits, sf, n_slots, 1, context).total_bytes;
+  L.dec_ws = take(L.dec_ws_bytes);
+  L.sel = take(sizeof(int32_t) * n_slots * nb);
+  L.list_ws_bytes = decode_plan(d, cfg->mse_bits, m, cfg->value_bits, sf, n_slots, g, nb * kBlockRows).total_bytes;
+  L.list_ws = take(L.list_ws_bytes);
+  L.total = at;
+  return L;
+}
+
+// records chosen for a budget of `budget` tokens over n_rec records
+static int64_t block_budget(int64_t budget, int64_t n_rec) {
+  return std::max<int64_t>(1, std::min<int64_t>((budget + kBlockRows - 1) / kBlockRows, n_rec));
+}
+
+size_t aqkv_decode_topk_blocks_workspace_bytes(const aqkv_config *cfg, int32_t batch, int32_t n_q_heads,
+                                               int32_t n_kv_heads, int64_t context_len, int64_t budget) {
+  if (check_config(cfg) != AQKV_OK) return 0;
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads || context_len < 0 || budget < 1)
+    return 0;
+  const int64_t n_slots = static_cast<int64_t>(batch) * n_kv_heads;
+  const int64_t n_rec = (context_len + kBlockRows - 1) / kBlockRows;
+  const int64_t nb = block_budget(std::min<int64_t>(budget, kMaxBudget), n_rec);
+  return block_topk_layout(cfg, n_slots, n_q_heads / n_kv_heads, context_len, n_rec, nb).total;
+}
+
+aqkv_status aqkv_decode_attention_topk_blocks(const aqkv_config *cfg, const aqkv_layer *layer,
+                                              const aqkv_cache *cache, int32_t batch, int32_t n_q_heads,
+                                              int32_t n_kv_heads, int64_t context_len, const float *q,
+                                              const float *q_rot, const float *q_sketch, int64_t budget,
+                                              float softmax_scale, int32_t *selected, float *out, void *workspace,
+                                              size_t workspace_bytes, void *stream) {
+  aqkv_status st = check_config(cfg);
+  if (st != AQKV_OK) return st;
+  if (!layer) return AQKV_ERR_NULL;
+  if ((st = check_cache_shape(cache)) != AQKV_OK) return st;
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || context_len < 0 || budget < 1) return AQKV_ERR_SHAPE;
+  if (n_q_heads % n_kv_heads) return AQKV_ERR_SHAPE;
+  const int g = n_q_heads / n_kv_heads;
+  if (g > kMaxQPerKv) return AQKV_ERR_UNSUPPORTED;
+  if (budget > kMaxBudget) return AQKV_ERR_UNSUPPORTED;
+  if (context_len > kMaxTopkContext) return AQKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(batch) * n_kv_heads != cache->n_slots) return AQKV_ERR_SHAPE;
+  if (context_len > cache->capacity) return AQKV_ERR_CAPACITY;
+  if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return AQKV_ERR_SHAPE;
+  const int d = cfg->head_dim, w = cfg->mse_bits, m = cfg->sketch_dim;
+  const bool sf = cfg->side_f16 != 0;
+  // both passes run on the matrix-core decoder
+  if (!decode_mfma_supported(d, w, 1, m, cfg->value_bits, sf) || !decode_mfma_supported(d, w, g, m, cfg->value_bits, sf))
+    return AQKV_ERR_UNSUPPORTED;
+  if (batch == 0) return AQKV_OK;
+  if (!out || !q || !q_sketch || !layer->sketch) return AQKV_ERR_NULL;
+  if (w > 0 && (!q_rot || !layer->centroids || !layer->rotation)) return AQKV_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(q_sketch, 16) || (q_rot && !aligned(q_rot, 16)) ||
+      (selected && !aligned(selected, 4)))
+    return AQKV_ERR_ALIGN;
+  const int64_t n_rec = (context_len + kBlockRows - 1) / kBlockRows;
+  const int64_t nb = block_budget(budget, n_rec);
+  const BlockTopkLayout TL = block_topk_layout(cfg, cache->n_slots, g, context_len, n_rec, nb);
+  if (!workspace || workspace_bytes < TL.total) return AQKV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return AQKV_ERR_ALIGN;
+  char *ws = static_cast<char *>(workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (context_len == 0) {   // nothing cached: a combine over no parts writes out = 0
+    DecodeJob zj{};
+    zj.d = d;
+    zj.g = g;
+    zj.n_slots = cache->n_slots;
+    zj.part_stride = 0;
+    zj.part_acc = reinterpret_cast<float *>(ws + TL.list_ws);
+    zj.part_ml = reinterpret_cast<float *>(ws + TL.list_ws);
+    zj.out = out;
+    return hip_status(launch_combine(zj, s));
+  }
+  if ((st = check_blocks(cache)) != AQKV_OK) return st;
+
+  // 1. the selection query of every KV slot, rotated and sketched
+  float *qsel_rot = reinterpret_cast<float *>(ws + TL.qsel_rot);
+  float *qsel_sk = reinterpret_cast<float *>(ws + TL.qsel_sk);
+  if (launch_selection_query(q, cache->n_slots, d, g, m, layer->rotation, layer->sketch, w > 0 ? qsel_rot : nullptr,
+                             qsel_sk, s) != hipSuccess)
+    return AQKV_ERR_HIP;
+  // 2. every record's largest cosine estimate (the decoder's scoring pass, one query per slot)
+  float *rec_max = reinterpret_cast<float *>(ws + TL.rec_max);
+  DecodeExtra score_pass{rec_max, n_rec, nullptr, 0, 0};
+  st = decode(cfg, layer, cache, batch, n_kv_heads, n_kv_heads, context_len, w > 0 ? qsel_rot : nullptr, qsel_sk,
+              softmax_scale, nullptr, reinterpret_cast<float *>(ws + TL.dec_out), ws + TL.dec_ws, TL.dec_ws_bytes,
+              stream, nullptr, true, nullptr, &score_pass);
+  if (st != AQKV_OK) return st;
+  // 3. the nb records with the largest maxima, in increasing order
+  int32_t *sel = selected ? selected : reinterpret_cast<int32_t *>(ws + TL.sel);
+  if (launch_select_records(rec_max, cache->n_slots, n_rec, static_cast<int>(nb), sel, s) != hipSuccess)
+    return AQKV_ERR_HIP;
+  // 4. decode over the chosen records (and the split combine)
+  DecodeExtra list_pass{nullptr, 0, sel, nb, context_len};
+  return decode(cfg, layer, cache, batch, n_q_heads, n_kv_heads, nb * kBlockRows, q_rot, q_sketch, softmax_scale,
+                nullptr, out, ws + TL.list_ws, TL.list_ws_bytes, stream, nullptr, false, nullptr, &list_pass);
 }
 
 size_t aqkv_decode_static_scratch_bytes(void) { return kStaticScratchBytes; }

@@ -365,8 +365,15 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
   // score stores share the vector-memory counter with the tile loads, and a wait
   // for a partial count is only sound with loads alone in flight
   const bool partial_waits = job.scores == nullptr;
+  // the record of tile `tile` of the block's range (wave-uniform): the next one, or the
+  // listed record (a record list makes the range an index into the slot's list)
+  auto rec_of = [&](int64_t tile) -> uint32_t {
+    const int64_t i = t_begin / kTT + tile;
+    return __builtin_amdgcn_readfirstlane(job.rec_list ? static_cast<uint32_t>(job.rec_list[slot * job.list_stride + i])
+                                                       : static_cast<uint32_t>(i));
+  };
   auto issue = [&](int64_t tile) {
-    const uint32_t rec = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(t_begin / kTT + tile));
+    const uint32_t rec = rec_of(tile);
     if (keys_only)
       copy_region<Gm::o_vcodes>(rs_blocks, rec * Gm::tile_bytes, slot_buf(tile), lane);
     else
@@ -436,10 +443,12 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
       else wait_vm<0>();
     }
     compiler_fence();
+    // the tile's first token and its valid tokens (listed records: the record's tokens
+    // below the cached length), before the next tile's loads are in flight
+    const int64_t t0 = job.rec_list ? static_cast<int64_t>(rec_of(tile)) * kTT : t_begin + tile * kTT;
+    const int nt = static_cast<int>(min<int64_t>(kTT, (job.rec_list ? job.list_context : t_end) - t0));
     if (tile + (kRing - 1) * kWaves < n_tiles) issue(tile + (kRing - 1) * kWaves);
     const uint8_t *tb = slot_buf(tile);
-    const int64_t t0 = t_begin + tile * kTT;
-    const int nt = static_cast<int>(min<int64_t>(kTT, t_end - t0));
 
     // ---------------- scores: 2 column tiles of 16 tokens, their matrix chains interleaved
     v4i acc[2][RB];
@@ -520,7 +529,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
         ++chunk;
       }
     }
-    float logit[2][RB], score[2][RB];
+    float logit[2][RB], score[2][RB], nrm_ct[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const int tok = 16 * ct + n16;
@@ -533,6 +542,7 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
         gam = W > 0 ? reinterpret_cast<const float *>(tb + Gm::o_rnorm)[tok] : nrm;
       }
       const bool valid = tok < nt;
+      nrm_ct[ct] = nrm;
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
         const int g = 4 * r + q;
@@ -552,13 +562,26 @@ __device__ __forceinline__ void decode_body(const DecodeJob &job, int64_t slot, 
       }
     }
     if (keys_only) {
+      if (job.scores) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-          const int g = 4 * r + q, tok = 16 * ct + n16;
-          if (g < G && tok < nt) job.scores[(head0 + g) * job.context + t0 + tok] = score[ct][r];
+          for (int r = 0; r < RB; ++r) {
+            const int g = 4 * r + q, tok = 16 * ct + n16;
+            if (g < G && tok < nt) job.scores[(head0 + g) * job.context + t0 + tok] = score[ct][r];
+          }
+      }
+      if (job.rec_max) {
+        // the record's largest cosine score / ||k|| of the first head (0 for a zero key)
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const float c = nrm_ct[ct] > 0.0f ? score[ct][0] / nrm_ct[ct] : 0.0f;
+          cmax = fmaxf(cmax, 16 * ct + n16 < nt ? c : -INFINITY);
         }
+        cmax = row_max16(cmax);
+        if (lane == 0) job.rec_max[slot * job.rec_max_stride + t0 / kTT] = cmax;
+      }
       continue;
     }
 

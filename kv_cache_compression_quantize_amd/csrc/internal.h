@@ -115,6 +115,15 @@ struct DecodeJob {
   int part_stride;       // partials per head (the decoder's splits; 0 when there is none)
   int scores_only;       // non-zero: only the score output is wanted (the matrix-core decoder then
                          // reads the key fields alone and writes no partials)
+  // scores-only calls of the matrix-core decoder (one query head per slot): per record, the
+  // largest cosine score / ||k|| of its tokens, at rec_max[slot * rec_max_stride + record]
+  float *rec_max;
+  int64_t rec_max_stride;
+  // matrix-core decoder over listed records only: context is then 32 x the list length,
+  // record i of the slot's range is rec_list[slot * list_stride + i], and tokens at or
+  // past list_context are masked
+  const int32_t *rec_list;
+  int64_t list_stride, list_context;
 };
 
 // The recent-token window of a decode call, merged in by the combine
@@ -183,6 +192,10 @@ int topk_chunks(int budget);
 hipError_t launch_selection_query(const float *q, int64_t n_slots, int d, int g, int m, const float *rotation,
                                   const float *sketch, float *q_rot, float *q_sk, hipStream_t stream);
 hipError_t launch_topk(const TopkJob &job, hipStream_t stream);
+// the `budget` records with the largest rec_max values of each slot ([n_slots][n_records],
+// overwritten with the order keys; ties to the lower record), as increasing record indices
+hipError_t launch_select_records(float *rec_max, int64_t n_slots, int64_t n_records, int budget,
+                                 int32_t *selected, hipStream_t stream);
 // the split combine with a recent-token window merged in (in place of launch_combine)
 hipError_t launch_combine_window(const DecodeJob &job, const WindowJob &wj, hipStream_t stream);
 bool decode_supported(int d, int w, int g, int m, int vb);

@@ -20,6 +20,7 @@
 //                           (max, sum, weighted value sum); the split combine
 //                           merges the chunks.
 #include "internal.h"
+#include "query_rows.h"
 
 namespace aqkv {
 namespace {
@@ -42,15 +43,15 @@ __device__ __forceinline__ float block_reduce_sum(float x, float *red) {
 
 // Per (KV slot, 64 output rows of the stacked [Pi; S]): the slot's selection
 // query q_sel = sum over its query heads of q_h / ||q_h|| is built in LDS, then
-// rotated and sketched as in query preparation (sixteen lanes per row, every
-// row load issued before the query is built).
-constexpr int kSelQRows = 64;
+// rotated and sketched by the query-preparation GEMV (query_rows.h; every row
+// load issued before the query is built).
 template <int D>
 __global__ __launch_bounds__(kThreads) void selection_query_kernel(const float *__restrict__ q, int g, int m,
                                                                    const float *__restrict__ rotation,
                                                                    const float *__restrict__ sketch,
                                                                    float *__restrict__ q_rot,
                                                                    float *__restrict__ q_sk, int chunks) {
+  static_assert(QueryRows<D>::kThreads == kThreads, "one GEMV block per selection block");
   __shared__ float qs[D];
   __shared__ float red[4];
   const int64_t slot = blockIdx.x / chunks;
@@ -58,20 +59,8 @@ __global__ __launch_bounds__(kThreads) void selection_query_kernel(const float *
   const int tid = threadIdx.x;
   const int d_rot = q_rot ? D : 0;
   const int rows = d_rot + m;
-  constexpr int kLanes = 16;
-  constexpr int kGroups = kThreads / kLanes;
-  constexpr int kIter = kSelQRows / kGroups;
-  constexpr int kPer = D / kLanes;
-  const int sub = tid % kLanes, grp = tid / kLanes;
-  float a[kIter][kPer];
-#pragma unroll
-  for (int it = 0; it < kIter; ++it) {
-    const int row = chunk * kSelQRows + it * kGroups + grp;
-    const float *src = row < d_rot ? rotation + static_cast<int64_t>(row) * D
-                                   : sketch + static_cast<int64_t>(row - d_rot) * D;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) a[it][i] = row < rows ? src[sub + kLanes * i] : 0.0f;
-  }
+  QueryRows<D> qr;
+  qr.load(rotation, sketch, d_rot, rows, chunk);
   float acc = 0.0f;
   for (int h = 0; h < g; ++h) {
     const float x = tid < D ? q[(slot * g + h) * D + tid] : 0.0f;
@@ -80,21 +69,7 @@ __global__ __launch_bounds__(kThreads) void selection_query_kernel(const float *
   }
   if (tid < D) qs[tid] = acc;
   __syncthreads();
-#pragma unroll
-  for (int it = 0; it < kIter; ++it) {
-    const int row = chunk * kSelQRows + it * kGroups + grp;
-    float v = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) v = fmaf(a[it][i], qs[sub + kLanes * i], v);
-#pragma unroll
-    for (int off = kLanes / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kLanes);
-    if (sub == 0 && row < rows) {
-      if (row < d_rot)
-        q_rot[slot * D + row] = v;
-      else
-        q_sk[slot * m + (row - d_rot)] = v;
-    }
-  }
+  qr.apply(qs, d_rot, rows, chunk, q_rot ? q_rot + slot * D : nullptr, q_sk + slot * m);
 }
 
 // --------------------------------------------------------------- top-K select
@@ -107,7 +82,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 struct SelectJob {
   float *scores;            // [n_slots][context]; overwritten with the order keys
-  const uint8_t *norm;      // key_norm field at its place in record 0
+  const uint8_t *norm;      // key_norm field at its place in record 0; null: the scores are
+                            // the ranking values themselves (record selection)
   int sf;                   // half norms (else fp32)
   int64_t rec, capacity, context;
   int budget;               // chosen tokens per slot (<= context)
@@ -184,15 +160,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectJob job)
     for (int u = 0; u < kBatch; ++u) {
       const int t = t0 + u * kSelThreads + tid;
       sc[u] = t < T ? sc_row[t] : 0.0f;
-      nn[u] = t < T ? load_side(job.norm + rec_row((row0 + t) & ~int64_t(31), 0, job.rec), (row0 + t) & 31,
-                                job.sf != 0)
-                    : 0.0f;
+      nn[u] = t < T && job.norm ? load_side(job.norm + rec_row((row0 + t) & ~int64_t(31), 0, job.rec),
+                                            (row0 + t) & 31, job.sf != 0)
+                                : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int t = t0 + u * kSelThreads + tid;
       if (t < T) {
-        const uint32_t k = order_key(nn[u] > 0.0f ? sc[u] / nn[u] : 0.0f);
+        const uint32_t k = order_key(!job.norm ? sc[u] : nn[u] > 0.0f ? sc[u] / nn[u] : 0.0f);
         keys[t] = k;
         atomicAdd(&hist[k >> 20], 1u);
       }
@@ -684,7 +660,7 @@ int topk_chunks(int budget) { return (budget + kChunkTokens - 1) / kChunkTokens;
 hipError_t launch_selection_query(const float *q, int64_t n_slots, int d, int g, int m, const float *rotation,
                                   const float *sketch, float *q_rot, float *q_sk, hipStream_t stream) {
   const int rows = (q_rot ? d : 0) + m;
-  const int chunks = (rows + kSelQRows - 1) / kSelQRows;
+  const int chunks = (rows + 63) / 64;   // 64 rows of [Pi; S] per block
   const unsigned grid = static_cast<unsigned>(n_slots * chunks);
   switch (d) {
     case 64:
@@ -700,6 +676,34 @@ hipError_t launch_selection_query(const float *q, int64_t n_slots, int d, int g,
   return hipGetLastError();
 }
 
+namespace {
+hipError_t launch_select(const SelectJob &s, int64_t n_slots, hipStream_t stream) {
+  if (s.context <= kLdsKeys) {
+    const size_t smem = sizeof(uint4) * static_cast<size_t>((s.context + 3) / 4);
+    if (smem > 64 * 1024) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(topk_select_kernel<true>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+      if (e != hipSuccess) return e;
+    }
+    topk_select_kernel<true><<<static_cast<unsigned>(n_slots), kSelThreads, smem, stream>>>(s);
+  } else {
+    topk_select_kernel<false><<<static_cast<unsigned>(n_slots), kSelThreads, 0, stream>>>(s);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_select_records(float *rec_max, int64_t n_slots, int64_t n_records, int budget,
+                                 int32_t *selected, hipStream_t stream) {
+  SelectJob s{};
+  s.scores = rec_max;
+  s.norm = nullptr;
+  s.context = n_records;
+  s.budget = budget;
+  s.selected = selected;
+  return launch_select(s, n_slots, stream);
+}
+
 hipError_t launch_topk(const TopkJob &j, hipStream_t stream) {
   SelectJob s{};
   s.scores = j.scores;
@@ -710,19 +714,7 @@ hipError_t launch_topk(const TopkJob &j, hipStream_t stream) {
   s.context = j.context;
   s.budget = j.budget;
   s.selected = j.selected;
-  hipError_t e;
-  if (j.context <= kLdsKeys) {
-    const size_t smem = sizeof(uint4) * static_cast<size_t>((j.context + 3) / 4);
-    if (smem > 64 * 1024) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void *>(topk_select_kernel<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-      if (e != hipSuccess) return e;
-    }
-    topk_select_kernel<true><<<static_cast<unsigned>(j.n_slots), kSelThreads, smem, stream>>>(s);
-  } else {
-    topk_select_kernel<false><<<static_cast<unsigned>(j.n_slots), kSelThreads, 0, stream>>>(s);
-  }
-  e = hipGetLastError();
+  hipError_t e = launch_select(s, j.n_slots, stream);
   if (e != hipSuccess) return e;
   SparseJob p{};
   p.d = j.d;

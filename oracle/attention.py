@@ -137,3 +137,37 @@ def decode_slot_top_k(q, key_rows, value_rows, rotation, sketch, centroids, w: i
 def _value_rows_subset(value_rows, sel):
     codes, scale, vmin = value_rows
     return (np.asarray(codes)[sel], np.asarray(scale)[sel], np.asarray(vmin)[sel])
+
+
+def select_top_k_blocks(q, key_rows, rotation, sketch, centroids, w: int, budget: int, block: int = 32):
+    """QUOKA's dynamic top-K selection taken at the granularity of contiguous
+    KV blocks (QUOKA article §2, the cache organised as contiguous memory
+    blocks; a reading: the article ranks keys).  Tokens are grouped into
+    consecutive blocks of `block` rows (the last one ragged); a block ranks by
+    the largest cosine score cos_t (select_top_k) of its tokens, and the
+    min(ceil(budget / block), number of blocks) blocks with the largest ranks
+    are chosen, ties to the lower block.  Returns (chosen block indices in
+    increasing order, the block ranks)."""
+    _, cos = select_top_k(q, key_rows, rotation, sketch, centroids, w, 1)
+    T = cos.shape[0]
+    n_blk = (T + block - 1) // block
+    rank = np.array([cos[b * block:(b + 1) * block].max() for b in range(n_blk)], dtype=np.float64)
+    nb = max(1, min((int(budget) + block - 1) // block, n_blk)) if n_blk else 0
+    order = np.argsort(-rank, kind="stable")[:nb]
+    return np.sort(order), rank
+
+
+def decode_slot_top_k_blocks(q, key_rows, value_rows, rotation, sketch, centroids, w: int, budget: int,
+                             softmax_scale=None, group: int = 32, block: int = 32):
+    """Decode attention of the G query heads of one KV slot over every token of
+    the chosen blocks (select_top_k_blocks).  Returns (chosen blocks, out [G, d])."""
+    blocks, _ = select_top_k_blocks(q, key_rows, rotation, sketch, centroids, w, budget, block)
+    T = np.asarray(key_rows[2]).shape[0]
+    rows = np.array([t for b in blocks for t in range(b * block, min((b + 1) * block, T))], dtype=np.int64)
+    q = np.asarray(q, dtype=np.float64)
+    if rows.size == 0:
+        return blocks, np.zeros_like(q)
+    sub_k = tuple(np.asarray(a)[rows] for a in key_rows)
+    sub_v = _value_rows_subset(value_rows, rows)
+    _, out = decode_slot(q, sub_k, sub_v, rotation, sketch, centroids, w, softmax_scale, group)
+    return blocks, out

@@ -295,6 +295,33 @@ def test_decode_topk_validation_codes():
                                           FAKE, 16, C.c_float(0.1), None, FAKE, FAKE, need, None) == -8
 
 
+def test_decode_topk_blocks_validation_codes():
+    lib = aqkv.lib()
+    cfg = aqkv.config(128, 2, 128)
+    layer = aqkv.LayerParams(FAKE, FAKE, FAKE, FAKE)
+    need = aqkv.decode_topk_blocks_workspace_bytes(cfg, 1, 4, 2, 64, 16)
+    assert need > 0 and need % 256 == 0
+    assert aqkv.decode_topk_blocks_workspace_bytes(cfg, 1, 4, 2, 64, 0) == 0
+    # more budget never needs less workspace; a budget past the context needs what the whole context does
+    assert aqkv.decode_topk_blocks_workspace_bytes(cfg, 1, 4, 2, 64, 64) >= need
+    assert aqkv.decode_topk_blocks_workspace_bytes(cfg, 1, 4, 2, 64, 10 ** 5) == \
+        aqkv.decode_topk_blocks_workspace_bytes(cfg, 1, 4, 2, 64, 64)
+
+    def call(budget=16, q=FAKE, hq=4, ws=need, c=cfg):
+        return lib.aqkv_decode_attention_topk_blocks(C.byref(c), C.byref(layer), C.byref(_cache()), 1, hq, 2, 64,
+                                                     q, FAKE, FAKE, budget, C.c_float(0.1), None, FAKE, FAKE, ws,
+                                                     None)
+
+    assert call(budget=0) == -2
+    assert call(budget=(1 << 20) + 1) == -8
+    assert call(q=None) == -1
+    assert call(q=FAKE + 4) == -3
+    assert call(hq=5) == -2
+    assert call(ws=need - 1) == -5
+    # shapes without a matrix-core decoder (sketch rows != d with mse bits) are not covered
+    assert call(c=aqkv.config(128, 2, 256)) == -8
+
+
 def test_noalloc_decode_validation_codes():
     # the allocation-free decode checks its sizes against the static scratch before any HIP call
     lib = aqkv.lib()

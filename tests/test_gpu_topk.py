@@ -122,3 +122,74 @@ def test_topk_many_equal_keys():
         sub_v = tuple(np.asarray(a)[sel[s]] for a in refs[s][1])
         _, o_ref = oatt.decode_slot(qh, sub_k, sub_v, hl.rotation, hl.sketch, hl.centroids, w)
         assert np.max(np.abs(out[0, s * G:(s + 1) * G] - o_ref)) <= OUT_ATOL
+
+
+# ------------------------------------------------------ block-record selection
+
+BLOCK_CASES = [
+    # d, w, m, G, T, budget, value bits, half side information
+    (128, 2, 128, 4, 1000, 128, 2, False), (128, 0, 512, 4, 4096, 512, 2, False),
+    (128, 0, 384, 4, 700, 90, 2, False), (256, 3, 256, 2, 300, 129, 2, False),
+    (128, 2, 128, 8, 2050, 1, 2, False), (128, 2, 128, 2, 900, 10 ** 5, 2, False),
+    (64, 1, 64, 2, 400, 65, 4, False), (256, 2, 256, 2, 300, 129, 2, True),
+]
+
+
+@pytest.mark.parametrize("d,w,m,G,T,budget,vb,sf", BLOCK_CASES)
+def test_topk_blocks_selection_and_decode(d, w, m, G, T, budget, vb, sf):
+    torch, dev = torch_dev()
+    say("top-k blocks", d, w, m, G, T, budget, vb, "half side" if sf else "")
+    B, Hkv = 2, 2
+    Hq = Hkv * G
+    hl = host_layer(d, w, m, layer=6)
+    cfg = cfg_of(hl, vb, sf)
+    layer = device_layer(hl)
+    rng = np.random.default_rng(d + T + budget + 1)
+    ks = [rng.standard_normal((T, d)).astype(np.float32) for _ in range(B * Hkv)]
+    vs = [(rng.standard_normal((T, d)) * 2).astype(np.float32) for _ in range(B * Hkv)]
+    cache, refs = _upload_oracle_cache(hl, cfg, ks, vs, vb, capacity=T + 3)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    qd = torch.from_numpy(q).to(dev)
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, qd)
+    n_blk = (T + 31) // 32
+    nb = max(1, min((budget + 31) // 32, n_blk))
+    sel = torch.full((B * Hkv, nb), -1, dtype=torch.int32, device=dev)
+    out = aqkv.decode_attention_topk_blocks(cfg, layer, cache, B, Hq, Hkv, T, qd, q_rot, q_sk, budget, selected=sel)
+    torch.cuda.synchronize()
+    out, sel = out.cpu().numpy(), sel.cpu().numpy()
+    worst, swapped = 0.0, 0
+    for s in range(B * Hkv):
+        b, h = divmod(s, Hkv)
+        qh = q[b, h * G:(h + 1) * G]
+        gs = sel[s]
+        assert np.all(np.diff(gs) > 0) and gs[0] >= 0 and gs[-1] < n_blk
+        oblk, rank = oatt.select_top_k_blocks(qh, refs[s][0], hl.rotation, hl.sketch, hl.centroids, w, budget)
+        thr = np.sort(rank)[::-1][nb - 1]
+        tol = 2e-3 * np.sqrt(np.mean(rank ** 2))
+        diff = np.setxor1d(gs, oblk)
+        assert np.all(np.abs(rank[diff] - thr) <= tol), (diff, rank[diff], thr)
+        swapped += diff.size // 2
+        # the output over every row of the GPU's chosen blocks
+        rows = np.array([t for blk in gs for t in range(32 * blk, min(32 * blk + 32, T))])
+        sub_k = tuple(np.asarray(a)[rows] for a in refs[s][0])
+        sub_v = tuple(np.asarray(a)[rows] for a in refs[s][1])
+        _, o_ref = oatt.decode_slot(qh, sub_k, sub_v, hl.rotation, hl.sketch, hl.centroids, w)
+        worst = max(worst, float(np.max(np.abs(out[b, h * G:(h + 1) * G] - o_ref))))
+    say(f"out err {worst:.2e}, near-tie swaps {swapped}")
+    assert worst <= OUT_ATOL
+    if nb == n_blk:
+        assert swapped == 0
+
+
+def test_topk_blocks_empty_context():
+    torch, dev = torch_dev()
+    d, w, m, G = 128, 2, 128, 2
+    hl = host_layer(d, w, m)
+    cfg = cfg_of(hl)
+    layer = device_layer(hl)
+    cache = aqkv.Cache.allocate(cfg, 1, 64)
+    q = torch.randn((1, G, d), device=dev)
+    q_rot, q_sk = aqkv.prepare_query(cfg, layer, q)
+    out = aqkv.decode_attention_topk_blocks(cfg, layer, cache, 1, G, 1, 0, q, q_rot, q_sk, 16)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)

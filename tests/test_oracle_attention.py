@@ -243,3 +243,46 @@ def test_top_k_scale_invariance_ties_and_an_aligned_key():
     sel1, cos1 = attention.select_top_k(q, (qk.idx, qk.bits, qk.norm, qk.rnorm), pi, s, c, w, budget=40)
     np.testing.assert_allclose(cos2, cos1, rtol=1e-12)
     np.testing.assert_array_equal(sel2, sel1)
+
+
+# ---------------------------------------------------------- block top-K
+
+def test_block_top_k_with_block_one_is_token_top_k():
+    # blocks of one row rank exactly as the token-level selection
+    q, x, v, (pi, s, c, t, w) = _topk_case(23)
+    qk = keys.quantize_keys(x, pi, s, c, t, w)
+    kr = (qk.idx, qk.bits, qk.norm, qk.rnorm)
+    vr = values.quantize_values(v)
+    for budget in (1, 37, 199, 500):
+        sel_t, cos = attention.select_top_k(q, kr, pi, s, c, w, budget)
+        sel_b, rank = attention.select_top_k_blocks(q, kr, pi, s, c, w, budget, block=1)
+        np.testing.assert_array_equal(sel_b, sel_t)
+        np.testing.assert_array_equal(rank, cos)
+        np.testing.assert_allclose(attention.decode_slot_top_k_blocks(q, kr, vr, pi, s, c, w, budget, block=1)[1],
+                                   attention.decode_slot_top_k(q, kr, vr, pi, s, c, w, budget)[1], rtol=1e-13)
+
+
+def test_block_top_k_full_budget_is_full_attention_and_ragged_tail():
+    q, x, v, (pi, s, c, t, w) = _topk_case(24, T=203)        # 7 blocks, the last of 11 rows
+    qk = keys.quantize_keys(x, pi, s, c, t, w)
+    kr = (qk.idx, qk.bits, qk.norm, qk.rnorm)
+    vr = values.quantize_values(v)
+    blocks, out = attention.decode_slot_top_k_blocks(q, kr, vr, pi, s, c, w, budget=10 ** 6)
+    np.testing.assert_array_equal(blocks, np.arange(7))
+    np.testing.assert_allclose(out, attention.decode_slot(q, kr, vr, pi, s, c, w)[1], rtol=1e-13)
+    # a budget below one block still takes one whole block
+    blocks1, _ = attention.select_top_k_blocks(q, kr, pi, s, c, w, budget=1)
+    assert blocks1.size == 1
+
+
+def test_block_top_k_keeps_the_best_tokens_block_and_ranks_by_the_block_maximum():
+    q, x, v, (pi, s, c, t, w) = _topk_case(25, T=320)
+    x[170] = 3.0 * attention.selection_query(q)      # the group's own direction: in block 5
+    qk = keys.quantize_keys(x, pi, s, c, t, w)
+    kr = (qk.idx, qk.bits, qk.norm, qk.rnorm)
+    blocks, rank = attention.select_top_k_blocks(q, kr, pi, s, c, w, budget=32)
+    assert list(blocks) == [5]
+    _, cos = attention.select_top_k(q, kr, pi, s, c, w, 1)
+    np.testing.assert_array_equal(rank, cos.reshape(10, 32).max(axis=1))
+    blocks4, _ = attention.select_top_k_blocks(q, kr, pi, s, c, w, budget=100)   # ceil(100 / 32) = 4 blocks
+    assert set(blocks4) == set(np.argsort(-rank, kind="stable")[:4]) and 5 in blocks4
