@@ -406,11 +406,13 @@ def cpu_baseline(w, layers, budget_s: float = 16.0) -> dict:
             "per_slot_s_1_thread": {str(k): v for k, v in one.items()}}
 
 
-# kernels of each call, as rocprofv3 names them (substring match)
+# kernels of each call, as rocprofv3 names them (substring match): (the alternatives one of
+# which every launch of the call runs, the companions it runs beside it)
 KERNEL_NAMES = {
-    "decode": ["decode_fast_kernel", "combine_kernel", "decode_kernel"],
-    "quantize_keys": ["quantize_keys_resident_kernel", "quantize_keys_stream_kernel", "quantize_keys_qjl_kernel"],
-    "quantize_values": ["quantize_values_kernel"],
+    "decode": (["decode_fast_kernel", "::decode_kernel"], ["combine_kernel"]),
+    "quantize_keys": (["quantize_keys_resident_kernel", "quantize_keys_stream_kernel", "quantize_keys_qjl_kernel"],
+                      []),
+    "quantize_values": (["quantize_values_kernel"], []),
 }
 
 
@@ -418,9 +420,10 @@ def write_counters(fetch_csv: str, write_csv: str, out: str, workload: str, laye
     """The HBM counter summary (counters_path) from two rocprofv3 --pmc passes (FETCH_SIZE, then
     WRITE_SIZE, both in KiB per dispatch) over `bench.py --calibrate-copy`: each
     counter is scaled by what it reads for the plain 1 GiB device copy (1 GiB
-    fetched and 1 GiB written), and each call's HBM bytes per launch are the sum
-    over its kernels of the mean per dispatch (over every dispatch of the kernel,
-    whatever its template arguments: for a whole stack, the mean over its layers)."""
+    fetched and 1 GiB written), and each call's HBM bytes per launch are the bytes
+    of all its kernels' dispatches over the number of its launches (the dispatches
+    of its main kernel, whichever variant and template arguments a launch runs: for
+    a whole stack, the mean over its layers)."""
     import csv
 
     def means(path, counter):
@@ -447,13 +450,14 @@ def write_counters(fetch_csv: str, write_csv: str, out: str, workload: str, laye
                            "write_factor": f_write},
            "kernels": {}}
 
-    def family_mean(table, sub):
-        vals = [v for k, vs in table.items() if sub in k for v in vs]
-        return float(np.mean(vals)) if vals else 0.0
+    def per_launch(table, main, extra):
+        launches = sum(len(vs) for k, vs in table.items() if any(x in k for x in main))
+        total = sum(sum(vs) for k, vs in table.items() if any(x in k for x in main + extra))
+        return total / launches if launches else 0.0
 
-    for call, subs in KERNEL_NAMES.items():
-        kb_f = sum(family_mean(fetch, x) for x in subs)
-        kb_w = sum(family_mean(write, x) for x in subs)
+    for call, (main, extra) in KERNEL_NAMES.items():
+        kb_f = per_launch(fetch, main, extra)
+        kb_w = per_launch(write, main, extra)
         if kb_f == 0 and kb_w == 0:
             continue
         rec["kernels"][call] = {"source_hash": source_hash(call),

@@ -4,8 +4,13 @@ still span several tiles and a ragged tail.
 
 Bars: packed codes and sign bits bit-exact outside the 1e-5 decision-boundary
 window (mismatch rate inside the window reported); value codes, scales and
-minima bit-exact (both sides decide them in IEEE fp32); norms to fp32
-rounding; scores within 1e-3 relative; attention outputs within 2e-3 absolute.
+minima bit-exact (both sides decide them in IEEE fp32); key norms within 2e-6
+relative (an fp32 sum of 128-256 squares); residual norms within 5e-5
+relative: the kernel takes gamma = n ||y - c[idx]|| in the rotated frame, and
+y carries the split-product error of the rotation (about 2^-22 per rotated
+coordinate, so ~3e-6 in ||y - c||, which is typically 0.1-0.3: up to ~1.5e-5
+relative), plus the fp32 rotation's departure from orthogonality (~1e-7);
+scores within 1e-3 relative; attention outputs within 2e-3 absolute.
 """
 import numpy as np
 import pytest
