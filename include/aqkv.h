@@ -369,11 +369,14 @@ aqkv_status aqkv_decode_attention_noalloc(const aqkv_config *cfg, const aqkv_lay
 
 /* ------------------------------------------------------- measurement helper */
 
-/* Reads `bytes` of device memory at `data` once, as a plain stream of 16-byte
- * loads spread over the whole GPU, and xors everything read into *sink (dev,
- * one uint32): the practical ceiling of HBM reads against which the decode's
- * streaming rate is compared (no step of the method).  data and bytes must be
- * multiples of 16.  Enqueues on `stream` only. */
+/* Reads `bytes` of device memory at `data` once, as a stream of non-temporal
+ * 16-byte loads spread over the whole GPU: the practical ceiling of HBM reads
+ * against which the decode's streaming rate is compared (no step of the
+ * method).  Every lane folds what it read into one word and stores it to
+ * *sink (dev, one uint32) only if that word is 0xFFFFFFFF: a dependency that
+ * keeps every load without a store or atomic per block (either measurably
+ * slows the stream), not a result.  data and bytes must be multiples of 16.
+ * Enqueues on `stream` only. */
 aqkv_status aqkv_read_stream(const void *data, size_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus

@@ -138,13 +138,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void *base, u
 
 // Wave-wide asynchronous copy of BYTES (multiple of 16) bytes at byte offset
 // soff (wave-uniform) of a plane to LDS: lane l moves bytes 16 l .. 16 l + 15
-// of every 1 KiB piece (buffer_load_dwordx4 ... lds).
+// of every 1 KiB piece (buffer_load_dwordx4 ... lds, non-temporal: each record
+// is read once).
 template <int BYTES>
 __device__ __forceinline__ void copy_region(__amdgpu_buffer_rsrc_t rs, uint32_t soff, uint8_t *l, int lane) {
 #pragma unroll
   for (int off = 0; off < BYTES; off += 1024) {
     if (BYTES - off >= 1024 || 16 * lane < BYTES - off)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8 *)(l + off), 16, 16 * lane, static_cast<int>(soff + off), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8 *)(l + off), 16, 16 * lane, static_cast<int>(soff + off), 0,
+                                               kStreamPolicy);
   }
 }
 template <int BYTES>

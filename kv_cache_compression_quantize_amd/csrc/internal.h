@@ -212,6 +212,16 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
+// Cache policy of data a kernel reads once (the K / V views being quantised, the
+// cache records a decode streams): non-temporal.  On MI355X a plain 4 GiB read
+// stream measured 5.6-6.1 TB/s, the same stream with non-temporal loads 6.2-6.7 TB/s.
+constexpr int kStreamPolicy = 2;   // the nt bit of a gfx950 vector-memory instruction's cache policy
+__device__ __forceinline__ uint4 stream_load(const uint4 *p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Side information as stored: fp32, or the nearest IEEE half (ties to even;
 // finite values beyond the half range saturate to +-65504, so a stored half is
 // never infinite unless the fp32 value was).

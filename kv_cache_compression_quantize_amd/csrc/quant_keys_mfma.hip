@@ -266,12 +266,12 @@ __device__ __forceinline__ void load_keys(const KeyJob &job, const TileLoc<D> &L
     for (int k = 0; k < Geo<D>::KS; ++k) {
       const int64_t off = L.src[nt] + 32 * k + 8 * g;
       if (BF16) {
-        R.v[nt][k][0] = L.valid[nt] ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(job.k) + off)
+        R.v[nt][k][0] = L.valid[nt] ? stream_load(reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(job.k) + off))
                                     : make_uint4(0, 0, 0, 0);
       } else {
         const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(job.k) + off);
-        R.v[nt][k][0] = L.valid[nt] ? p[0] : make_uint4(0, 0, 0, 0);
-        R.v[nt][k][1] = L.valid[nt] ? p[1] : make_uint4(0, 0, 0, 0);
+        R.v[nt][k][0] = L.valid[nt] ? stream_load(p) : make_uint4(0, 0, 0, 0);
+        R.v[nt][k][1] = L.valid[nt] ? stream_load(p + 1) : make_uint4(0, 0, 0, 0);
       }
     }
 }

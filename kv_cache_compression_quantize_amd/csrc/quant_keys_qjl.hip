@@ -216,7 +216,7 @@ __device__ __forceinline__ void load_tile(const KeyJob &job, int64_t tile, int64
     for (int j = 0; j < IPW; ++j) {
       const int ins = wave * IPW + j;
       uint8_t *dst = ins < 16 * T ? slot + ins * 1024 : dummy + (ins - 16 * T) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8 *)dst, 16, static_cast<int>(voff[j]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_u8 *)dst, 16, static_cast<int>(voff[j]), 0, 0, kStreamPolicy);
     }
   } else {
 #pragma unroll
@@ -228,7 +228,7 @@ __device__ __forceinline__ void load_tile(const KeyJob &job, int64_t tile, int64
       const KeyAt a = key_at(job, B, key0, key0 + i < total ? i : 0);
       uint8_t *dst = real ? slot + ins * 1024 : dummy + (ins - 16 * T) * 1024;
       fb[j] = k + a.src + 8 * part;
-      __builtin_amdgcn_global_load_lds(static_cast<const void *>(fb[j]), (lds_u8 *)dst, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void *>(fb[j]), (lds_u8 *)dst, 16, 0, kStreamPolicy);
     }
   }
 }

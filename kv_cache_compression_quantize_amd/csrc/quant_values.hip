@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueJob job, int 
     if (tt >= t_lo && tt < t_hi) {
       const uint4 *src = reinterpret_cast<const uint4 *>(lbase + 8 * a * stride_bytes);
 #pragma unroll
-      for (int l = 0; l < kLoads; ++l) raw[a][l] = src[l];
+      for (int l = 0; l < kLoads; ++l) raw[a][l] = stream_load(src + l);
     }
   }
 
