@@ -33,15 +33,28 @@ def _counter_csv(path, counter, rows):
 
 def test_counter_summary_is_calibrated_by_the_copy(tmp_path):
     gib_kib = 1 << 20
-    # the copy reads half of its bytes through FETCH_SIZE (factor 2) and all through WRITE_SIZE
+    # the copy reads half of its bytes through FETCH_SIZE (factor 2) and all through WRITE_SIZE;
+    # two decode launches (each a decode kernel and a combine); four key launches of a layer
+    # stack, two on each of two alternative kernels
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [
         ("__amd_rocclr_copyBuffer", gib_kib / 2), ("__amd_rocclr_copyBuffer", 10.0),
         ("void aqkv::fast::decode_fast_kernel<128, 2, 2, 1, 2>(aqkv::DecodeJob)", 1000.0),
         ("void aqkv::fast::decode_fast_kernel<128, 2, 2, 1, 2>(aqkv::DecodeJob)", 1200.0),
-        ("aqkv::(anonymous namespace)::combine_kernel(aqkv::DecodeJob)", 10.0)])
+        ("aqkv::(anonymous namespace)::combine_kernel(aqkv::DecodeJob)", 10.0),
+        ("aqkv::(anonymous namespace)::combine_kernel(aqkv::DecodeJob)", 30.0),
+        ("void aqkv::(anonymous namespace)::quantize_keys_qjl_kernel<8>(aqkv::KeyJob, unsigned char const*, long)",
+         500.0),
+        ("void aqkv::(anonymous namespace)::quantize_keys_qjl_kernel<8>(aqkv::KeyJob, unsigned char const*, long)",
+         500.0),
+        ("void aqkv::(anonymous namespace)::quantize_keys_resident_kernel<128, 0, true, 12>(aqkv::KeyJob, long)",
+         300.0),
+        ("void aqkv::(anonymous namespace)::quantize_keys_resident_kernel<128, 0, true, 12>(aqkv::KeyJob, long)",
+         300.0)])
     _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [
         ("__amd_rocclr_copyBuffer", gib_kib),
         ("void aqkv::fast::decode_fast_kernel<128, 2, 2, 1, 2>(aqkv::DecodeJob)", 4.0),
+        ("void aqkv::fast::decode_fast_kernel<128, 2, 2, 1, 2>(aqkv::DecodeJob)", 4.0),
+        ("aqkv::(anonymous namespace)::combine_kernel(aqkv::DecodeJob)", 2.0),
         ("aqkv::(anonymous namespace)::combine_kernel(aqkv::DecodeJob)", 2.0)])
     out = tmp_path / "c.json"
     rec = bench.write_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(out), "wl", 3)
@@ -49,11 +62,14 @@ def test_counter_summary_is_calibrated_by_the_copy(tmp_path):
     assert rec["calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert rec["calibration"]["write_factor"] == pytest.approx(1.0)
     dec = rec["kernels"]["decode"]
-    # mean per dispatch of each kernel, summed over the call's kernels, scaled, in bytes
-    assert dec["fetch_bytes_per_launch"] == pytest.approx((1100.0 + 10.0) * 1024 * 2.0)
+    # all of the call's bytes over its launches (its main kernel's dispatches), scaled, in bytes
+    assert dec["fetch_bytes_per_launch"] == pytest.approx((1000.0 + 1200.0 + 10.0 + 30.0) / 2 * 1024 * 2.0)
     assert dec["write_bytes_per_launch"] == pytest.approx((4.0 + 2.0) * 1024)
     assert dec["source_hash"] == bench.source_hash("decode")
-    assert "quantize_keys" not in rec["kernels"]      # no dispatch of it in the files
+    # alternative kernels of one call are averaged, never added
+    keys = rec["kernels"]["quantize_keys"]
+    assert keys["fetch_bytes_per_launch"] == pytest.approx((500.0 + 300.0) / 2 * 1024 * 2.0)
+    assert "quantize_values" not in rec["kernels"]      # no dispatch of it in the files
     assert json.loads(out.read_text()) == rec
 
 
