@@ -105,14 +105,14 @@ class Path:
     """All buffers for one layer of the workload and the four calls of one step
     (aux: also the buffers of the window and top-K detail calls)."""
 
-    def __init__(self, w, layer: int, rotation: str = "qr", aux: bool = True):
+    def __init__(self, w, layer: int, rotation: str = "qr", aux: bool = True, side_f16: bool = False):
         import torch
 
         from kv_cache_compression_quantize_amd import aqkv
         self.aqkv = aqkv
         self.w = w
         self.layer_index = layer
-        self.cfg = aqkv.config(w.head_dim, w.mse_bits, w.sketch_dim(layer), w.value_bits, w.value_group)
+        self.cfg = aqkv.config(w.head_dim, w.mse_bits, w.sketch_dim(layer), w.value_bits, w.value_group, side_f16)
         self.layer = build_layer(w, layer, rotation)
         self.x = make_inputs(w, layer)
         dev = torch.device("cuda:0")
@@ -199,23 +199,25 @@ class Path:
 class Stack:
     """The paths of the workload's layers; one step runs every layer in order."""
 
-    def __init__(self, w, layers, rotation: str = "qr", aux_layers=()):
+    def __init__(self, w, layers, rotation: str = "qr", aux_layers=(), side_f16: bool = False):
         self.w = w
         self.paths = []
         for layer in layers:
-            self.paths.append(Path(w, layer, rotation, aux=layer in aux_layers))
+            self.paths.append(Path(w, layer, rotation, aux=layer in aux_layers, side_f16=side_f16))
 
     def step(self, evs=None):
         for i, p in enumerate(self.paths):
             p.step(evs[i] if evs else None)
 
 
-def unit_costs(w, layer: int) -> dict:
-    """Algorithmic bytes / flops per unit of each kernel (stated in the design notes)."""
+def unit_costs(w, layer: int, side_f16: bool = False) -> dict:
+    """Algorithmic bytes / flops per unit of each kernel (stated in the design notes); side_f16:
+    norms, scales and minima stored as halves."""
     d, wb, m, vb = w.head_dim, w.mse_bits, w.sketch_dim(layer), w.value_bits
     in_bytes = 2 if w.dtype == "bf16" else 4
-    key_row = wb * d // 8 + m // 8 + 4 + (4 if wb > 0 else 0)
-    val_row = d * vb // 8 + 2 * 4 * (d // w.value_group)
+    e = 2 if side_f16 else 4
+    key_row = wb * d // 8 + m // 8 + e + (e if wb > 0 else 0)
+    val_row = d * vb // 8 + 2 * e * (d // w.value_group)
     return {
         # decode: the compressed planes of one token of one kv head
         "decode_bytes_per_token_head": key_row + val_row,
@@ -226,9 +228,9 @@ def unit_costs(w, layer: int) -> dict:
     }
 
 
-def compression_ratio(w, layers) -> float:
+def compression_ratio(w, layers, side_f16: bool = False) -> float:
     """bf16 K + V bytes over compressed bytes, summed over the layers."""
-    uc = [unit_costs(w, layer)["decode_bytes_per_token_head"] for layer in layers]
+    uc = [unit_costs(w, layer, side_f16)["decode_bytes_per_token_head"] for layer in layers]
     return 4 * w.head_dim * len(layers) / float(sum(uc))
 
 
@@ -484,6 +486,8 @@ def main():
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--rotation", choices=["qr", "hadamard"], default="qr",
                     help="the keys' rotation: Haar (QR of a Gaussian) or randomised Hadamard")
+    ap.add_argument("--side-f16", action="store_true",
+                    help="store norms, value scales and minima as IEEE halves (the cache's half side-information option)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step captured once as a HIP graph instead of launching each call from Python")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -508,7 +512,7 @@ def main():
     reps = [layer for layer in representative_layers(w) if layer in layers] or layers[:1]
     log(f"workload {w.name}: setting up inputs for {len(layers)} layer(s)")
     t_setup = time.perf_counter()
-    stack = Stack(w, layers, args.rotation, aux_layers=() if args.no_detail else reps)
+    stack = Stack(w, layers, args.rotation, aux_layers=() if args.no_detail else reps, side_f16=args.side_f16)
     torch.cuda.synchronize()
     log(f"set-up {time.perf_counter() - t_setup:.1f} s; warmup")
     for _ in range(args.warmup):
@@ -557,7 +561,7 @@ def main():
         torch.cuda.synchronize()
 
     th = w.n_slots * w.context                       # token-heads per layer
-    ucs = [unit_costs(w, layer) for layer in layers]
+    ucs = [unit_costs(w, layer, args.side_f16) for layer in layers]
     dec_bytes = [u["decode_bytes_per_token_head"] * th for u in ucs]
     qk_flops = [u["qkeys_flops_per_key"] * th for u in ucs]
     qk_bytes = [u["qkeys_bytes_per_key"] * th for u in ucs]
@@ -573,7 +577,8 @@ def main():
                       "recipe": w.recipe, "launch": "hip_graph" if args.graph else "eager",
                       "rotation": args.rotation if w.mse_bits > 0 else None,
                       "compressed_bytes_per_step": int(sum(dec_bytes)),
-                      "compression_ratio_vs_bf16": compression_ratio(w, layers),
+                      "side_info": "f16" if args.side_f16 else "fp32",
+                      "compression_ratio_vs_bf16": compression_ratio(w, layers, args.side_f16),
                       "arithmetic": ARITHMETIC}}
     if in_step is not None:
         tot = {n: sum(s[n] for s in in_step) for n in CALLS}
@@ -608,7 +613,8 @@ def main():
             rec["roofline"] = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
                                "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS}
             alg_bytes = sum(by) / n_launch
-        rec["roofline"]["traffic"] = traffic_from_profiles(dominant, w.name, layer_tag)
+        # the committed counters were taken with fp32 side information
+        rec["roofline"]["traffic"] = None if args.side_f16 else traffic_from_profiles(dominant, w.name, layer_tag)
         rec["roofline"]["algorithmic_bytes_per_launch"] = alg_bytes
         rec["roofline"]["launch_ms"] = tot[dominant] / n_launch
         rec["roofline"]["launches_per_step"] = n_launch
@@ -637,7 +643,7 @@ def main():
             path = stack.paths[layers.index(layer)]
             per = time_calls(path, reps=max(5, min(steps, 20)))
             cold = time_decode_cold(path, reps=5)
-            uc = unit_costs(w, layer)
+            uc = unit_costs(w, layer, args.side_f16)
             db = uc["decode_bytes_per_token_head"] * th
             rec["detail"][f"layer{layer}"] = {
                 "sketch_dim": w.sketch_dim(layer),
