@@ -408,6 +408,8 @@ def cpu_baseline(w, layers, budget_s: float = 16.0) -> dict:
             "per_slot_s_1_thread": {str(k): v for k, v in one.items()}}
 
 
+CALIBRATION_COPIES = 3   # plain 1 GiB device copies after the timed steps (--calibrate-copy)
+
 # kernels of each call, as rocprofv3 names them (substring match): (the alternatives one of
 # which every launch of the call runs, the companions it runs beside it)
 KERNEL_NAMES = {
@@ -430,19 +432,22 @@ def write_counters(fetch_csv: str, write_csv: str, out: str, workload: str, laye
 
     def means(path, counter):
         acc = collections.defaultdict(list)
+        copies = []
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter:
                     acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
-        return acc
+                    if "copyBuffer" in r["Kernel_Name"]:
+                        copies.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+        return acc, copies
 
-    fetch, write = means(fetch_csv, "FETCH_SIZE"), means(write_csv, "WRITE_SIZE")
+    (fetch, copies_f), (write, copies_w) = means(fetch_csv, "FETCH_SIZE"), means(write_csv, "WRITE_SIZE")
     gib_kib = float(1 << 20)
-    # the 1 GiB copy: FETCH_SIZE reads about half its bytes on this part, so the cut is a
-    # quarter (the input set-up copies are a few MB)
-    copy_f = [v for k, vs in fetch.items() if "copyBuffer" in k for v in vs if v > 0.25 * gib_kib]
-    copy_w = [v for k, vs in write.items() if "copyBuffer" in k for v in vs if v > 0.25 * gib_kib]
-    if not copy_f or not copy_w:
+    # the 1 GiB copies of --calibrate-copy are the run's last CALIBRATION_COPIES copy dispatches
+    # (the input set-up copies come before the timed steps and can be as large)
+    copy_f = [v for _, v in sorted(copies_f)[-CALIBRATION_COPIES:] if v > 0.25 * gib_kib]
+    copy_w = [v for _, v in sorted(copies_w)[-CALIBRATION_COPIES:] if v > 0.25 * gib_kib]
+    if len(copy_f) < CALIBRATION_COPIES or len(copy_w) < CALIBRATION_COPIES:
         raise SystemExit("no 1 GiB copy dispatch in the counter files (run bench.py with --calibrate-copy)")
     f_fetch = gib_kib / float(np.mean(copy_f))
     f_write = gib_kib / float(np.mean(copy_w))
@@ -556,7 +561,7 @@ def main():
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
         dst = torch.empty_like(src)
-        for _ in range(3):
+        for _ in range(CALIBRATION_COPIES):
             dst.copy_(src)
         torch.cuda.synchronize()
 

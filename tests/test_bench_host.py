@@ -25,10 +25,10 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 def _counter_csv(path, counter, rows):
     with open(path, "w", newline="") as f:
-        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
         wr.writeheader()
-        for name, value in rows:
-            wr.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+        for i, (name, value) in enumerate(rows):
+            wr.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
 
 
 def test_counter_summary_is_calibrated_by_the_copy(tmp_path):
@@ -36,8 +36,11 @@ def test_counter_summary_is_calibrated_by_the_copy(tmp_path):
     # the copy reads half of its bytes through FETCH_SIZE (factor 2) and all through WRITE_SIZE;
     # two decode launches (each a decode kernel and a combine); four key launches of a layer
     # stack, two on each of two alternative kernels
+    # an input set-up copy as large as half the calibration copy comes first and must not count
+    copies_f = [("__amd_rocclr_copyBuffer", gib_kib / 2)] * bench.CALIBRATION_COPIES
+    copies_w = [("__amd_rocclr_copyBuffer", gib_kib)] * bench.CALIBRATION_COPIES
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [
-        ("__amd_rocclr_copyBuffer", gib_kib / 2), ("__amd_rocclr_copyBuffer", 10.0),
+        ("__amd_rocclr_copyBuffer", gib_kib / 3), ("__amd_rocclr_copyBuffer", 10.0),
         ("void aqkv::fast::decode_fast_kernel<128, 2, 2, 1, 2>(aqkv::DecodeJob)", 1000.0),
         ("void aqkv::fast::decode_fast_kernel<128, 2, 2, 1, 2>(aqkv::DecodeJob)", 1200.0),
         ("aqkv::(anonymous namespace)::combine_kernel(aqkv::DecodeJob)", 10.0),
@@ -49,13 +52,13 @@ def test_counter_summary_is_calibrated_by_the_copy(tmp_path):
         ("void aqkv::(anonymous namespace)::quantize_keys_resident_kernel<128, 0, true, 12>(aqkv::KeyJob, long)",
          300.0),
         ("void aqkv::(anonymous namespace)::quantize_keys_resident_kernel<128, 0, true, 12>(aqkv::KeyJob, long)",
-         300.0)])
+         300.0)] + copies_f)
     _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [
-        ("__amd_rocclr_copyBuffer", gib_kib),
+        ("__amd_rocclr_copyBuffer", gib_kib / 1.5),
         ("void aqkv::fast::decode_fast_kernel<128, 2, 2, 1, 2>(aqkv::DecodeJob)", 4.0),
         ("void aqkv::fast::decode_fast_kernel<128, 2, 2, 1, 2>(aqkv::DecodeJob)", 4.0),
         ("aqkv::(anonymous namespace)::combine_kernel(aqkv::DecodeJob)", 2.0),
-        ("aqkv::(anonymous namespace)::combine_kernel(aqkv::DecodeJob)", 2.0)])
+        ("aqkv::(anonymous namespace)::combine_kernel(aqkv::DecodeJob)", 2.0)] + copies_w)
     out = tmp_path / "c.json"
     rec = bench.write_counters(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), str(out), "wl", 3)
     assert rec["workload"] == "wl" and rec["layer"] == 3
