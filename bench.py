@@ -105,7 +105,8 @@ class Path:
     """All buffers for one layer of the workload and the four calls of one step
     (aux: also the buffers of the window and top-K detail calls)."""
 
-    def __init__(self, w, layer: int, rotation: str = "qr", aux: bool = True, side_f16: bool = False):
+    def __init__(self, w, layer: int, rotation: str = "qr", aux: bool = True, side_f16: bool = False,
+                 topk_budget=None):
         import torch
 
         from kv_cache_compression_quantize_amd import aqkv
@@ -138,7 +139,7 @@ class Path:
                                      device=dev).to(torch.bfloat16)
             self.q_f32 = self.x["q"].float().contiguous()
             # query-aware top-K preselection with QUOKA's budget rule min(4096, max(1024, T / 8))
-            self.budget = min(4096, max(1024, w.context // 8))
+            self.budget = topk_budget or min(4096, max(1024, w.context // 8))
             self.tws = torch.empty(max(aqkv.decode_topk_workspace_bytes(self.cfg, w.batch, w.n_q_heads,
                                                                         w.n_kv_heads, w.context, self.budget), 256),
                                    dtype=torch.uint8, device=dev)
@@ -199,11 +200,12 @@ class Path:
 class Stack:
     """The paths of the workload's layers; one step runs every layer in order."""
 
-    def __init__(self, w, layers, rotation: str = "qr", aux_layers=(), side_f16: bool = False):
+    def __init__(self, w, layers, rotation: str = "qr", aux_layers=(), side_f16: bool = False, topk_budget=None):
         self.w = w
         self.paths = []
         for layer in layers:
-            self.paths.append(Path(w, layer, rotation, aux=layer in aux_layers, side_f16=side_f16))
+            self.paths.append(Path(w, layer, rotation, aux=layer in aux_layers, side_f16=side_f16,
+                                   topk_budget=topk_budget))
 
     def step(self, evs=None):
         for i, p in enumerate(self.paths):
@@ -491,6 +493,8 @@ def main():
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--rotation", choices=["qr", "hadamard"], default="qr",
                     help="the keys' rotation: Haar (QR of a Gaussian) or randomised Hadamard")
+    ap.add_argument("--topk-budget", type=int, default=None,
+                    help="tokens the top-K detail legs keep per KV head (default: QUOKA's min(4096, max(1024, T/8)))")
     ap.add_argument("--side-f16", action="store_true",
                     help="store norms, value scales and minima as IEEE halves (the cache's half side-information option)")
     ap.add_argument("--graph", action="store_true",
@@ -517,7 +521,8 @@ def main():
     reps = [layer for layer in representative_layers(w) if layer in layers] or layers[:1]
     log(f"workload {w.name}: setting up inputs for {len(layers)} layer(s)")
     t_setup = time.perf_counter()
-    stack = Stack(w, layers, args.rotation, aux_layers=() if args.no_detail else reps, side_f16=args.side_f16)
+    stack = Stack(w, layers, args.rotation, aux_layers=() if args.no_detail else reps, side_f16=args.side_f16,
+                  topk_budget=args.topk_budget)
     torch.cuda.synchronize()
     log(f"set-up {time.perf_counter() - t_setup:.1f} s; warmup")
     for _ in range(args.warmup):
