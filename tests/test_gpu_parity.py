@@ -48,9 +48,21 @@ KEY_CASES = [
 
 @pytest.mark.parametrize("d,w,m,dtype", KEY_CASES)
 def test_quantize_keys_parity(d, w, m, dtype):
+    _key_parity(d, w, m, dtype, 2, 2, 1000)
+
+
+# the pure-QJL kernel at every wave count (k = 320 .. 512 in steps of 64) over 40000 keys:
+# 625 tiles of 64 keys on at most 256 blocks, so every block runs its loop two or three
+# times (ring reuse, the next tile prepared while the current one is in the matrix
+# units, sign rows stored in batches) and slot boundaries fall inside tiles
+@pytest.mark.parametrize("m", [320, 384, 448, 512])
+def test_quantize_keys_qjl_many_tiles(m):
+    _key_parity(128, 0, m, "bf16", 2, 4, 5000)
+
+
+def _key_parity(d, w, m, dtype, B, H, T):
     torch, dev = torch_dev()
-    say("quantize_keys", d, w, m, dtype)
-    B, H, T = 2, 2, 1000
+    say("quantize_keys", d, w, m, dtype, B, H, T)
     k = _as_dtype(_kv(B, H, T, d, seed=d + w + m), dtype)
     k[0, 0, 5] = 0.0                     # a zero key
     k[1, 1, 7] *= 1024.0                 # a large one (power of two: stays exactly representable)
