@@ -191,6 +191,28 @@ def test_quantize_values_bit_exact(d, vb, dtype):
         np.testing.assert_array_equal(gpu["vmin"].view(np.uint32), vm.view(np.uint32))
 
 
+# the value kernel over many records (8k-32k records, thousands of blocks, every
+# records-per-block shape: d = 64, 128, 256; partly covered records at both ends)
+@pytest.mark.parametrize("d,vb,dtype,B,H,T,off", [(128, 2, "bf16", 2, 4, 32768, 0), (64, 4, "fp32", 4, 4, 32000, 5),
+                                                  (256, 2, "bf16", 2, 2, 32768, 13)])
+def test_quantize_values_many_records(d, vb, dtype, B, H, T, off):
+    torch, dev = torch_dev()
+    say("quantize_values many records", d, vb, dtype, B, H, T, off)
+    v = _as_dtype(_kv(B, H, T, d, seed=11 + d + vb, scale=2.0), dtype)
+    hl = host_layer(d, 2, d)
+    cfg = cfg_of(hl, vb)
+    cache = aqkv.Cache.allocate(cfg, B * H, off + T + 7)
+    aqkv.quantize_values(cfg, to_device_kv(v, dtype), cache, off)
+    torch.cuda.synchronize()
+    for s in range(B * H):
+        b, h = divmod(s, H)
+        gpu = read_planes(cache, s, 0, off + T)    # (codes come in whole 32-token blocks)
+        vc, vs, vm = ovals.quantize_values(v[b, h], vb)
+        np.testing.assert_array_equal(olay.unpack_value_codes(gpu["vcodes"], off + T, d, vb)[off:], vc)
+        np.testing.assert_array_equal(gpu["vscale"][off:].view(np.uint32), vs.view(np.uint32))
+        np.testing.assert_array_equal(gpu["vmin"][off:].view(np.uint32), vm.view(np.uint32))
+
+
 @pytest.mark.parametrize("d,w,m", [(128, 2, 128), (256, 3, 256), (128, 0, 192)])
 def test_prepared_key_operands_match_one_call(d, w, m):
     # one operand pass, then appends of 1, 2, 37 and the rest of the tokens: the same
