@@ -53,17 +53,26 @@ constexpr int kRing = 4;                // raw key tiles in LDS: the one being p
 constexpr int kKeyBuf = kCB * kKS * 1024;   // f16 operand fragments of one team's keys (16 KiB)
 constexpr float kUp = 256.0f;           // the sketch is scaled by 2^8 before the split
 
-// Key teams per block (one: the kernel serves sketches of 320 rows and more, W >= 5 waves)
+// Key teams per block (one: the kernel serves sketches of 320 rows and more, W >= 5 row
+// groups of 64 rows)
 __host__ __device__ constexpr int teams_of(int W) { return 1; }
+// Waves per block.  Waves w and w + 4 of a block share a SIMD, so with W waves of two
+// 32-row tiles each, W = 5 .. 8, one SIMD always carries four tiles.  For W = 5 and 6 the
+// block runs 8 waves instead, wave w taking tiles w and (when it exists) w + 8 of the 2 W:
+// every SIMD then carries at most three tiles, and the preparation is spread over 512
+// threads.  Split this way, a wave's tiles are not the two halves of one sign word, so
+// each tile's 16 bits go to their half of the word in LDS.
+__host__ __device__ constexpr int waves_of(int W) { return W <= 6 ? 8 : W; }
+__host__ __device__ constexpr bool split_of(int W) { return waves_of(W) != W; }
 // Raw loads (1 KiB each) per wave and tile: every wave issues the same number on every
 // path through the loop (the loads past a tile's 16 T go to a dummy LDS area, a tile past
 // the last reloads a valid key), so the number of vector-memory operations issued after
 // any point is fixed and a partial vmcnt wait is exact
 __host__ __device__ constexpr int loads_per_wave(int W) {
-  return (16 * teams_of(W) + W * teams_of(W) - 1) / (W * teams_of(W));
+  return (16 * teams_of(W) + waves_of(W) * teams_of(W) - 1) / (waves_of(W) * teams_of(W));
 }
 __host__ __device__ constexpr int dummy_bytes(int W) {
-  return (loads_per_wave(W) * W * teams_of(W) - 16 * teams_of(W)) * 1024;
+  return (loads_per_wave(W) * waves_of(W) * teams_of(W) - 16 * teams_of(W)) * 1024;
 }
 // Tiles whose sign rows and norms are stored together
 constexpr int kBatch = 8;
@@ -264,7 +273,7 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 template <int W, int T>
 __device__ __forceinline__ void stage(const uint8_t *raw, uint8_t *kbuf, float *knorm, int64_t key0,
                                       int64_t total) {
-  constexpr int NT = 64 * W * T, PIECES = 1024 * T, CPT = (PIECES + NT - 1) / NT;
+  constexpr int NT = 64 * waves_of(W) * T, PIECES = 1024 * T, CPT = (PIECES + NT - 1) / NT;
   // (rolled: the pieces share registers, which the resident sketch leaves few of)
 #pragma unroll 1
   for (int j = 0; j < CPT; ++j) {
@@ -310,7 +319,7 @@ __device__ __forceinline__ void store_batch(const KeyJob &job, int64_t batch0, i
                                             int n0, const uint32_t *sgn, const float *knorm, int64_t total) {
   constexpr int NB = kBatch, TK = kTileKeys * T, SW = sgn_words(W), srow = 8 * W;
   const int tid = threadIdx.x;
-  const int key = tid / W, u = tid - key * W;
+  const int key = tid / W, u = tid - key * W;   // (threads past 64 W store nothing)
   uint2 sv[NB];
   float nv[NB];
   uint2 *sp[NB];
@@ -320,14 +329,15 @@ __device__ __forceinline__ void store_batch(const KeyJob &job, int64_t batch0, i
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int64_t key0 = (batch0 + j * stride) * TK;
-    ok[j] = j < count && key0 + key < total;
+    ok[j] = j < count && key < TK && key0 + key < total;
     const TileBase B = tile_base(job, key0);
     const KeyAt a = key_at(job, B, key0, ok[j] ? key : 0);
     const int64_t rb = (a.row >> 5) * job.rec, ri = a.row & 31;
     sp[j] = reinterpret_cast<uint2 *>(job.signs + rb + ri * srow + 8 * u);
     np[j] = job.norm + rb + ri * (sf ? 2 : 4);
-    sv[j] = *reinterpret_cast<const uint2 *>(sgn + (((s0 + j) % (NB + 1)) * TK + key) * SW + 2 * u);
-    nv[j] = knorm[((n0 + j) % (NB + 2)) * TK + key];
+    const int kk = key < TK ? key : 0;
+    sv[j] = *reinterpret_cast<const uint2 *>(sgn + (((s0 + j) % (NB + 1)) * TK + kk) * SW + 2 * u);
+    nv[j] = knorm[((n0 + j) % (NB + 2)) * TK + kk];
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -343,15 +353,19 @@ __device__ __forceinline__ void store_batch(const KeyJob &job, int64_t batch0, i
 }
 
 template <int W>
-__global__ __launch_bounds__(64 * W * teams_of(W)) void quantize_keys_qjl_kernel(KeyJob job, const uint8_t *ops,
-                                                                                  int64_t n_tiles) {
+__global__ __launch_bounds__(64 * waves_of(W) * teams_of(W)) void quantize_keys_qjl_kernel(KeyJob job,
+                                                                                            const uint8_t *ops,
+                                                                                            int64_t n_tiles) {
   constexpr int T = teams_of(W), NB = kBatch;
   constexpr int TK = kTileKeys * T;   // keys per tile
   constexpr int SW = sgn_words(W);
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave % W, team = wave / W;     // row group and key team of this wave
+  constexpr bool kSplit = split_of(W);
+  const int rg = kSplit ? 0 : wave % W, team = kSplit ? 0 : wave / W;   // row group and key team of this wave
+  // (split: this wave's tiles are `wave` and, when two, wave + 8)
+  const bool two = !kSplit || wave + 8 < 2 * W;
   const int n = lane & 31, hh = lane >> 5;
   uint8_t *ring = smem;
   uint8_t *kbuf = ring + kRing * raw_bytes(T);                                 // [2][T][kKeyBuf]
@@ -362,16 +376,19 @@ __global__ __launch_bounds__(64 * W * teams_of(W)) void quantize_keys_qjl_kernel
   const int64_t stride = gridDim.x;
   constexpr int IPW = loads_per_wave(W);
 
-  // this wave's rows of S: operand tiles 2 rg, 2 rg + 1, every k-step, hi and lo
+  // this wave's rows of S: operand tiles 2 rg, 2 rg + 1 (split: wave, wave + 8), every
+  // k-step, hi and lo
   v8h A[kRT][kKS][2];
 #pragma unroll
-  for (int r = 0; r < kRT; ++r)
+  for (int r = 0; r < kRT; ++r) {
+    const int t = kSplit ? (r == 0 ? wave : (two ? wave + 8 : wave)) : kRT * rg + r;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
-        A[r][ks][p] = *reinterpret_cast<const v8h *>(ops + static_cast<int64_t>(kRT * rg + r) * kTileOps +
-                                                     (2 * ks + p) * 1024 + lane * 16);
+        A[r][ks][p] =
+            *reinterpret_cast<const v8h *>(ops + static_cast<int64_t>(t) * kTileOps + (2 * ks + p) * 1024 + lane * 16);
+  }
 
   // byte offsets of this lane's pieces of its loads inside a tile's key rows (load j of
   // wave w fills units 64 (w IPW + j) + lane: key = unit / 16, piece per raw_unit)
@@ -435,20 +452,36 @@ __global__ __launch_bounds__(64 * W * teams_of(W)) void quantize_keys_qjl_kernel
         for (int p = 0; p < 2; ++p)
 #pragma unroll
           for (int r = 0; r < kRT; ++r)
-            acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r][ks][p], Bk[ks], acc[r], 0, 0, 0);
+            if (r == 0 || two) acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[r][ks][p], Bk[ks], acc[r], 0, 0, 0);
       // the next tile's operands are prepared while the matrix instructions run
       if (cb == 0 && next < n_tiles)
         stage<W, T>(ring + ((it + 1) % kRing) * raw_bytes(T), kbuf + ((it + 1) & 1) * kKeyBuf * T,
                     knorm + ((it + 1) % (NB + 2)) * TK, next * TK, total);
       // bit 16 r + e of the word: the sign of z (set = negative); acc starts at +0, so a
-      // zero product sum is never -0
-      uint32_t h = 0u;
+      // zero product sum is never -0.  Stored bit 1 = non-negative projection; a zero key
+      // stores all ones.
+      if (!kSplit) {
+        uint32_t h = 0u;
 #pragma unroll
-      for (int r = kRT - 1; r >= 0; --r)
+        for (int r = kRT - 1; r >= 0; --r)
 #pragma unroll
-        for (int e = 15; e >= 0; --e) h = __builtin_amdgcn_alignbit(h, __float_as_uint(acc[r][e]), 31);
-      // stored bit 1 = non-negative projection; a zero key stores all ones
-      sg[key * SW + 2 * rg + hh] = kn[key] > 0.0f ? ~h : 0xffffffffu;
+          for (int e = 15; e >= 0; --e) h = __builtin_amdgcn_alignbit(h, __float_as_uint(acc[r][e]), 31);
+        sg[key * SW + 2 * rg + hh] = kn[key] > 0.0f ? ~h : 0xffffffffu;
+      } else {
+        // tile t's 16 bits: half t % 2 of word 2 (t / 2) + hh
+        uint16_t *sg16 = reinterpret_cast<uint16_t *>(sg);
+#pragma unroll
+        for (int r = 0; r < kRT; ++r) {
+          if (r == 0 || two) {
+            const int t = r == 0 ? wave : wave + 8;
+            uint32_t h = 0u;
+#pragma unroll
+            for (int e = 15; e >= 0; --e) h = __builtin_amdgcn_alignbit(h, __float_as_uint(acc[r][e]), 31);
+            sg16[(key * SW + 2 * (t >> 1) + hh) * 2 + (t & 1)] =
+                static_cast<uint16_t>(kn[key] > 0.0f ? ~h : 0xffffu);
+          }
+        }
+      }
     }
   }
   // the tiles since the last batch (it >= 1 here); then no load may still be writing LDS
@@ -472,7 +505,7 @@ hipError_t launch_w(const KeyJob &job, const uint8_t *ops, hipStream_t stream) {
   const int64_t n_tiles = (total + kTileKeys * T - 1) / (kTileKeys * T);
   constexpr int64_t kCUs = 256;   // one resident block per compute unit
   const int64_t blocks = std::min<int64_t>(n_tiles, kCUs);
-  kern<<<static_cast<unsigned>(blocks), 64 * W * T, smem, stream>>>(job, ops, n_tiles);
+  kern<<<static_cast<unsigned>(blocks), 64 * waves_of(W) * T, smem, stream>>>(job, ops, n_tiles);
   return hipGetLastError();
 }
 
