@@ -37,9 +37,10 @@
 // Every shape parameter is a template constant, so a tile is straight-line
 // code.  A tile is one 32-token block record of the cache (all seven fields
 // contiguous); it goes HBM -> LDS with buffer_load_dwordx4 ... lds (per-slot
-// buffer resource, wave-uniform record offset) into a per-wave ring of three
-// tile buffers, so two tiles stream in while one is computed.  The
-// waves merge in LDS; combine_kernel merges the splits.
+// buffer resource, wave-uniform record offset) into a per-wave ring of two
+// tile buffers, so the next tile streams in while one is computed (ring_of
+// below: deeper rings cost resident waves).  The waves merge in LDS;
+// combine_kernel merges the splits.
 #pragma once
 
 #include <math.h>
