@@ -245,71 +245,120 @@ template <int D, int W, int MC, int G, int PL>
 __device__ __forceinline__ void pack_query(const DecodeJob &job, int64_t head0, const float *kappa, uint8_t *ops,
                                            HeadConst *hc) {
   constexpr int RB = heads_rb(G), HC = D / 64, NP = popc(PL), NC = NP * HC + MC, m = 64 * MC;
+  // Every block runs this before its tiles stream (only the first tile's loads are in
+  // flight), so the query's global reads are issued together rather than one dependent
+  // round per word: each round costs a full memory latency under the other blocks' load.
+  constexpr int kWords = RB * NC;                    // words of this thread: word tid of each (r, c)
+  constexpr int kGrp = kWords < 8 ? kWords : 8;      // words whose values are loaded together
+  constexpr int kHW = (G + kWaves - 1) / kWaves;     // heads a wave reduces
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // word tid of chunk (r, c) holds bytes i0 .. i0 + 3 of operand lane l = tid / 4
+  const int l = tid >> 2, i0 = (tid & 3) * 4;
+  const int row = l % 16, q = l / 16, t = row % 4;
+  // the values behind word j = r NC + c: coordinates of q_rot (plane a of PL, rows
+  // t = mse hi / lo) or rows of q_sketch (qjl rows), or none
+  auto word_src = [&](int j, int &a) -> const float * {
+    const int r = j / NC, c = j % NC, g = 4 * r + row / 4;
+    a = 1;
+    if (g >= G) return nullptr;
+    if (c < NP * HC) {
+      if (t >= 2) return nullptr;
+      int n = 0;
+#pragma unroll
+      for (int b = 1; b < (1 << W); ++b)
+        if ((PL >> b) & 1) {
+          if (n == c / HC) a = b;
+          ++n;
+        }
+      return job.q_rot + (head0 + g) * D + (D / 4) * q + 16 * (c % HC) + i0;
+    }
+    if (W == 0 ? t >= 3 : t < 2) return nullptr;
+    return job.q_sketch + (head0 + g) * m + 16 * MC * q + 16 * (c - NP * HC) + i0;
+  };
+  float vq[kGrp][4];
+  auto load_group = [&](int j0) {
+#pragma unroll
+    for (int jj = 0; jj < kGrp; ++jj) {
+      int a;
+      const float *src = j0 + jj < kWords ? word_src(j0 + jj, a) : nullptr;
+      // loads without branches (a branch around them makes the compiler wait on each):
+      // a word with no source reads the slot's first sketched row and drops it
+      const float *rd = src ? src : job.q_sketch + head0 * m;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const float x = rd[bb];
+        vq[jj][bb] = src ? x : 0.0f;
+      }
+    }
+  };
+
+  // the rows each wave reduces (head g = wave + 4 h), then the first group of words
+  float rv[kHW][W > 0 ? D / 64 : 1], sv[kHW][MC];
+#pragma unroll
+  for (int h = 0; h < kHW; ++h) {
+    const int g = wave + kWaves * h;
+    if (g < G) {
+      if constexpr (W > 0)
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) rv[h][k] = job.q_rot[(head0 + g) * D + lane + 64 * k];
+#pragma unroll
+      for (int k = 0; k < MC; ++k) sv[h][k] = job.q_sketch[(head0 + g) * m + lane + 64 * k];
+    }
+  }
+  load_group(0);
+
   float km = 0.0f;
 #pragma unroll
   for (int a = 1; a < (1 << W); ++a)
     if ((PL >> a) & 1) km = fmaxf(km, fabsf(kappa[a - 1]));
-  for (int g = wave; g < G; g += kWaves) {
-    float mx = 0.0f, sr = 0.0f, mq = 0.0f, sq = 0.0f;
-    if constexpr (W > 0)
-      for (int j = lane; j < D; j += 64) {
-        const float v = job.q_rot[(head0 + g) * D + j];
-        sr += v;
-        mx = fmaxf(mx, km * fabsf(v));
-      }
-    for (int i = lane; i < m; i += 64) {
-      const float v = job.q_sketch[(head0 + g) * m + i];
-      sq += v;
-      mq = fmaxf(mq, fabsf(2.0f * v));
-    }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, off));
-      mq = fmaxf(mq, __shfl_xor(mq, off));
-      sr += __shfl_xor(sr, off);
-      sq += __shfl_xor(sq, off);
+  for (int h = 0; h < kHW; ++h) {
+    const int g = wave + kWaves * h;
+    if (g < G) {
+      float mx = 0.0f, sr = 0.0f, mq = 0.0f, sq = 0.0f;
+      if constexpr (W > 0)
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) {
+          sr += rv[h][k];
+          mx = fmaxf(mx, km * fabsf(rv[h][k]));
+        }
+#pragma unroll
+      for (int k = 0; k < MC; ++k) {
+        sq += sv[h][k];
+        mq = fmaxf(mq, fabsf(2.0f * sv[h][k]));
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+        mq = fmaxf(mq, __shfl_xor(mq, off));
+        sr += __shfl_xor(sr, off);
+        sq += __shfl_xor(sq, off);
+      }
+      if (lane == 0)
+        hc[g] = HeadConst{mx > 0.0f ? mx / 16383.0f : 1.0f, mq > 0.0f ? mq / 16383.0f : 1.0f,
+                          W > 0 ? job.centroids[0] * sr : 0.0f, -sq};
     }
-    if (lane == 0)
-      hc[g] = HeadConst{mx > 0.0f ? mx / 16383.0f : 1.0f, mq > 0.0f ? mq / 16383.0f : 1.0f,
-                        W > 0 ? job.centroids[0] * sr : 0.0f, -sq};
   }
   __syncthreads();
-  for (int e4 = tid; e4 < RB * NC * 256; e4 += kThreads) {
-    const int rc = e4 / 256, rem = e4 % 256;
-    const int r = rc / NC, c = rc % NC;
-    const int l = rem / 4, i0 = (rem % 4) * 4;
-    const int row = l % 16, q = l / 16;
-    const int g = 4 * r + row / 4, t = row % 4;
-    uint32_t word = 0;
-    if (g < G) {
-      const float *src = nullptr;
-      float scl = 0.0f;
-      if (c < NP * HC) {
-        if (t < 2) {
-          // the (c / HC)-th plane of PL, coordinates (D/4) q + 16 h .. + 15
-          int a = 1, n = 0;
 #pragma unroll
-          for (int b = 1; b < (1 << W); ++b)
-            if ((PL >> b) & 1) {
-              if (n == c / HC) a = b;
-              ++n;
-            }
-          src = job.q_rot + (head0 + g) * D + (D / 4) * q + 16 * (c % HC) + i0;
-          scl = kappa[a - 1] / hc[g].sig_mse;
-        }
-      } else if (W == 0 ? t < 3 : t >= 2) {
-        src = job.q_sketch + (head0 + g) * m + 16 * MC * q + 16 * (c - NP * HC) + i0;
-        scl = 2.0f / hc[g].sig_qjl;
-      }
-      if (src) {
+  for (int j0 = 0; j0 < kWords; j0 += kGrp) {
+    if (j0 > 0) load_group(j0);
+#pragma unroll
+    for (int jj = 0; jj < kGrp; ++jj) {
+      const int j = j0 + jj;
+      if (j >= kWords) break;
+      const int c = j % NC, g = 4 * (j / NC) + row / 4;
+      int a;
+      uint32_t word = 0;
+      if (word_src(j, a)) {
+        const float scl = c < NP * HC ? kappa[a - 1] / hc[g].sig_mse : 2.0f / hc[g].sig_qjl;
         // pure QJL: the B bytes of this K-slot carry the bit times 2^e (e = 4 hf + i0 / 4, the
         // bit's place in its byte; -128 for e = 7), so the value becomes Q = v 2^(7 - e)
         // (-v for e = 7), < 2^21 in magnitude, in base-128 digits Q >> 14, (Q >> 7) & 127, Q & 127
         const int e = 4 * ((MC * q + (c - NP * HC)) & 1) + i0 / 4;
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-          int v = static_cast<int>(rintf(src[bb] * scl));
+          int v = static_cast<int>(rintf(vq[jj][bb] * scl));
           v = max(-16383, min(16383, v));
           int part;
           if constexpr (W == 0) {
@@ -321,8 +370,8 @@ __device__ __forceinline__ void pack_query(const DecodeJob &job, int64_t head0, 
           word |= (static_cast<uint32_t>(part) & 0xffu) << (8 * bb);
         }
       }
+      reinterpret_cast<uint32_t *>(ops)[j * kThreads + tid] = word;
     }
-    reinterpret_cast<uint32_t *>(ops)[e4] = word;
   }
   __syncthreads();
 }
