@@ -229,17 +229,30 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeJob job) {
 // Merge the split partials of one query head: M = max_i m_i, weights
 // w_i = 2^(m_i - M) (0 for empty splits), out = sum_i w_i acc_i / sum_i w_i l_i.
 // The weights go to LDS (1024 splits per pass); 256 / d threads share a channel,
-// each summing every (256 / d)-th split with independent loads in flight.
+// each summing every (256 / d)-th split.  The thread's first (m, l) pair and its
+// first kPre partial outputs are loaded at the start, together: the partials do not
+// depend on the weights, and one memory latency then covers the whole merge of
+// the usual split counts.  Loads are branch-free (clamped index, value dropped),
+// and the sums run in the same order as without the prefetch.
 __global__ __launch_bounds__(256) void combine_kernel(DecodeJob job) {
+  constexpr int kPre = 16;
   __shared__ float wts[1024];
   __shared__ float red[256];
   const int64_t head = blockIdx.x;
   const int d = job.d, ns = job.part_stride, tid = threadIdx.x;
   const float *ml = job.part_ml + head * ns * 2;
   const float *acc = job.part_acc + head * ns * d;
+  const int P = 256 / d;                  // threads per channel
+  const int j = tid % d, p = tid / d;
+  const int i0 = min(tid, ns - 1);
+  const float m0 = ml[2 * i0], l0 = ml[2 * i0 + 1];
+  float pre[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) pre[k] = acc[static_cast<int64_t>(min(p + P * k, ns - 1)) * d + j];
   // M over the non-empty splits
   float mx = -INFINITY;
-  for (int i = tid; i < ns; i += 256)
+  if (tid < ns && l0 > 0.0f) mx = fmaxf(mx, m0);
+  for (int i = tid + 256; i < ns; i += 256)
     if (ml[2 * i + 1] > 0.0f) mx = fmaxf(mx, ml[2 * i]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -247,20 +260,26 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeJob job) {
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
-  const int P = 256 / d;                  // threads per channel
-  const int j = tid % d, p = tid / d;
   float o = 0.0f, lsum = 0.0f;
   for (int c0 = 0; c0 < ns; c0 += 1024) {
     const int cn = min(1024, ns - c0);
     for (int i = tid; i < cn; i += 256) {
-      const float l = ml[2 * (c0 + i) + 1];
-      const float w = l > 0.0f ? exp2f(ml[2 * (c0 + i)] - mx) : 0.0f;
+      const bool first = c0 == 0 && i == tid;
+      const float l = first ? l0 : ml[2 * (c0 + i) + 1];
+      const float m = first ? m0 : ml[2 * (c0 + i)];
+      const float w = l > 0.0f ? exp2f(m - mx) : 0.0f;
       wts[i] = w;
       lsum = fmaf(l, w, lsum);
     }
     __syncthreads();
+    int i = p;
+    if (c0 == 0) {
+#pragma unroll
+      for (int k = 0; k < kPre; ++k, i += P)
+        if (i < cn) o = fmaf(pre[k], wts[i], o);
+    }
 #pragma unroll 8
-    for (int i = p; i < cn; i += P) o = fmaf(acc[static_cast<int64_t>(c0 + i) * d + j], wts[i], o);
+    for (; i < cn; i += P) o = fmaf(acc[static_cast<int64_t>(c0 + i) * d + j], wts[i], o);
     __syncthreads();
   }
   // sum of the l weights over the block, partial outputs over the P threads of a channel
