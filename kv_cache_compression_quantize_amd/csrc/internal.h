@@ -70,6 +70,10 @@ struct KeyJob {
   // cache fields, each at its place in record 0; row r at + rec_row(r, row bytes, rec)
   uint8_t *codes, *signs, *norm, *rnorm;
   int64_t rec;
+  // pure-QJL kernel only: floor(n / n_tokens) and floor(n / heads) for n < 2^31 as
+  // (n * m) >> (31 + s) (set by its launcher)
+  uint32_t tok_m, head_m;
+  int tok_s, head_s;
 };
 
 struct ValueJob {

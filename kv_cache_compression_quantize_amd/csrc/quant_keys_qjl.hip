@@ -137,6 +137,19 @@ struct KeyAt {
   int64_t row;   // cache row (slot * capacity + token_offset + t)
 };
 
+// Division of 0 <= n < 2^31 by a launch-invariant d >= 1 as one multiply and a shift
+// (Granlund and Montgomery, "Division by invariant integers using multiplication", 1994,
+// Theorem 4.2 with 31-bit dividends): s = ceil(log2 d), m = ceil(2^(31 + s) / d) < 2^32,
+// floor(n / d) = (n m) >> (31 + s)
+inline void div_magic(int64_t d, uint32_t &m, int &s) {
+  s = 0;
+  while ((int64_t(1) << s) < d) ++s;
+  m = static_cast<uint32_t>(((uint64_t(1) << (31 + s)) + static_cast<uint64_t>(d) - 1) / static_cast<uint64_t>(d));
+}
+__device__ __forceinline__ uint32_t div_by(uint32_t n, uint32_t m, int s) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> (31 + s));
+}
+
 // The tile's first key, located once per tile (wave-uniform)
 struct TileBase {
   int64_t slot, b, h, t;
@@ -146,8 +159,8 @@ __device__ __forceinline__ TileBase tile_base(const KeyJob &job, int64_t key0) {
   TileBase B;
   const int64_t total = job.n_slots * job.n_tokens;
   if (total < (int64_t(1) << 31)) {
-    B.slot = static_cast<uint32_t>(key0) / static_cast<uint32_t>(job.n_tokens);
-    B.b = static_cast<uint32_t>(B.slot) / static_cast<uint32_t>(job.heads);
+    B.slot = div_by(static_cast<uint32_t>(key0), job.tok_m, job.tok_s);
+    B.b = div_by(static_cast<uint32_t>(B.slot), job.head_m, job.head_s);
   } else {
     B.slot = key0 / job.n_tokens;
     B.b = B.slot / job.heads;
@@ -292,7 +305,9 @@ __device__ __forceinline__ void stage(const uint8_t *raw, uint8_t *kbuf, float *
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
     ss = row_sum16(ss);
-    const float n = key0 + i < total ? sqrtf(ss) : 0.0f;
+    // (the hardware square root, within 1 ulp: the norm is stored to fp32 accuracy and
+    // only its exponent picks the scale, which never changes a sign)
+    const float n = key0 + i < total ? __builtin_amdgcn_sqrtf(ss) : 0.0f;
     int ex = 0;
     (void)frexpf(n, &ex);                                      // n = f 2^ex, f in [0.5, 1)
     ex = max(-100, min(ex, 120));
@@ -493,8 +508,11 @@ __global__ __launch_bounds__(64 * waves_of(W) * teams_of(W)) void quantize_keys_
 }
 
 template <int W>
-hipError_t launch_w(const KeyJob &job, const uint8_t *ops, hipStream_t stream) {
+hipError_t launch_w(const KeyJob &job_in, const uint8_t *ops, hipStream_t stream) {
   constexpr int T = teams_of(W);
+  KeyJob job = job_in;
+  div_magic(std::max<int64_t>(job.n_tokens, 1), job.tok_m, job.tok_s);
+  div_magic(std::max<int64_t>(job.heads, 1), job.head_m, job.head_s);
   auto kern = quantize_keys_qjl_kernel<W>;
   static_assert(qjl_smem(W) <= 160 * 1024, "LDS of one block");
   const int smem = qjl_smem(W);
