@@ -70,11 +70,24 @@ struct KeyJob {
   // cache fields, each at its place in record 0; row r at + rec_row(r, row bytes, rec)
   uint8_t *codes, *signs, *norm, *rnorm;
   int64_t rec;
-  // pure-QJL kernel only: floor(n / n_tokens) and floor(n / heads) for n < 2^31 as
-  // (n * m) >> (31 + s) (set by its launcher)
+  // floor(n / n_tokens) and floor(n / heads) for n < 2^31 as (n * m) >> (31 + s)
+  // (div_magic; set by the key kernels' launchers)
   uint32_t tok_m, head_m;
   int tok_s, head_s;
 };
+
+// Division of 0 <= n < 2^31 by a launch-invariant d >= 1 as one multiply and a shift
+// (Granlund and Montgomery, "Division by invariant integers using multiplication", 1994,
+// Theorem 4.2 with 31-bit dividends): s = ceil(log2 d), m = ceil(2^(31 + s) / d) < 2^32,
+// floor(n / d) = (n m) >> (31 + s)
+inline void div_magic(int64_t d, uint32_t &m, int &s) {
+  s = 0;
+  while ((int64_t(1) << s) < d) ++s;
+  m = static_cast<uint32_t>(((uint64_t(1) << (31 + s)) + static_cast<uint64_t>(d) - 1) / static_cast<uint64_t>(d));
+}
+__device__ __forceinline__ uint32_t div_by(uint32_t n, uint32_t m, int s) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> (31 + s));
+}
 
 struct ValueJob {
   const void *v;

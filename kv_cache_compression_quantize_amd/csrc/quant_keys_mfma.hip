@@ -215,12 +215,12 @@ template <int D>
 __device__ __forceinline__ TileLoc<D> locate(const KeyJob &job, int64_t key0, int n) {
   TileLoc<D> L;
   const int64_t total = job.n_slots * job.n_tokens;
-  // the wave-uniform part: slot and token of the tile's first key (32-bit
-  // division when the sizes allow it)
+  // the wave-uniform part: slot and token of the tile's first key (a multiply and
+  // a shift when the sizes allow it)
   int64_t slot0, b0;
   if (total < (int64_t(1) << 31)) {
-    slot0 = static_cast<uint32_t>(key0) / static_cast<uint32_t>(job.n_tokens);
-    b0 = static_cast<uint32_t>(slot0) / static_cast<uint32_t>(job.heads);
+    slot0 = div_by(static_cast<uint32_t>(key0), job.tok_m, job.tok_s);
+    b0 = div_by(static_cast<uint32_t>(slot0), job.head_m, job.head_s);
   } else {
     slot0 = key0 / job.n_tokens;
     b0 = slot0 / job.heads;
@@ -310,14 +310,17 @@ __device__ __forceinline__ void prepare_keys(const RawKeys<D, BF16> &R, float (&
       for (int s = 0; s < 8; ++s) ss = fmaf(x[k][s], x[k][s], ss);
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    const float n = sqrtf(ss);
+    // (hardware square root and reciprocal below, each within 1 ulp: the norm is stored
+    // to fp32 accuracy, and the scale moves every projection by the same factor, far
+    // inside the decision windows)
+    const float n = __builtin_amdgcn_sqrtf(ss);
     nrm[nt] = n;
     if (BF16) {
       int e = 0;
       (void)frexpf(n, &e);                                       // n = f 2^e, f in [0.5, 1)
       e = max(-100, min(e, 120));
       const float sc = n > 0.0f ? ldexpf(1.0f, 8 - e) : 0.0f;   // n sc in [128, 256)
-      yscale[nt] = n > 0.0f ? 1.0f / (n * sc) : 0.0f;
+      yscale[nt] = n > 0.0f ? __builtin_amdgcn_rcpf(n * sc) : 0.0f;
 #pragma unroll
       for (int k = 0; k < Geo<D>::KS; ++k)
 #pragma unroll
@@ -409,7 +412,7 @@ __device__ __forceinline__ void index_thresholds(IndexState<D, W> &S, const floa
   constexpr int K = 1 << W;
 #pragma unroll
   for (int nt = 0; nt < Geo<D>::NT; ++nt) {
-    const float inv = 1.0f / yscale[nt];
+    const float inv = __builtin_amdgcn_rcpf(yscale[nt]);   // (1 ulp; rcp(0) = +inf)
 #pragma unroll
     for (int j = 0; j < IndexState<D, W>::NU; ++j) S.bts[j][nt] = S.bnd[K / 2 + j] * inv;
   }
@@ -581,7 +584,7 @@ __device__ __forceinline__ void index_end(const IndexState<D, W> &S, const float
     float esq = S.esq[nt];
     esq += __shfl_xor(esq, 16);
     esq += __shfl_xor(esq, 32);
-    gam[nt] = nrm[nt] * (sqrtf(esq) * kDown8);
+    gam[nt] = nrm[nt] * (__builtin_amdgcn_sqrtf(esq) * kDown8);
   }
 }
 
@@ -930,8 +933,11 @@ size_t stream_smem() {
 }
 
 template <int D, int W, bool BF16>
-hipError_t launch_dwt(const KeyJob &job, hipStream_t stream) {
+hipError_t launch_dwt(const KeyJob &job_in, hipStream_t stream) {
   using Gm = Geo<D>;
+  KeyJob job = job_in;
+  div_magic(std::max<int64_t>(job.n_tokens, 1), job.tok_m, job.tok_s);
+  div_magic(std::max<int64_t>(job.heads, 1), job.head_m, job.head_s);
   const int64_t total = job.n_slots * job.n_tokens;
   const int64_t n_tiles = (total + Gm::KT - 1) / Gm::KT;
   const size_t ops = key_operand_bytes(D, W, job.m);

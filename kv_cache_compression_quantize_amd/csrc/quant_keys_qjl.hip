@@ -137,19 +137,6 @@ struct KeyAt {
   int64_t row;   // cache row (slot * capacity + token_offset + t)
 };
 
-// Division of 0 <= n < 2^31 by a launch-invariant d >= 1 as one multiply and a shift
-// (Granlund and Montgomery, "Division by invariant integers using multiplication", 1994,
-// Theorem 4.2 with 31-bit dividends): s = ceil(log2 d), m = ceil(2^(31 + s) / d) < 2^32,
-// floor(n / d) = (n m) >> (31 + s)
-inline void div_magic(int64_t d, uint32_t &m, int &s) {
-  s = 0;
-  while ((int64_t(1) << s) < d) ++s;
-  m = static_cast<uint32_t>(((uint64_t(1) << (31 + s)) + static_cast<uint64_t>(d) - 1) / static_cast<uint64_t>(d));
-}
-__device__ __forceinline__ uint32_t div_by(uint32_t n, uint32_t m, int s) {
-  return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> (31 + s));
-}
-
 // The tile's first key, located once per tile (wave-uniform)
 struct TileBase {
   int64_t slot, b, h, t;
