@@ -26,10 +26,9 @@
 // fragment buffers (one 1 KiB fragment per 32 keys and k-step; the 16-byte
 // units XOR-swizzled so that both these writes and the operand reads are free
 // of bank conflicts).  Each wave's sign words meet in LDS (rows padded to a
-// conflict-free stride) and leave as whole 8-byte pieces of each row; the rows
-// and norms of several tiles are stored together (with stores and loads both
-// in flight the compiler waits for every memory access before reusing a
-// store's registers, so batching pays that wait once per batch).
+// conflict-free stride) and leave as whole 8-byte pieces of each row, one tile
+// after the barrier that ends it (kBatch: storing every tile measured faster
+// than gathering the rows of 2, 4 or 8 tiles into one burst of stores).
 #include <algorithm>
 
 #include "internal.h"
@@ -74,8 +73,9 @@ __host__ __device__ constexpr int loads_per_wave(int W) {
 __host__ __device__ constexpr int dummy_bytes(int W) {
   return (loads_per_wave(W) * waves_of(W) * teams_of(W) - 16 * teams_of(W)) * 1024;
 }
-// Tiles whose sign rows and norms are stored together
-constexpr int kBatch = 8;
+// Tiles whose sign rows and norms are stored together (one: k = 512 0.96 ms against 0.96,
+// 0.99 and 1.00 ms for 2, 4 and 8; k = 384 0.85 against 0.85, 0.86 and 0.87 ms)
+constexpr int kBatch = 1;
 
 // Sign-row stride in LDS, in 4-byte words: at least the row, 2 mod 4 so that the 32 keys
 // a wave writes (and 2 words each) land in 64 different banks
