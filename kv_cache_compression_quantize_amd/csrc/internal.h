@@ -100,6 +100,10 @@ struct ValueJob {
   // cache fields, each at its place in record 0; row r at + rec_row(r, row bytes, rec)
   uint8_t *codes, *side;
   int64_t rec;
+  // floor(n / records per slot) and floor(n / heads) for n < 2^31 as (n * m) >> (31 + s)
+  // (div_magic; set by the value kernel's launcher)
+  uint32_t bps_m, head_m;
+  int bps_s, head_s;
 };
 
 struct QueryJob {

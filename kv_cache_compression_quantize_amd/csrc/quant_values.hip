@@ -41,6 +41,8 @@
 // bits of the other tokens (read-modify-write), so appends of any length work.
 // The pass is a streaming one: HBM bandwidth with a thin VALU margin
 // (about 9 vector instructions per value).
+#include <algorithm>
+
 #include "internal.h"
 
 namespace aqkv {
@@ -91,12 +93,15 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueJob job, int 
   const int rid0 = blockIdx.x * kRpb + sub;
   const bool live = rid0 < n_rec;                  // the last block may hold fewer records (all reach the barrier)
   const int rid = live ? rid0 : 0;
-  const int64_t s = rid / blocks_per_slot;
-  const int64_t ct0 = (job.token_offset / kBlockTokens + rid % blocks_per_slot) * kBlockTokens;
+  // slot and record of the slot, batch and head: multiply-shift divisions (rid < 2^31)
+  const uint32_t su = div_by(static_cast<uint32_t>(rid), job.bps_m, job.bps_s);
+  const int64_t s = su;
+  const int64_t ct0 = (job.token_offset / kBlockTokens + (rid - static_cast<int>(su) * blocks_per_slot)) * kBlockTokens;
   // tokens [t_lo, t_hi) of the record are in this call
   const int t_lo = live ? static_cast<int>(max<int64_t>(ct0, job.token_offset) - ct0) : 0;
   const int t_hi = live ? static_cast<int>(min<int64_t>(ct0 + kBlockTokens, job.token_offset + job.n_tokens) - ct0) : 0;
-  const int64_t b = s / job.heads, h = s % job.heads;
+  const uint32_t bu = div_by(su, job.head_m, job.head_s);
+  const int64_t b = bu, h = static_cast<int64_t>(su) - static_cast<int64_t>(bu) * job.heads;
   const int64_t stride_bytes = job.token_stride * kElt;
   const char *rbase = static_cast<const char *>(job.v) +
                       (b * job.batch_stride + h * job.head_stride) * kElt + (ct0 - job.token_offset) * stride_bytes;
@@ -216,7 +221,8 @@ __global__ __launch_bounds__(256) void quantize_values_kernel(ValueJob job, int 
 }
 
 template <int D>
-hipError_t launch_d(const ValueJob &job, hipStream_t stream) {
+hipError_t launch_d(const ValueJob &job_in, hipStream_t stream) {
+  ValueJob job = job_in;
   const int64_t first = job.token_offset / kBlockTokens;
   const int64_t last = (job.token_offset + job.n_tokens - 1) / kBlockTokens;
   const int64_t per_slot = last - first + 1;
@@ -225,6 +231,8 @@ hipError_t launch_d(const ValueJob &job, hipStream_t stream) {
   constexpr int kRpb = 256 / D;
   const dim3 grid(static_cast<unsigned>((n_rec + kRpb - 1) / kRpb));
   const int bps = static_cast<int>(per_slot), nr = static_cast<int>(n_rec);
+  div_magic(per_slot, job.bps_m, job.bps_s);
+  div_magic(std::max<int64_t>(job.heads, 1), job.head_m, job.head_s);
   const bool bf16 = job.dtype == AQKV_BF16;
   if (job.vb == 2) {
     if (bf16) quantize_values_kernel<D, 2, true><<<grid, 256, 0, stream>>>(job, bps, nr);
