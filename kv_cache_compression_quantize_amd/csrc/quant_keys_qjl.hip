@@ -14,9 +14,10 @@
 //
 // Weight-stationary layout: a block holds the whole sketch in registers, wave
 // (row group r, key team t) two 32-row tiles (64 rows: 2 tiles x 8 k-steps x
-// hi/lo, 128 VGPRs), W = k / 64 row groups of 64 keys a tile.  The operand
-// rows are permuted so that the 32 C rows a lane holds for one key (16 of each
-// tile) are exactly one 32-bit word of the key's sign row.  A block walks
+// hi/lo, 128 VGPRs), W = k / 64 row groups of 64 keys a tile (k = 320 and 384:
+// 2 W waves of one tile each).  The operand rows are permuted so that the 32 C
+// rows a lane holds for one key (16 of each tile) are exactly one 32-bit word of
+// the key's sign row.  A block walks
 // tiles of 64 keys with one barrier per tile.  Keys travel HBM -> LDS by
 // buffer_load_dwordx4 ... lds into a four-slot ring, issued three tiles ahead;
 // while the matrix instructions of tile i run, the block prepares tile i + 1:
@@ -57,11 +58,11 @@ constexpr float kUp = 256.0f;           // the sketch is scaled by 2^8 before th
 __host__ __device__ constexpr int teams_of(int W) { return 1; }
 // Waves per block.  Waves w and w + 4 of a block share a SIMD, so with W waves of two
 // 32-row tiles each, W = 5 .. 8, one SIMD always carries four tiles.  For W = 5 and 6 the
-// block runs 8 waves instead, wave w taking tiles w and (when it exists) w + 8 of the 2 W:
-// every SIMD then carries at most three tiles, and the preparation is spread over 512
-// threads.  Split this way, a wave's tiles are not the two halves of one sign word, so
-// each tile's 16 bits go to their half of the word in LDS.
-__host__ __device__ constexpr int waves_of(int W) { return W <= 6 ? 8 : W; }
+// block runs 2 W waves of one tile each instead (wave w takes tile w): every SIMD carries
+// at most three tiles on three waves, so more waves hide each other's latencies, and the
+// preparation is spread over 128 W threads.  Split this way, a wave's tile is one half of
+// a sign word, so its 16 bits go to their half of the word in LDS.
+__host__ __device__ constexpr int waves_of(int W) { return W <= 6 ? 2 * W : W; }
 __host__ __device__ constexpr bool split_of(int W) { return waves_of(W) != W; }
 // Raw loads (1 KiB each) per wave and tile: every wave issues the same number on every
 // path through the loop (the loads past a tile's 16 T go to a dummy LDS area, a tile past
@@ -366,8 +367,8 @@ __global__ __launch_bounds__(64 * waves_of(W) * teams_of(W)) void quantize_keys_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr bool kSplit = split_of(W);
   const int rg = kSplit ? 0 : wave % W, team = kSplit ? 0 : wave / W;   // row group and key team of this wave
-  // (split: this wave's tiles are `wave` and, when two, wave + 8)
-  const bool two = !kSplit || wave + 8 < 2 * W;
+  // (split: this wave's one tile is tile `wave`)
+  constexpr bool two = !kSplit;
   const int n = lane & 31, hh = lane >> 5;
   uint8_t *ring = smem;
   uint8_t *kbuf = ring + kRing * raw_bytes(T);                                 // [2][T][kKeyBuf]
@@ -378,12 +379,12 @@ __global__ __launch_bounds__(64 * waves_of(W) * teams_of(W)) void quantize_keys_
   const int64_t stride = gridDim.x;
   constexpr int IPW = loads_per_wave(W);
 
-  // this wave's rows of S: operand tiles 2 rg, 2 rg + 1 (split: wave, wave + 8), every
+  // this wave's rows of S: operand tiles 2 rg, 2 rg + 1 (split: tile `wave` alone), every
   // k-step, hi and lo
   v8h A[kRT][kKS][2];
 #pragma unroll
   for (int r = 0; r < kRT; ++r) {
-    const int t = kSplit ? (r == 0 ? wave : (two ? wave + 8 : wave)) : kRT * rg + r;
+    const int t = kSplit ? wave : kRT * rg + r;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(64 * waves_of(W) * teams_of(W)) void quantize_keys_
 #pragma unroll
         for (int r = 0; r < kRT; ++r) {
           if (r == 0 || two) {
-            const int t = r == 0 ? wave : wave + 8;
+            const int t = wave;
             uint32_t h = 0u;
 #pragma unroll
             for (int e = 15; e >= 0; --e) h = __builtin_amdgcn_alignbit(h, __float_as_uint(acc[r][e]), 31);
